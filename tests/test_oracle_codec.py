@@ -1,0 +1,171 @@
+"""Pins of the oracle's int8 codec (compensator rows, smoothing, rounding).
+
+What fixes it, besides itself: the byte count the pages print (1.19 bytes per
+value, 3.4x, ~70 %), exactness of the row extraction, a brute-force top-C
+choice, the textbook per-row symmetric int8 quantizer of torch
+(``torch.quantize_per_channel``) at C = 0 with smoothing off, the half-LSB
+error bound of round-to-nearest, power-of-two scale invariance, an exact
+integer round trip, permutation equivariance, and the pages' qualitative
+claims that compensators and smoothing reduce the quantization error.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def _rand(rng, dk, dv, outlier_rows=(), outlier_cols=(), scale=1.0):
+    H = rng.standard_normal((dk, dv)) * scale
+    for r in outlier_rows:
+        H[r] *= 40
+    for c in outlier_cols:
+        H[:, c] *= 25
+    return H.astype(np.float32)
+
+
+def test_page_byte_count(orc):
+    g = json.load(open(GOLD))
+    d = g["head_dim_assumed"]["value"]
+    C = g["compensator_tokens"]["value"]
+    bpv = orc.state_bytes(d, d, C) / (d * d)
+    assert round(bpv, g["bytes_per_value"]["decimals"]) == g["bytes_per_value"]["value"]
+    assert round(g["fp32_bytes_per_value"]["value"] / bpv, 1) == g["reduction_vs_fp32"]["value"]
+    assert round(1 - bpv / 4, 1) == g["storage_cut_fraction"]["value"]
+    assert orc.state_bytes(128, 128, 4) == 19472
+
+
+def test_zero_state(orc):
+    cd = orc.quantize(np.zeros((16, 16), np.float32), 3)
+    assert not cd["sq"].any() and not cd["r"].any() and not cd["cv"].any()
+    assert (cd["s"] == 1).all()
+    assert list(cd["idx"]) == [0, 1, 2]
+
+
+@pytest.mark.parametrize("C", [0, 1, 4, 8])
+def test_extraction_is_exact(orc, C):
+    rng = np.random.default_rng(10 + C)
+    H = _rand(rng, 32, 24, outlier_rows=(3, 17, 30))
+    cd = orc.quantize(H, C)
+    m = np.abs(H).max(1)
+    want = sorted(sorted(range(32), key=lambda i: (-m[i], i))[:C])
+    assert list(cd["idx"]) == want
+    for c, i in enumerate(cd["idx"]):
+        assert cd["cv"][c].tobytes() == H[i].tobytes()     # bitwise copy
+        assert not cd["sq"][i].any() and cd["r"][i] == 0
+    D = orc.dequantize(cd)
+    for i in cd["idx"]:
+        assert (D[i] == H[i].astype(np.float64)).all()
+
+
+@pytest.mark.parametrize("C", [0, 1, 2, 3, 4])
+def test_top_c_bruteforce_with_ties(orc, C):
+    rng = np.random.default_rng(20 + C)
+    for trial in range(200):
+        H = rng.integers(-3, 4, (4, 4)).astype(np.float32)   # many ties
+        cd = orc.quantize(H, C)
+        m = np.abs(H).max(1)
+        ranked = sorted(range(4), key=lambda i: (-m[i], i))
+        assert list(cd["idx"]) == sorted(ranked[:C])
+
+
+def test_textbook_per_row_int8_matches_torch(orc):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(30)
+    H = _rand(rng, 64, 48)
+    cd = orc.quantize(H, 0, smooth=0)
+    assert (cd["s"] == 1).all()
+    amax = np.abs(H).max(1)
+    # the scale is the row absmax over 127 (one fp32 division)
+    np.testing.assert_array_equal(cd["r"], amax / np.float32(127))
+    ref = torch.quantize_per_channel(torch.from_numpy(H), torch.from_numpy(cd["r"]).double(),
+                                     torch.zeros(64, dtype=torch.long), 0,
+                                     torch.qint8).int_repr().numpy()
+    diff = np.abs(ref.astype(int) - cd["sq"].astype(int))
+    assert diff.max() <= 1
+    assert (diff > 0).sum() <= 3          # only exact-half cases may round apart
+    # the row maximum lands on +-127
+    rows = np.arange(64)
+    assert (np.abs(cd["sq"][rows, np.abs(H).argmax(1)]) == 127).all()
+
+
+@pytest.mark.parametrize("smooth", [0, 1])
+@pytest.mark.parametrize("C", [0, 4])
+def test_half_lsb_error_bound(orc, smooth, C):
+    rng = np.random.default_rng(40 + smooth + C)
+    H = _rand(rng, 128, 128, outlier_rows=(5, 77), outlier_cols=(9, 100))
+    cd = orc.quantize(H, C, smooth)
+    D = orc.dequantize(cd)
+    err = np.abs(D - H.astype(np.float64))
+    lsb = cd["r"].astype(np.float64)[:, None] * cd["s"].astype(np.float64)[None, :]
+    assert (err <= lsb * (0.5 + 1e-4) + 1e-30).all()
+    assert np.abs(cd["sq"].astype(int)).max() <= 127
+
+
+@pytest.mark.parametrize("smooth", [0, 1])
+def test_power_of_two_invariance(orc, smooth):
+    rng = np.random.default_rng(50)
+    H = _rand(rng, 32, 16, outlier_rows=(2,), outlier_cols=(7,))
+    H[:, 3] = 0                                   # a zero column keeps s = 1
+    a = orc.quantize(H, 2, smooth)
+    for e in (-7, 3, 11):
+        b = orc.quantize(H * np.float32(2.0 ** e), 2, smooth)
+        assert (a["sq"] == b["sq"]).all() and (a["idx"] == b["idx"]).all()
+        np.testing.assert_array_equal(b["cv"], a["cv"] * np.float32(2.0 ** e))
+        if smooth:
+            assert (a["r"] == b["r"]).all()
+            s_expect = a["s"] * np.float32(2.0 ** e)
+            s_expect[3] = 1
+            np.testing.assert_array_equal(b["s"], s_expect)
+        else:
+            np.testing.assert_array_equal(b["r"], a["r"] * np.float32(2.0 ** e))
+
+
+@pytest.mark.parametrize("smooth", [0, 1])
+def test_integer_matrix_round_trip(orc, smooth):
+    rng = np.random.default_rng(60)
+    n = 24
+    M = rng.integers(-126, 127, (n, n))
+    perm = rng.permutation(n)
+    M[np.arange(n), perm] = 127 * rng.choice([-1, 1], n)   # +-127 in every row and column
+    H = M.astype(np.float32)
+    a = orc.quantize(H, 0, smooth)
+    assert (a["sq"] == M).all()
+    b = orc.quantize(orc.dequantize(a).astype(np.float32), 0, smooth)
+    for key in ("sq", "r", "s"):
+        assert (a[key] == b[key]).all()
+
+
+def test_permutation_equivariance(orc):
+    rng = np.random.default_rng(70)
+    H = _rand(rng, 32, 20, outlier_rows=(4, 9), outlier_cols=(2,))
+    pr, pc = rng.permutation(32), rng.permutation(20)
+    a = orc.quantize(H, 3)
+    b = orc.quantize(H[pr][:, pc], 3)
+    inv = np.argsort(pr)
+    assert sorted(pr[b["idx"]]) == sorted(a["idx"])
+    assert (b["sq"] == a["sq"][pr][:, pc]).all()
+    assert (b["r"] == a["r"][pr]).all() and (b["s"] == a["s"][pc]).all()
+    # compensator rows carry the same values, permuted in their columns
+    for c, i in enumerate(b["idx"]):
+        j = list(a["idx"]).index(pr[i])
+        assert (b["cv"][c] == a["cv"][j][pc]).all()
+    assert inv.shape == (32,)
+
+
+def test_compensators_and_smoothing_reduce_error(orc):
+    """The pages' claims: keeping the largest outliers in high precision and
+    smoothing the residual each lower the quantization error (forum mirror,
+    'Abstract (translated)', techniques 2 and 3)."""
+    rng = np.random.default_rng(80)
+    H = _rand(rng, 128, 128, outlier_rows=(1, 20, 64, 90), outlier_cols=(3, 50))
+    H64 = H.astype(np.float64)
+
+    def mse(C, sm):
+        return float(((orc.dequantize(orc.quantize(H, C, sm)) - H64) ** 2).mean())
+
+    base, comp, both = mse(0, 0), mse(4, 0), mse(4, 1)
+    assert comp < 0.5 * base
+    assert both < comp
