@@ -1,0 +1,190 @@
+/*
+ * lq.h -- C ABI of the MI355X (gfx950) int8-state Gated DeltaNet / Kimi Delta
+ * Attention decode path ("LeapQuant"): liblq.so.
+ *
+ * Method sources (web pages about one preprint):
+ *   [abstract]  LeapQuant abstract, HFEPX eval-paper page (opentrain.ai),
+ *               section "Abstract".
+ *   [forum]     zhichai.net forum mirror "LeapQuant: Training-Free 8-bit
+ *               Quantization for Linear Attention Recurrent States", section
+ *               "Abstract (translated)", techniques 1-3.
+ *   [news ¶n]   globaltechnewsdesk.com article "A linear-attention method
+ *               cuts state ...", paragraph n.
+ *
+ * Model.  Per (batch b, head h) the recurrent state is H (dk x dv; row i = key
+ * channel, column j = value channel).  One token (q, k in R^dk, v in R^dv,
+ * beta, alpha) updates it by the gated delta rule
+ *     H <- (I - beta k k^T) D H + beta k v^T,   o = H^T q  (after the update),
+ * with D = alpha I (decay_mode LQ_DECAY_SCALAR, Gated DeltaNet) or
+ * D = diag(alpha) (LQ_DECAY_PER_KEY, Kimi Delta Attention).
+ *
+ * Stored state (the "codec"; [news ¶5]: 1.19 bytes per value at
+ * dk = dv = 128, C = 4):  H = deq + sum_c e_{idx_c} cv_c^T with
+ * deq_ij = sq_ij * row_scale_i * col_scale_j,  sq int8 in [-127, 127].
+ * It stays fixed for a window of W tokens ([news ¶3]); the window's updates
+ * live in an fp32 buffer (WY form, see lq_gdn_decode_step) and the state is
+ * rebuilt and requantized once at the window's end (lq_gdn_window_flush).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers, owned by the caller, contiguous
+ *     row-major in the shapes given, 16-byte aligned, except beta and the
+ *     scalar-mode alpha (one float per head), which need 4-byte alignment
+ *     only.  The library allocates
+ *     nothing, keeps no global state except the last HIP error code (per
+ *     thread), never synchronises, and is re-entrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
+ *     asynchronously on it.
+ *   - Return value: LQ_OK or an LQ_ERR_* code.  Argument checks run first and
+ *     make no HIP call; on any error nothing is enqueued.  LQ_ERR_HIP means a
+ *     launch failed; lq_last_hip_error() gives the hipError_t.
+ *   - Non-finite inputs are not checked; they propagate.
+ *   - Supported: dk = dv in {16, 64, 128}; 1 <= W <= 32; 0 <= C <= 8; all
+ *     sequences of a batch share the window position (lockstep decode).
+ */
+#ifndef LQ_H
+#define LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lq_status {
+    LQ_OK = 0,
+    LQ_ERR_NULL = 1,          /* a required pointer is NULL */
+    LQ_ERR_DIMS = 2,          /* B, H, dk, dv, W <= 0; C < 0 or C > dk; bad mode flag */
+    LQ_ERR_UNSUPPORTED = 3,   /* valid but not built: dk/dv, W > 32 or C > 8 */
+    LQ_ERR_WINDOW_FULL = 4,   /* decode_step with pos >= W: flush first */
+    LQ_ERR_POS = 5,           /* pos < 0, n_buffered outside [0, W], T < 0 */
+    LQ_ERR_ALIGN = 6,         /* a pointer is misaligned (see conventions) */
+    LQ_ERR_HIP = 7            /* kernel launch failed, see lq_last_hip_error() */
+};
+
+enum lq_decay_mode { LQ_DECAY_SCALAR = 0, LQ_DECAY_PER_KEY = 1 };
+
+/* Problem shape.  smooth: 1 = residual smoothing on (per-column scaling,
+ * [forum] technique 3), 0 = off (col_scale written as 1). */
+typedef struct lq_dims {
+    int32_t B, H, dk, dv, W, C;
+    int32_t decay_mode;
+    int32_t smooth;
+} lq_dims;
+
+/* Device arrays of one layer's quantized state and window buffer.
+ * gd = dk for LQ_DECAY_PER_KEY, 1 for LQ_DECAY_SCALAR.
+ *   sq        int8  [B,H,dk,dv]   quantized residual
+ *   row_scale fp32  [B,H,dk]      per-row scale (0 for an all-zero row)
+ *   col_scale fp32  [B,H,dv]      per-column smoothing factor
+ *   comp_idx  int32 [B,H,C]       compensator rows, ascending
+ *   comp_val  fp32  [B,H,C,dv]    compensator rows' values (exact fp32)
+ *   buf_k     fp32  [B,H,W,dk]    window buffer: keys
+ *   buf_y     fp32  [B,H,W,dk]    window buffer: WY left factors y_n
+ *   buf_u     fp32  [B,H,W,dv]    window buffer: WY value terms u_n
+ *   buf_g     fp32  [B,H,W,gd]    window buffer: window-local cumulative log decay
+ * comp_idx/comp_val may be NULL when C = 0. */
+typedef struct lq_state {
+    int8_t *sq;
+    float *row_scale;
+    float *col_scale;
+    int32_t *comp_idx;
+    float *comp_val;
+    float *buf_k;
+    float *buf_y;
+    float *buf_u;
+    float *buf_g;
+} lq_state;
+
+/*
+ * One decode token for every (b, h).  [abstract]: within a window, outputs
+ * come from the fixed low-bit state together with high-precision buffered
+ * updates; [forum] technique 2: compensator tokens share the update path of
+ * real tokens.
+ *
+ * pos = n = number of tokens already buffered in this window (0..W-1).
+ * Appends slot n to the buffer (g_n = g_{n-1} + log alpha, g_{-1} = 0;
+ * E_i = exp(g_n - g_i);  rr_i = <k, E_i o k_i>;
+ * y_n = beta (exp(g_n) o k - sum_{i<n} rr_i y_i);
+ * u_n = beta (v - sum_{i<n} rr_i u_i)) and writes
+ *     o = Hb^T q' + sum_{i<=n} a_i u_i,   a_i = <q, E_i o k_i>,
+ *     q' = exp(g_n) o q - sum_{i<=n} a_i y_i,
+ * which is exactly H_n^T q for the state H_n reached from the window-base
+ * state Hb (the dequantized codec) by the window's n+1 delta-rule steps.
+ *   q, k  fp32 [B,H,dk];  v, o fp32 [B,H,dv];  beta fp32 [B,H];
+ *   alpha fp32 [B,H] (scalar mode) or [B,H,dk] (per-key mode), in (0, 1].
+ * Reads the codec and buffer slots 0..n-1; writes buffer slot n and o.
+ * Errors: LQ_ERR_WINDOW_FULL if pos >= W, LQ_ERR_POS if pos < 0.
+ */
+int lq_gdn_decode_step(const lq_dims *d, const lq_state *st, int32_t pos,
+                       const float *q, const float *k, const float *v,
+                       const float *alpha, const float *beta, float *o, void *stream);
+
+/*
+ * Window boundary for every (b, h) ([news ¶3]: the state is rebuilt and
+ * quantized once at the boundary; [forum] techniques 2-3, [news ¶4]).
+ * From the codec and n_buffered slots (0..W) it rebuilds
+ *     H = Gamma Hb + sum_i (E_{N-1,i} o k_i) (u_i - Hb^T y_i)^T
+ * (Gamma = diag exp(g_{N-1})), then requantizes it in place:
+ *   1. m_i = max_j |H_ij|; the C rows with the largest m_i (ties: lower row)
+ *      become compensator tokens, comp_idx ascending, comp_val = exact rows;
+ *      R = H with those rows zeroed;
+ *   2. col_scale_j = max_i |R_ij| (1 if below 2^-120, or if smooth = 0);
+ *      Y_ij = R_ij * (1 / col_scale_j);
+ *   3. rho_i = max_j |Y_ij|;  row_scale_i = rho_i / 127;
+ *      sq_ij = clamp(rint(Y_ij * (127 / rho_i)), -127, 127); a row with
+ *      rho_i below 2^-120 is all zeros with row_scale_i = 0;
+ * every step one IEEE fp32 operation (round to nearest even), so the bytes
+ * are a function of the fp32 H.  h_out (nullable, fp32 [B,H,dk,dv])
+ * receives that fp32 H.  n_buffered = 0 is a no-op.  The caller then
+ * restarts the window at pos 0.
+ * Errors: LQ_ERR_POS if n_buffered < 0 or > W.
+ */
+int lq_gdn_window_flush(const lq_dims *d, const lq_state *st, int32_t n_buffered,
+                        float *h_out, void *stream);
+
+/*
+ * Quantizes an fp32 state h [B,H,dk,dv] into the codec of st (steps 1-3 of
+ * lq_gdn_window_flush; buffers untouched).  Used to start decoding from a
+ * prefilled state.
+ */
+int lq_gdn_state_quantize(const lq_dims *d, const float *h, const lq_state *st, void *stream);
+
+/*
+ * Writes the fp32 state the codec stands for into h_out [B,H,dk,dv]:
+ * (sq_ij * row_scale_i) * col_scale_j, with compensator rows set to comp_val.
+ */
+int lq_gdn_state_dequantize(const lq_dims *d, const lq_state *st, float *h_out, void *stream);
+
+/*
+ * Dense fp32-state gated delta rule over T tokens, state h [B,H,dk,dv] updated
+ * in place.  The fp32-state baseline the pages compare against ([abstract]:
+ * FP32 baseline), and the prefill that produces a starting state.  Inputs are
+ * [T,B,H,...] (shapes as in lq_gdn_decode_step); o (nullable) [T,B,H,dv].
+ * d->W, d->C and d->smooth are ignored.  Errors: LQ_ERR_POS if T < 0.
+ */
+int lq_gdn_fp32_recurrence(const lq_dims *d, float *h, int32_t T,
+                           const float *q, const float *k, const float *v,
+                           const float *alpha, const float *beta, float *o, void *stream);
+
+/* Bytes of one layer's codec arrays (sq, scales, compensators), i.e.
+ * B*H*(dk*dv + 4dk + 4dv + C*(4dv + 4)); 0 if d is NULL or invalid. */
+size_t lq_state_bytes(const lq_dims *d);
+
+/* Bytes of one layer's window buffer (buf_k, buf_y, buf_u, buf_g); 0 if invalid. */
+size_t lq_buffer_bytes(const lq_dims *d);
+
+/* Static description of a status code (never NULL). */
+const char *lq_status_str(int status);
+
+/* hipError_t of the last LQ_ERR_HIP returned on the calling thread (0 if none). */
+int lq_last_hip_error(void);
+
+/* LQ_OK if every entry point accepts the shape d (same checks they run). */
+int lq_check_dims(const lq_dims *d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LQ_H */

@@ -37,6 +37,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#define LQO_TINY 0x1p-120f
+
 /* ------------------------------------------------------------------------ */
 /* Recurrence                                                               */
 /* ------------------------------------------------------------------------ */
@@ -99,12 +101,14 @@ void lqo_step(int dk, int dv, int per_key, double *H,
  *              in ascending row order
  *   Q3  cv_c = H[idx_c][:] (exact copy); R = H with those rows zeroed.  A
  *              compensator token is the pair (key e_idx, value cv).
- *   Q4  s_j  = max_i |R_ij|, 1 if that is 0 (or if smoothing is off)
+ *   Q4  s_j  = max_i |R_ij|; 1 if that is below TINY (or smoothing is off)
  *   Q5  Y_ij = R_ij * (1 / s_j)
  *   Q6  rho_i = max_j |Y_ij|;  r_i = rho_i / 127
  *   Q7  sq_ij = clamp(rint(Y_ij * (127 / rho_i)), -127, 127); a row with
- *              rho_i = 0 is all zeros with r_i = 0.
+ *              rho_i below TINY is all zeros with r_i = 0.
  *
+ * TINY = 2^-120 keeps both reciprocals finite (1/s_j and 127/rho_i overflow
+ * fp32 below about 2^-121); magnitudes that small are taken as zero.
  * Every operation is one fp32 IEEE op (round to nearest even); rint rounds
  * half to even.  1/s_j and 127/rho_i are each one correctly rounded
  * division.  Returns 0, or -1 on bad sizes.
@@ -150,7 +154,7 @@ int lqo_quantize(int dk, int dv, int C, int smooth, const float *H,
             float a = fabsf(R[(size_t)i * dv + j]);
             if (a > mx) mx = a;
         }
-        s[j] = (smooth && mx > 0.0f) ? mx : 1.0f;
+        s[j] = (smooth && mx >= LQO_TINY) ? mx : 1.0f;
     }
     /* Q5 (R is overwritten by Y) */
     for (int j = 0; j < dv; ++j) {
@@ -164,7 +168,7 @@ int lqo_quantize(int dk, int dv, int C, int smooth, const float *H,
             float a = fabsf(R[(size_t)i * dv + j]);
             if (a > rho) rho = a;
         }
-        if (rho == 0.0f) {
+        if (rho < LQO_TINY) {
             r[i] = 0.0f;
             for (int j = 0; j < dv; ++j) sq[(size_t)i * dv + j] = 0;
             continue;

@@ -1,0 +1,159 @@
+// lq_api.hip -- the C ABI of liblq.so: argument checks, dispatch, status.
+// Every check runs before any HIP call; on an error nothing is enqueued.
+#include "lq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Token inputs: q, k, v, o vectors 16-byte aligned; alpha 16-byte aligned in
+// per-key mode and 4-byte aligned (one float per head) in scalar mode; beta
+// 4-byte aligned.
+int check_tokens(const lq_dims* d, const float* q, const float* k, const float* v,
+                 const float* alpha, const float* beta, const float* o, bool o_required) {
+    if (!q || !k || !v || !alpha || !beta || (o_required && !o)) return LQ_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o))) return LQ_ERR_ALIGN;
+    if (d->decay_mode == LQ_DECAY_PER_KEY ? !aligned16(alpha) : !aligned4(alpha)) return LQ_ERR_ALIGN;
+    if (!aligned4(beta)) return LQ_ERR_ALIGN;
+    return LQ_OK;
+}
+
+int check_dims(const lq_dims* d) {
+    if (!d) return LQ_ERR_NULL;
+    if (d->B <= 0 || d->H <= 0 || d->dk <= 0 || d->dv <= 0 || d->W <= 0) return LQ_ERR_DIMS;
+    if (d->C < 0 || d->C > d->dk) return LQ_ERR_DIMS;
+    if (d->decay_mode != LQ_DECAY_SCALAR && d->decay_mode != LQ_DECAY_PER_KEY) return LQ_ERR_DIMS;
+    if (d->smooth != 0 && d->smooth != 1) return LQ_ERR_DIMS;
+    if ((int64_t)d->B * (int64_t)d->H > 0x7fffffffLL) return LQ_ERR_DIMS;
+    if (d->dk != d->dv || (d->dk != 16 && d->dk != 64 && d->dk != 128)) return LQ_ERR_UNSUPPORTED;
+    if (d->W > 32 || d->C > 8) return LQ_ERR_UNSUPPORTED;
+    return LQ_OK;
+}
+
+// Codec arrays (and, if with_buffer, the window buffer) present and aligned.
+int check_state(const lq_dims* d, const lq_state* st, bool with_buffer) {
+    if (!st) return LQ_ERR_NULL;
+    const void* req[] = {st->sq, st->row_scale, st->col_scale};
+    for (const void* p : req)
+        if (!p) return LQ_ERR_NULL;
+    if (d->C > 0 && (!st->comp_idx || !st->comp_val)) return LQ_ERR_NULL;
+    for (const void* p : req)
+        if (!aligned16(p)) return LQ_ERR_ALIGN;
+    if (d->C > 0 && (!aligned16(st->comp_idx) || !aligned16(st->comp_val))) return LQ_ERR_ALIGN;
+    if (with_buffer) {
+        const void* buf[] = {st->buf_k, st->buf_y, st->buf_u, st->buf_g};
+        for (const void* p : buf)
+            if (!p) return LQ_ERR_NULL;
+        for (const void* p : buf)
+            if (!aligned16(p)) return LQ_ERR_ALIGN;
+    }
+    return LQ_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p) return LQ_ERR_NULL;
+    for (const void* p : ps)
+        if (!aligned16(p)) return LQ_ERR_ALIGN;
+    return LQ_OK;
+}
+
+int finish(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip = (int)e;
+        return LQ_ERR_HIP;
+    }
+    return LQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lq_check_dims(const lq_dims* d) { return check_dims(d); }
+
+int lq_gdn_decode_step(const lq_dims* d, const lq_state* st, int32_t pos, const float* q,
+                       const float* k, const float* v, const float* alpha, const float* beta,
+                       float* o, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, true))) return rc;
+    if ((rc = check_tokens(d, q, k, v, alpha, beta, o, true))) return rc;
+    if (pos < 0) return LQ_ERR_POS;
+    if (pos >= d->W) return LQ_ERR_WINDOW_FULL;
+    return finish(lq::launch_decode(*d, *st, pos, q, k, v, alpha, beta, o, (hipStream_t)stream));
+}
+
+int lq_gdn_window_flush(const lq_dims* d, const lq_state* st, int32_t n_buffered, float* h_out,
+                        void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, true))) return rc;
+    if (h_out && !aligned16(h_out)) return LQ_ERR_ALIGN;
+    if (n_buffered < 0 || n_buffered > d->W) return LQ_ERR_POS;
+    if (n_buffered == 0) return LQ_OK;
+    return finish(lq::launch_flush(*d, *st, n_buffered, h_out, (hipStream_t)stream));
+}
+
+int lq_gdn_state_quantize(const lq_dims* d, const float* h, const lq_state* st, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, false))) return rc;
+    if ((rc = check_ptrs({h}))) return rc;
+    return finish(lq::launch_quantize(*d, h, *st, (hipStream_t)stream));
+}
+
+int lq_gdn_state_dequantize(const lq_dims* d, const lq_state* st, float* h_out, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, false))) return rc;
+    if ((rc = check_ptrs({h_out}))) return rc;
+    return finish(lq::launch_dequantize(*d, *st, h_out, (hipStream_t)stream));
+}
+
+int lq_gdn_fp32_recurrence(const lq_dims* d, float* h, int32_t T, const float* q, const float* k,
+                           const float* v, const float* alpha, const float* beta, float* o,
+                           void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_ptrs({h}))) return rc;
+    if ((rc = check_tokens(d, q, k, v, alpha, beta, o, false))) return rc;
+    if (T < 0) return LQ_ERR_POS;
+    if (T == 0) return LQ_OK;
+    return finish(lq::launch_fp32_recurrence(*d, h, T, q, k, v, alpha, beta, o, (hipStream_t)stream));
+}
+
+size_t lq_state_bytes(const lq_dims* d) {
+    if (check_dims(d) != LQ_OK) return 0;
+    const size_t heads = (size_t)d->B * d->H;
+    const size_t dk = d->dk, dv = d->dv, C = d->C;
+    return heads * (dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4));
+}
+
+size_t lq_buffer_bytes(const lq_dims* d) {
+    if (check_dims(d) != LQ_OK) return 0;
+    const size_t heads = (size_t)d->B * d->H;
+    const size_t gd = d->decay_mode == LQ_DECAY_PER_KEY ? d->dk : 1;
+    return heads * (size_t)d->W * 4 * (2 * (size_t)d->dk + d->dv + gd);
+}
+
+const char* lq_status_str(int status) {
+    switch (status) {
+        case LQ_OK: return "ok";
+        case LQ_ERR_NULL: return "null pointer";
+        case LQ_ERR_DIMS: return "invalid dimensions";
+        case LQ_ERR_UNSUPPORTED: return "unsupported shape (dk = dv in {16, 64, 128}, W <= 32, C <= 8)";
+        case LQ_ERR_WINDOW_FULL: return "window full: flush before the next decode step";
+        case LQ_ERR_POS: return "window position or token count out of range";
+        case LQ_ERR_ALIGN: return "misaligned pointer (16 bytes; 4 for beta and scalar alpha)";
+        case LQ_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int lq_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+"""Thin ctypes binding of liblq.so (C ABI declared in include/lq.h).
+
+The functions carry the C names and only marshal arguments: torch device
+tensors become device pointers, the current torch stream becomes the HIP
+stream.  Before each call the binding checks dtype, device, contiguity and
+shape of every tensor against the lq_dims, because the C ABI sees only
+pointers.  Every step of the computation runs in the HIP kernels; if the
+library is missing, loading fails loudly (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblq.so")
+
+LQ_OK, LQ_ERR_NULL, LQ_ERR_DIMS, LQ_ERR_UNSUPPORTED, LQ_ERR_WINDOW_FULL, LQ_ERR_POS, \
+    LQ_ERR_ALIGN, LQ_ERR_HIP = range(8)
+LQ_DECAY_SCALAR, LQ_DECAY_PER_KEY = 0, 1
+
+# every symbol include/lq.h declares
+EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_state_quantize",
+           "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_state_bytes",
+           "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims")
+
+
+class lq_dims(ct.Structure):
+    _fields_ = [(n, ct.c_int32) for n in ("B", "H", "dk", "dv", "W", "C", "decay_mode", "smooth")]
+
+
+class lq_state(ct.Structure):
+    _fields_ = [(n, ct.c_void_p) for n in ("sq", "row_scale", "col_scale", "comp_idx", "comp_val",
+                                           "buf_k", "buf_y", "buf_u", "buf_g")]
+
+
+class LQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _lib.lq_status_str(status).decode() if _lib is not None else str(status)
+        extra = f" (hipError {_lib.lq_last_hip_error()})" if status == LQ_ERR_HIP else ""
+        super().__init__(f"{fn}: {msg}{extra} [status {status}]")
+
+
+_lib = None
+
+
+def load() -> ct.CDLL:
+    """Loads liblq.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m recurrent_state_quant_lq_amd.build`")
+        L = ct.CDLL(LIB_PATH)
+        D, S, P, I = ct.POINTER(lq_dims), ct.POINTER(lq_state), ct.c_void_p, ct.c_int32
+        L.lq_gdn_decode_step.argtypes = [D, S, I, P, P, P, P, P, P, P]
+        L.lq_gdn_window_flush.argtypes = [D, S, I, P, P]
+        L.lq_gdn_state_quantize.argtypes = [D, P, S, P]
+        L.lq_gdn_state_dequantize.argtypes = [D, S, P, P]
+        L.lq_gdn_fp32_recurrence.argtypes = [D, P, I, P, P, P, P, P, P, P]
+        for f in ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_state_quantize",
+                  "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_check_dims",
+                  "lq_last_hip_error"):
+            getattr(L, f).restype = ct.c_int
+        L.lq_check_dims.argtypes = [D]
+        L.lq_state_bytes.argtypes = [D]
+        L.lq_state_bytes.restype = ct.c_size_t
+        L.lq_buffer_bytes.argtypes = [D]
+        L.lq_buffer_bytes.restype = ct.c_size_t
+        L.lq_status_str.argtypes = [ct.c_int]
+        L.lq_status_str.restype = ct.c_char_p
+        L.lq_last_hip_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def make_dims(B, H, dk, dv, W, C, decay_mode=LQ_DECAY_SCALAR, smooth=1) -> lq_dims:
+    return lq_dims(B, H, dk, dv, W, C, decay_mode, smooth)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ct.c_void_p(stream.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(fn, rc):
+    if rc != LQ_OK:
+        raise LQError(fn, rc)
+
+
+@dataclass
+class LayerState:
+    """Device tensors of one layer's codec and window buffer (torch-owned)."""
+    dims: lq_dims
+    sq: torch.Tensor
+    row_scale: torch.Tensor
+    col_scale: torch.Tensor
+    comp_idx: torch.Tensor
+    comp_val: torch.Tensor
+    buf_k: torch.Tensor
+    buf_y: torch.Tensor
+    buf_u: torch.Tensor
+    buf_g: torch.Tensor
+
+    @staticmethod
+    def allocate(d: lq_dims, device="cuda") -> "LayerState":
+        B, H, dk, dv, W, C = d.B, d.H, d.dk, d.dv, d.W, d.C
+        gd = dk if d.decay_mode == LQ_DECAY_PER_KEY else 1
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        return LayerState(d, z((B, H, dk, dv), torch.int8), z((B, H, dk), torch.float32),
+                          z((B, H, dv), torch.float32), z((B, H, max(C, 1)), torch.int32),
+                          z((B, H, max(C, 1), dv), torch.float32),
+                          z((B, H, W, dk), torch.float32), z((B, H, W, dk), torch.float32),
+                          z((B, H, W, dv), torch.float32), z((B, H, W, gd), torch.float32))
+
+    def check(self, with_buffer=True):
+        d = self.dims
+        B, H, dk, dv, W, C = d.B, d.H, d.dk, d.dv, d.W, d.C
+        gd = dk if d.decay_mode == LQ_DECAY_PER_KEY else 1
+        _check(self.sq, "sq", (B, H, dk, dv), torch.int8)
+        _check(self.row_scale, "row_scale", (B, H, dk), torch.float32)
+        _check(self.col_scale, "col_scale", (B, H, dv), torch.float32)
+        _check(self.comp_idx, "comp_idx", (B, H, max(C, 1)), torch.int32)
+        _check(self.comp_val, "comp_val", (B, H, max(C, 1), dv), torch.float32)
+        if with_buffer:
+            _check(self.buf_k, "buf_k", (B, H, W, dk), torch.float32)
+            _check(self.buf_y, "buf_y", (B, H, W, dk), torch.float32)
+            _check(self.buf_u, "buf_u", (B, H, W, dv), torch.float32)
+            _check(self.buf_g, "buf_g", (B, H, W, gd), torch.float32)
+
+    def c_state(self) -> lq_state:
+        return lq_state(*[_ptr(getattr(self, n)) for n in
+                          ("sq", "row_scale", "col_scale", "comp_idx", "comp_val",
+                           "buf_k", "buf_y", "buf_u", "buf_g")])
+
+    def codec(self) -> dict:
+        """Host copies of the codec arrays (comp arrays cut to C)."""
+        C = self.dims.C
+        return dict(sq=self.sq.cpu().numpy(), r=self.row_scale.cpu().numpy(),
+                    s=self.col_scale.cpu().numpy(), idx=self.comp_idx[..., :C].cpu().numpy(),
+                    cv=self.comp_val[..., :C, :].cpu().numpy())
+
+    def load_codec(self, cd: dict):
+        """Uploads host codec arrays ([B,H,...], comp arrays with C entries)."""
+        C = self.dims.C
+        self.sq.copy_(torch.as_tensor(cd["sq"]))
+        self.row_scale.copy_(torch.as_tensor(cd["r"]))
+        self.col_scale.copy_(torch.as_tensor(cd["s"]))
+        if C:
+            self.comp_idx[..., :C].copy_(torch.as_tensor(cd["idx"]))
+            self.comp_val[..., :C, :].copy_(torch.as_tensor(cd["cv"]))
+
+
+def _token_shapes(d: lq_dims, T=None):
+    pre = (d.B, d.H) if T is None else (T, d.B, d.H)
+    ash = pre + ((d.dk,) if d.decay_mode == LQ_DECAY_PER_KEY else ())
+    return dict(q=pre + (d.dk,), k=pre + (d.dk,), v=pre + (d.dv,), alpha=ash, beta=pre,
+                o=pre + (d.dv,))
+
+
+def lq_gdn_decode_step(st: LayerState, pos: int, q, k, v, alpha, beta, o, stream=None):
+    d = st.dims
+    st.check()
+    sh = _token_shapes(d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
+        _check(t, name, sh[name], torch.float32)
+    cs = st.c_state()
+    rc = load().lq_gdn_decode_step(ct.byref(d), ct.byref(cs), int(pos), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
+    _raise("lq_gdn_decode_step", rc)
+
+
+def lq_gdn_window_flush(st: LayerState, n_buffered: int, h_out=None, stream=None):
+    d = st.dims
+    st.check()
+    if h_out is not None:
+        _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
+    cs = st.c_state()
+    rc = load().lq_gdn_window_flush(ct.byref(d), ct.byref(cs), int(n_buffered), _ptr(h_out),
+                                    _stream(stream))
+    _raise("lq_gdn_window_flush", rc)
+
+
+def lq_gdn_state_quantize(st: LayerState, h, stream=None):
+    d = st.dims
+    st.check(with_buffer=False)
+    _check(h, "h", (d.B, d.H, d.dk, d.dv), torch.float32)
+    cs = st.c_state()
+    rc = load().lq_gdn_state_quantize(ct.byref(d), _ptr(h), ct.byref(cs), _stream(stream))
+    _raise("lq_gdn_state_quantize", rc)
+
+
+def lq_gdn_state_dequantize(st: LayerState, h_out, stream=None):
+    d = st.dims
+    st.check(with_buffer=False)
+    _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
+    cs = st.c_state()
+    rc = load().lq_gdn_state_dequantize(ct.byref(d), ct.byref(cs), _ptr(h_out), _stream(stream))
+    _raise("lq_gdn_state_dequantize", rc)
+
+
+def lq_gdn_fp32_recurrence(d: lq_dims, h, T: int, q, k, v, alpha, beta, o=None, stream=None):
+    _check(h, "h", (d.B, d.H, d.dk, d.dv), torch.float32)
+    sh = _token_shapes(d, T)
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+        _check(t, name, sh[name], torch.float32)
+    if o is not None:
+        _check(o, "o", sh["o"], torch.float32)
+    rc = load().lq_gdn_fp32_recurrence(ct.byref(d), _ptr(h), int(T), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
+    _raise("lq_gdn_fp32_recurrence", rc)
+
+
+def lq_state_bytes(d: lq_dims) -> int:
+    return int(load().lq_state_bytes(ct.byref(d)))
+
+
+def lq_buffer_bytes(d: lq_dims) -> int:
+    return int(load().lq_buffer_bytes(ct.byref(d)))
+
+
+def lq_check_dims(d: lq_dims) -> int:
+    return int(load().lq_check_dims(ct.byref(d)))

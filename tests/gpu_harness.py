@@ -1,0 +1,197 @@
+"""Shared driver of the GPU parity tests: runs the HIP path and the CPU oracle
+side by side on the same seeded inputs, window by window (resync protocol).
+
+Per window both sides start from the ORACLE's codec bytes.  The HIP path runs
+the window's decode steps and the flush; then, for each sampled head:
+  * o_t (every step) against the oracle's window outputs, norm-wise:
+    max_j |do_j| / max_j |o_j| <= O_TOL;
+  * the WY buffer the kernels wrote against the oracle's buffer;
+  * the fp32 state the flush handed to its rounding step (h_out) against the
+    oracle's fp64 state;
+  * the flush's codec bytes against the oracle's codec OF THAT SAME fp32
+    state: bit-exact;
+and the oracle's own next codec is uploaded into those heads.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle as O
+from recurrent_state_quant_lq_amd import inputs, lq
+from recurrent_state_quant_lq_amd.configs import Workload
+
+O_TOL = 2e-3      # max relative error on o_t (norm-wise per token and head)
+H_TOL = 1e-5      # rebuilt fp32 state vs oracle fp64 state (max-abs relative)
+BUF_TOL = 1e-5    # WY buffer rows (max-abs relative per slot)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dims_of(wl: Workload, W=None, C=None, smooth=None) -> lq.lq_dims:
+    return lq.make_dims(wl.B, wl.H, wl.dk, wl.dv, W or wl.W, wl.C if C is None else C,
+                        lq.LQ_DECAY_PER_KEY if wl.per_key else lq.LQ_DECAY_SCALAR,
+                        wl.smooth if smooth is None else smooth)
+
+
+def rel_err(a, b, axis=-1):
+    """max |a-b| / max |b| along axis, maximised over the rest."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    num = np.abs(a - b).max(axis=axis)
+    den = np.maximum(np.abs(b).max(axis=axis), 1e-30)
+    return float((num / den).max())
+
+
+def codec_equal(gpu: dict, orc: dict) -> bool:
+    for key in ("sq", "r", "s", "idx", "cv"):
+        g, o = np.ascontiguousarray(gpu[key]), np.ascontiguousarray(orc[key])
+        if g.shape != o.shape or g.tobytes() != o.tobytes():
+            return False
+    return True
+
+
+def upload_head_codec(st: lq.LayerState, b: int, h: int, cd: dict):
+    C = st.dims.C
+    st.sq[b, h].copy_(torch.from_numpy(cd["sq"]))
+    st.row_scale[b, h].copy_(torch.from_numpy(cd["r"]))
+    st.col_scale[b, h].copy_(torch.from_numpy(cd["s"]))
+    if C:
+        st.comp_idx[b, h, :C].copy_(torch.from_numpy(cd["idx"]))
+        st.comp_val[b, h, :C].copy_(torch.from_numpy(cd["cv"]))
+
+
+def head_codec(st: lq.LayerState, b: int, h: int) -> dict:
+    C = st.dims.C
+    return dict(sq=st.sq[b, h].cpu().numpy(), r=st.row_scale[b, h].cpu().numpy(),
+                s=st.col_scale[b, h].cpu().numpy(), idx=st.comp_idx[b, h, :C].cpu().numpy(),
+                cv=st.comp_val[b, h, :C].cpu().numpy())
+
+
+class TokenSource:
+    """Prefill + decode tokens of a workload.  Small workloads draw them on the
+    host (numpy Philox), large ones on the device in chunks (torch Philox);
+    both come from recurrent_state_quant_lq_amd.inputs."""
+
+    def __init__(self, wl: Workload, host: bool, chunk: int = 256):
+        self.wl, self.host, self.chunk = wl, host, chunk
+        self.out = inputs.make_outliers(wl.seed, wl.H, wl.dk, wl.dv) if wl.outliers else None
+        self._host = None
+        if host:
+            self._host = inputs.host_tokens(wl.seed, wl.prefill + wl.T, wl.B, wl.H, wl.dk, wl.dv,
+                                            per_key=wl.per_key, beta_lo=wl.beta_lo,
+                                            beta_hi=wl.beta_hi, outliers=self.out)
+
+    def tokens(self, t0: int, t1: int) -> dict:
+        """Device tensors [t1-t0, B, H, ...] of absolute tokens t0..t1-1."""
+        wl = self.wl
+        if self.host:
+            return {k: torch.from_numpy(np.ascontiguousarray(v[t0:t1])).cuda()
+                    for k, v in self._host.items()}
+        # device chunks of `chunk` tokens, chunk c seeded by (seed, c)
+        parts = []
+        c0, c1 = t0 // self.chunk, (t1 - 1) // self.chunk
+        for c in range(c0, c1 + 1):
+            tk = inputs.device_tokens(wl.seed * 1000 + c, self.chunk, wl.B, wl.H, wl.dk, wl.dv,
+                                      per_key=wl.per_key, beta_lo=wl.beta_lo, beta_hi=wl.beta_hi,
+                                      device="cuda", outliers=self.out)
+            a = max(t0, c * self.chunk) - c * self.chunk
+            b = min(t1, (c + 1) * self.chunk) - c * self.chunk
+            parts.append({k: v[a:b] for k, v in tk.items()})
+        return {k: torch.cat([p[k] for p in parts]).contiguous() for k in parts[0]}
+
+
+@dataclass
+class Report:
+    o_err: float = 0.0
+    h_err: float = 0.0
+    buf_err: float = 0.0
+    windows: int = 0
+    heads: int = 0
+    bytes_exact: bool = True
+    mismatches: list = field(default_factory=list)
+
+
+def prefill_state(wl: Workload, src: TokenSource, st: lq.LayerState, sample, chunk=256):
+    """Starting codec: the oracle's quantization of its own fp64 prefill for
+    the sampled heads; the HIP fp32 recurrence + quantizer for the others."""
+    d = st.dims
+    B, H, dk, dv = wl.B, wl.H, wl.dk, wl.dv
+    start = {}
+    if wl.prefill == 0:
+        for bh in sample:
+            start[bh] = O.quantize(np.zeros((dk, dv), np.float32), d.C, d.smooth)
+        st.sq.zero_(); st.row_scale.zero_(); st.col_scale.fill_(1.0)
+        st.comp_val.zero_()
+        st.comp_idx.copy_(torch.arange(st.comp_idx.shape[-1], dtype=torch.int32).expand_as(st.comp_idx))
+    else:
+        h = torch.zeros((B, H, dk, dv), dtype=torch.float32, device="cuda")
+        Hs = {bh: np.zeros((dk, dv)) for bh in sample}
+        for t0 in range(0, wl.prefill, chunk):
+            t1 = min(wl.prefill, t0 + chunk)
+            tk = src.tokens(t0, t1)
+            lq.lq_gdn_fp32_recurrence(d, h, t1 - t0, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"])
+            for (b, hh) in sample:
+                ht = {k: v[:, b, hh].cpu().numpy() for k, v in tk.items()}
+                _, _, Hs[(b, hh)], _ = O.run_head(dk, dv, wl.per_key, t1 - t0, 0, 1, route=0,
+                                                  use_codec=False, tok=ht, H0=Hs[(b, hh)])
+        lq.lq_gdn_state_quantize(st, h)
+        for bh in sample:
+            start[bh] = O.quantize(Hs[bh].astype(np.float32), d.C, d.smooth)
+    for (b, hh), cd in start.items():
+        upload_head_codec(st, b, hh, cd)
+    torch.cuda.synchronize()
+    return start
+
+
+def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smooth=None,
+               T=None, check_buffers=True, log_every=0) -> Report:
+    d = dims_of(wl, W, C, smooth)
+    W, T = d.W, (T if T is not None else wl.T)
+    src = TokenSource(wl, host_tokens)
+    st = lq.LayerState.allocate(d)
+    codec = prefill_state(wl, src, st, sample)
+    rep = Report(heads=len(sample))
+    o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+    h_out = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    t = 0
+    while t < T:
+        N = min(W, T - t)
+        tk = src.tokens(wl.prefill + t, wl.prefill + t + N)
+        outs = torch.empty((N, wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+        for n in range(N):
+            lq.lq_gdn_decode_step(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                  tk["beta"][n], o)
+            outs[n].copy_(o)
+        bufs = ({k: getattr(st, "buf_" + k).clone() for k in ("k", "y", "u", "g")}
+                if check_buffers else None)
+        lq.lq_gdn_window_flush(st, N, h_out)
+        torch.cuda.synchronize()
+        for (b, h) in sample:
+            ht = {k: v[:, b, h].cpu().numpy() for k, v in tk.items()}
+            res = O.window(codec[(b, h)], ht, wl.per_key, W, d.C, d.smooth, route="wy")
+            rep.o_err = max(rep.o_err, rel_err(outs[:, b, h].cpu().numpy(), res["o"]))
+            hg = h_out[b, h].cpu().numpy()
+            rep.h_err = max(rep.h_err, float(np.abs(hg - res["H"]).max() / max(np.abs(res["H"]).max(), 1e-30)))
+            if check_buffers:
+                for key in ("k", "y", "u", "g"):
+                    g = bufs[key][b, h, :N].cpu().numpy()
+                    rep.buf_err = max(rep.buf_err, rel_err(g, res["buf"][key][:N]))
+            gc = head_codec(st, b, h)
+            if not codec_equal(gc, O.quantize(hg, d.C, d.smooth)):
+                rep.bytes_exact = False
+                rep.mismatches.append((t, b, h))
+            codec[(b, h)] = res["codec"]
+            upload_head_codec(st, b, h, res["codec"])
+        rep.windows += 1
+        t += N
+        if log_every and rep.windows % log_every == 0:
+            say(f"  window {rep.windows}: o_err {rep.o_err:.2e} h_err {rep.h_err:.2e} "
+                f"buf_err {rep.buf_err:.2e} exact {rep.bytes_exact}")
+    return rep

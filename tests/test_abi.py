@@ -1,0 +1,136 @@
+"""Host-only checks of the C ABI library (no GPU needed, no kernel launched).
+
+The library must load, export every function include/lq.h declares, and
+reject bad arguments with the documented status before any HIP call.
+"""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+from recurrent_state_quant_lq_amd import lq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH), reason="liblq.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(lq.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    L = ct.CDLL(lq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _dims(**kw):
+    base = dict(B=2, H=3, dk=128, dv=128, W=16, C=4, decay_mode=0, smooth=1)
+    base.update(kw)
+    return lq.lq_dims(*[base[n] for n in ("B", "H", "dk", "dv", "W", "C", "decay_mode", "smooth")])
+
+
+def test_sizes():
+    L = lq.load()
+    d = _dims()
+    assert L.lq_state_bytes(ct.byref(d)) == 6 * 19472
+    assert L.lq_buffer_bytes(ct.byref(d)) == 6 * 16 * 4 * (128 + 128 + 128 + 1)
+    dk = _dims(decay_mode=1)
+    assert L.lq_buffer_bytes(ct.byref(dk)) == 6 * 16 * 4 * (4 * 128)
+    assert L.lq_state_bytes(None) == 0
+    assert L.lq_state_bytes(ct.byref(_dims(dk=0))) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), lq.LQ_OK),
+    (dict(B=0), lq.LQ_ERR_DIMS), (dict(H=-1), lq.LQ_ERR_DIMS), (dict(W=0), lq.LQ_ERR_DIMS),
+    (dict(C=-1), lq.LQ_ERR_DIMS), (dict(dk=16, dv=16, C=17), lq.LQ_ERR_DIMS),
+    (dict(decay_mode=2), lq.LQ_ERR_DIMS), (dict(smooth=3), lq.LQ_ERR_DIMS),
+    (dict(dk=96, dv=96), lq.LQ_ERR_UNSUPPORTED), (dict(dk=128, dv=64), lq.LQ_ERR_UNSUPPORTED),
+    (dict(W=33), lq.LQ_ERR_UNSUPPORTED), (dict(C=9), lq.LQ_ERR_UNSUPPORTED),
+    (dict(dk=16, dv=16, W=4, C=1), lq.LQ_OK), (dict(dk=64, dv=64, W=32, C=8), lq.LQ_OK),
+])
+def test_check_dims(kw, status):
+    assert lq.load().lq_check_dims(ct.byref(_dims(**kw))) == status
+
+
+def _fake_state(C=4, misalign=None, null=None):
+    names = ("sq", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_k", "buf_y", "buf_u", "buf_g")
+    vals = []
+    for i, n in enumerate(names):
+        p = 0x100000 * (i + 1)
+        if n == misalign:
+            p += 4
+        if n == null:
+            p = None
+        vals.append(p)
+    return lq.lq_state(*vals)
+
+
+A = ct.c_void_p(0x7000000)      # an aligned address that is never dereferenced
+B4 = ct.c_void_p(0x7000004)
+
+
+def test_decode_argument_errors():
+    L = lq.load()
+    d = _dims()
+    st = _fake_state()
+    call = lambda dd, s, pos, *p: L.lq_gdn_decode_step(dd, s, pos, *p, None)
+    args = (A, A, A, A, A, A)
+    assert call(None, ct.byref(st), 0, *args) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), None, 0, *args) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), ct.byref(st), 16, *args) == lq.LQ_ERR_WINDOW_FULL
+    assert call(ct.byref(d), ct.byref(st), 99, *args) == lq.LQ_ERR_WINDOW_FULL
+    assert call(ct.byref(d), ct.byref(st), -1, *args) == lq.LQ_ERR_POS
+    assert call(ct.byref(d), ct.byref(st), 0, A, A, None, A, A, A) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), ct.byref(st), 0, A, B4, A, A, A, A) == lq.LQ_ERR_ALIGN
+    for n in ("sq", "buf_y", "comp_val"):
+        assert call(ct.byref(d), ct.byref(_fake_state(null=n)), 0, *args) == lq.LQ_ERR_NULL
+        assert call(ct.byref(d), ct.byref(_fake_state(misalign=n)), 0, *args) == lq.LQ_ERR_ALIGN
+    # beta and the scalar-mode alpha need only 4-byte alignment
+    assert call(ct.byref(d), ct.byref(st), 16, A, A, A, B4, B4, A) == lq.LQ_ERR_WINDOW_FULL
+    assert call(ct.byref(_dims(decay_mode=1)), ct.byref(st), 16, A, A, A, B4, A, A) == lq.LQ_ERR_ALIGN
+    assert call(ct.byref(d), ct.byref(st), 16, A, A, A, A, ct.c_void_p(0x7000002), A) == lq.LQ_ERR_ALIGN
+    # C = 0 does not need compensator arrays
+    d0 = _dims(C=0)
+    st0 = _fake_state(null="comp_idx")
+    assert call(ct.byref(d0), ct.byref(st0), 16, *args) == lq.LQ_ERR_WINDOW_FULL
+    assert call(ct.byref(_dims(dk=96, dv=96)), ct.byref(st), 0, *args) == lq.LQ_ERR_UNSUPPORTED
+
+
+def test_flush_and_codec_argument_errors():
+    L = lq.load()
+    d = _dims()
+    st = _fake_state()
+    assert L.lq_gdn_window_flush(ct.byref(d), ct.byref(st), -1, None, None) == lq.LQ_ERR_POS
+    assert L.lq_gdn_window_flush(ct.byref(d), ct.byref(st), 17, None, None) == lq.LQ_ERR_POS
+    assert L.lq_gdn_window_flush(ct.byref(d), ct.byref(st), 0, None, None) == lq.LQ_OK  # no-op
+    assert L.lq_gdn_window_flush(ct.byref(d), ct.byref(st), 3, B4, None) == lq.LQ_ERR_ALIGN
+    assert L.lq_gdn_window_flush(ct.byref(d), ct.byref(_fake_state(null="buf_g")), 3, None,
+                                 None) == lq.LQ_ERR_NULL
+    assert L.lq_gdn_state_quantize(ct.byref(d), None, ct.byref(st), None) == lq.LQ_ERR_NULL
+    assert L.lq_gdn_state_quantize(ct.byref(d), B4, ct.byref(st), None) == lq.LQ_ERR_ALIGN
+    assert L.lq_gdn_state_dequantize(ct.byref(d), ct.byref(st), None, None) == lq.LQ_ERR_NULL
+    # the codec calls do not need the window buffer
+    stq = _fake_state(null="buf_k")
+    assert L.lq_gdn_state_quantize(ct.byref(_dims(B=0)), A, ct.byref(stq), None) == lq.LQ_ERR_DIMS
+    assert L.lq_gdn_fp32_recurrence(ct.byref(d), A, -1, A, A, A, A, A, None, None) == lq.LQ_ERR_POS
+    assert L.lq_gdn_fp32_recurrence(ct.byref(d), A, 0, A, A, A, A, A, None, None) == lq.LQ_OK
+    assert L.lq_gdn_fp32_recurrence(ct.byref(d), A, 4, A, A, A, A, A, B4, None) == lq.LQ_ERR_ALIGN
+
+
+def test_status_strings():
+    L = lq.load()
+    for s in range(8):
+        assert L.lq_status_str(s)
+    assert L.lq_status_str(1234) == b"unknown status"
+    assert L.lq_last_hip_error() == 0

@@ -1,0 +1,281 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C ABI).
+
+Tolerances (written here, derived in the design notes):
+  o_t     <= 2e-3 max relative error, norm-wise per token and head;
+  h_out   <= 1e-5 (max-abs relative) against the oracle's fp64 state;
+  buffers <= 1e-5 per slot;
+  codec   bit-exact: the HIP flush's bytes equal the oracle codec of the
+          same fp32 state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from recurrent_state_quant_lq_amd import lq
+from recurrent_state_quant_lq_amd.configs import PRESETS
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import (BUF_TOL, H_TOL, O_TOL, codec_equal, dims_of, head_codec,  # noqa: E402
+                         rel_err, resync_run, say, upload_head_codec)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lq.load()
+
+
+def _check(rep, name):
+    say(f"{name}: windows {rep.windows} heads {rep.heads} o_err {rep.o_err:.3e} "
+        f"h_err {rep.h_err:.3e} buf_err {rep.buf_err:.3e} bytes_exact {rep.bytes_exact}")
+    assert rep.bytes_exact, rep.mismatches[:5]
+    assert rep.o_err <= O_TOL
+    assert rep.h_err <= H_TOL
+    assert rep.buf_err <= BUF_TOL
+
+
+# ---------------------------------------------------------------------------
+# workload presets
+# ---------------------------------------------------------------------------
+
+def test_tiny_gdn_all_windows():
+    wl = PRESETS["tiny_gdn"]
+    _check(resync_run(wl, [(0, 0)], host_tokens=True), "tiny_gdn")
+
+
+def test_gdn_layer_all_heads():
+    wl = PRESETS["gdn_layer"]
+    _check(resync_run(wl, [(0, h) for h in range(wl.H)], host_tokens=True), "gdn_layer")
+
+
+def test_gdn_batched_full_size_sampled():
+    wl = PRESETS["gdn_batched"]
+    sample = [(0, 0), (17, 5), (40, 31), (63, 31)]
+    _check(resync_run(wl, sample, host_tokens=False, T=256, log_every=8), "gdn_batched")
+
+
+def test_kda_full_size_sampled():
+    wl = PRESETS["kda"]
+    sample = [(0, 0), (9, 20), (31, 31)]
+    _check(resync_run(wl, sample, host_tokens=False, T=128, log_every=4), "kda")
+
+
+@pytest.mark.parametrize("W", [8, 16, 32])
+def test_outlier_sweep_full_size_sampled(W):
+    wl = PRESETS["outlier_sweep"]
+    sample = [(0, 3), (255, 31)]
+    _check(resync_run(wl, sample, host_tokens=False, W=W, T=2 * W + 3, log_every=0),
+           f"outlier_sweep W={W}")
+
+
+# ---------------------------------------------------------------------------
+# smaller shapes, ragged windows, degenerate settings
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,W,C,kda,smooth,T", [
+    (16, 4, 1, False, 1, 23),     # ragged last window
+    (16, 16, 0, True, 0, 40),
+    (64, 8, 8, True, 1, 21),
+    (64, 32, 3, False, 1, 70),
+    (128, 1, 0, False, 0, 7),     # W = 1: per-token quantization
+    (128, 16, 4, True, 1, 37),
+    (128, 32, 8, True, 0, 33),
+    (128, 5, 2, False, 1, 12),    # W not a power of two
+])
+def test_shapes_and_edges(dk, W, C, kda, smooth, T):
+    wl = PRESETS["gdn_layer"].with_(B=2, H=3, dk=dk, dv=dk, W=W, C=C, T=T, prefill=40,
+                                    decay=1 if kda else 0, smooth=smooth, seed=77 + dk + W)
+    sample = [(b, h) for b in range(2) for h in range(3)]
+    _check(resync_run(wl, sample, host_tokens=True), f"shape dk={dk} W={W} C={C} kda={kda}")
+
+
+def test_outlier_inputs_small():
+    wl = PRESETS["outlier_sweep"].with_(B=2, H=4, T=40, prefill=64, seed=5)
+    _check(resync_run(wl, [(b, h) for b in range(2) for h in range(4)], host_tokens=True),
+           "outliers small")
+
+
+def test_beta_zero_pure_decay():
+    """beta = 0: the state only decays; o = Hb^T (exp(g_n) o q)."""
+    wl = PRESETS["gdn_layer"].with_(B=1, H=2, T=20, prefill=30, beta_lo=0.0, beta_hi=0.0, seed=9)
+    _check(resync_run(wl, [(0, 0), (0, 1)], host_tokens=True), "beta=0")
+
+
+# ---------------------------------------------------------------------------
+# codec kernels: bit-exact quantizer, dequantizer
+# ---------------------------------------------------------------------------
+
+def _adversarial(rng, dk, dv):
+    mats = []
+    z = np.zeros((dk, dv), np.float32)
+    mats.append(z)                                                  # all zero
+    m = rng.standard_normal((dk, dv)).astype(np.float32)
+    m[5] = 0; m[:, 7] = 0                                           # zero row and column
+    mats.append(m)
+    t = rng.integers(-3, 4, (dk, dv)).astype(np.float32)            # ties everywhere
+    mats.append(t)
+    e = (rng.standard_normal((dk, dv)) * np.exp(rng.uniform(-30, 30, (dk, 1)))).astype(np.float32)
+    mats.append(e)                                                  # huge row dynamic range
+    dn = (rng.standard_normal((dk, dv)) * 1e-39).astype(np.float32)  # denormals
+    dn[0, 0] = 1e-38
+    mats.append(dn)
+    h = (rng.integers(-254, 255, (dk, dv)) / 2.0).astype(np.float32)  # half-way values
+    h[:, 0] = 127.0
+    mats.append(h)
+    nz = rng.standard_normal((dk, dv)).astype(np.float32)
+    nz[nz > 1.5] = -0.0                                             # negative zeros
+    mats.append(nz)
+    o = rng.standard_normal((dk, dv)).astype(np.float32)
+    o[[1, 9, 30 % dk, dk - 1]] *= 1000                             # outlier rows
+    o[:, [2, dv - 3]] *= 300                                        # outlier columns
+    mats.append(o)
+    return mats
+
+
+@pytest.mark.parametrize("dk,C,smooth", [(16, 1, 1), (64, 8, 0), (128, 4, 1), (128, 0, 1), (128, 8, 1)])
+def test_quantize_kernel_bit_exact(dk, C, smooth):
+    rng = np.random.default_rng(dk + C)
+    mats = _adversarial(rng, dk, dk)
+    B = len(mats)
+    d = lq.make_dims(B, 1, dk, dk, 16, C, 0, smooth)
+    st = lq.LayerState.allocate(d)
+    h = torch.from_numpy(np.stack(mats)[:, None]).cuda()
+    lq.lq_gdn_state_quantize(st, h)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.quantize(mats[b], C, smooth)
+        assert codec_equal(head_codec(st, b, 0), ref), f"matrix {b}"
+    # dequantize kernel: fp32 (q*r)*s against the oracle's fp64 value
+    hd = torch.empty_like(h)
+    lq.lq_gdn_state_dequantize(st, hd)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.dequantize(O.quantize(mats[b], C, smooth))
+        got = hd[b, 0].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 2.5 * np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) + 1e-45)
+
+
+# ---------------------------------------------------------------------------
+# fp32-state recurrence kernel
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,kda", [(16, False), (64, True), (128, False), (128, True)])
+def test_fp32_recurrence_kernel(dk, kda):
+    from recurrent_state_quant_lq_amd import inputs
+    B, H, T = 2, 3, 40
+    tok = inputs.host_tokens(31 + dk, T, B, H, dk, dk, per_key=kda, beta_lo=0.1, beta_hi=0.9)
+    d = lq.make_dims(B, H, dk, dk, 16, 0, int(kda), 1)
+    rng = np.random.default_rng(dk)
+    H0 = (rng.standard_normal((B, H, dk, dk)) * 0.3).astype(np.float32)
+    h = torch.from_numpy(H0).cuda()
+    o = torch.empty((T, B, H, dk), dtype=torch.float32, device="cuda")
+    tk = {k: torch.from_numpy(v).cuda() for k, v in tok.items()}
+    lq.lq_gdn_fp32_recurrence(d, h, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], o)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for hh in range(H):
+            ht = O.head_tokens(tok, b, hh)
+            o_ref, _, H_ref, _ = O.run_head(dk, dk, kda, T, 0, 1, route=0, use_codec=False, tok=ht,
+                                            H0=H0[b, hh].astype(np.float64))
+            assert rel_err(o[:, b, hh].cpu().numpy(), o_ref) < 1e-5
+            assert np.abs(h[b, hh].cpu().numpy() - H_ref).max() / np.abs(H_ref).max() < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# memory safety and determinism
+# ---------------------------------------------------------------------------
+
+GUARD = 4096
+
+
+def _guarded(shape, dtype, fill):
+    n = int(np.prod(shape))
+    base = torch.full((n + 2 * GUARD,), fill, dtype=dtype, device="cuda")
+    return base, base[GUARD:GUARD + n].view(shape)
+
+
+def test_canaries_and_untouched_slots():
+    """Every array sits between guard regions; decode at slot n writes only
+    slot n of the buffer; nothing is written outside the arrays."""
+    d = lq.make_dims(3, 5, 128, 128, 16, 4, 1, 1)
+    B, H, dk, W, C = 3, 5, 128, 16, 4
+    arrays = {}
+    spec = dict(sq=((B, H, dk, dk), torch.int8), row_scale=((B, H, dk), torch.float32),
+                col_scale=((B, H, dk), torch.float32), comp_idx=((B, H, C), torch.int32),
+                comp_val=((B, H, C, dk), torch.float32), buf_k=((B, H, W, dk), torch.float32),
+                buf_y=((B, H, W, dk), torch.float32), buf_u=((B, H, W, dk), torch.float32),
+                buf_g=((B, H, W, dk), torch.float32))
+    for name, (shape, dt) in spec.items():
+        arrays[name] = _guarded(shape, dt, 7)
+    st = lq.LayerState(d, *[arrays[n][1] for n in spec])
+    rng = np.random.default_rng(3)
+    hq = torch.from_numpy((rng.standard_normal((B, H, dk, dk)) * 0.1).astype(np.float32)).cuda()
+    lq.lq_gdn_state_quantize(st, hq)
+    from recurrent_state_quant_lq_amd import inputs
+    tok = inputs.host_tokens(4, 6, B, H, dk, dk, per_key=True, beta_lo=0.1, beta_hi=0.9)
+    tk = {k: torch.from_numpy(v).cuda() for k, v in tok.items()}
+    ob, o = _guarded((B, H, dk), torch.float32, 7)
+    hb, hout = _guarded((B, H, dk, dk), torch.float32, 7)
+    for n in range(6):
+        before = {k: getattr(st, "buf_" + k).clone() for k in ("k", "y", "u", "g")}
+        lq.lq_gdn_decode_step(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o)
+        torch.cuda.synchronize()
+        for k in ("k", "y", "u", "g"):
+            after = getattr(st, "buf_" + k)
+            keep = [i for i in range(W) if i != n]
+            assert torch.equal(after[:, :, keep], before[k][:, :, keep]), (k, n)
+    lq.lq_gdn_window_flush(st, 6, hout)
+    torch.cuda.synchronize()
+    for name, (base, view) in list(arrays.items()) + [("o", (ob, o)), ("h_out", (hb, hout))]:
+        g = base.cpu()
+        assert (g[:GUARD] == 7).all() and (g[-GUARD:] == 7).all(), name
+
+
+def test_run_to_run_bitwise_determinism():
+    wl = PRESETS["kda"].with_(B=4, H=8, T=20, prefill=0, seed=12)
+    outs = []
+    for rep in range(2):
+        d = dims_of(wl)
+        st = lq.LayerState.allocate(d)
+        from recurrent_state_quant_lq_amd import inputs
+        tok = inputs.host_tokens(wl.seed, wl.T, wl.B, wl.H, wl.dk, wl.dv, per_key=True,
+                                 beta_lo=0.1, beta_hi=0.9)
+        tk = {k: torch.from_numpy(v).cuda() for k, v in tok.items()}
+        o = torch.empty((wl.B, wl.H, wl.dv), device="cuda")
+        hout = torch.empty((wl.B, wl.H, wl.dk, wl.dv), device="cuda")
+        acc = []
+        for t in range(wl.T):
+            n = t % wl.W
+            lq.lq_gdn_decode_step(st, n, tk["q"][t], tk["k"][t], tk["v"][t], tk["alpha"][t], tk["beta"][t], o)
+            acc.append(o.clone())
+            if n == wl.W - 1 or t == wl.T - 1:
+                lq.lq_gdn_window_flush(st, n + 1, hout)
+                acc.append(hout.clone())
+                acc.append(st.sq.clone().float())
+        torch.cuda.synchronize()
+        outs.append(acc)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_flush_with_zero_buffered_is_noop():
+    d = lq.make_dims(2, 2, 64, 64, 8, 2, 0, 1)
+    st = lq.LayerState.allocate(d)
+    st.sq.fill_(3)
+    before = st.sq.clone()
+    lq.lq_gdn_window_flush(st, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(st.sq, before)
+
+
+def test_window_full_is_rejected():
+    d = lq.make_dims(1, 1, 16, 16, 4, 1, 0, 1)
+    st = lq.LayerState.allocate(d)
+    z = torch.zeros((1, 1, 16), device="cuda")
+    with pytest.raises(lq.LQError) as e:
+        lq.lq_gdn_decode_step(st, 4, z, z, z, torch.ones((1, 1), device="cuda"),
+                              torch.zeros((1, 1), device="cuda"), z)
+    assert e.value.status == lq.LQ_ERR_WINDOW_FULL

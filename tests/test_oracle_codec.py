@@ -169,3 +169,23 @@ def test_compensators_and_smoothing_reduce_error(orc):
     base, comp, both = mse(0, 0), mse(4, 0), mse(4, 1)
     assert comp < 0.5 * base
     assert both < comp
+
+
+@pytest.mark.parametrize("smooth", [0, 1])
+def test_tiny_magnitudes_stay_finite(orc, smooth):
+    """Rows or columns below 2^-120 count as zero: every codec value stays
+    finite and the reconstruction error of such a row is below 2^-120."""
+    rng = np.random.default_rng(90)
+    H = rng.standard_normal((32, 16)).astype(np.float32)
+    H[3] *= np.float32(1e-38)                   # a row in the denormal range
+    H[7] *= np.float32(2.0 ** -125)
+    H[:, 5] *= np.float32(1e-39)                # a tiny column
+    D = (rng.standard_normal((16, 16)) * 1e-39).astype(np.float32)   # all denormal
+    for M in (H, D, np.full((8, 8), np.float32(2.0 ** -121))):
+        cd = orc.quantize(M, 1, smooth)
+        for key in ("r", "s", "cv"):
+            assert np.isfinite(cd[key]).all()
+        assert np.abs(cd["sq"].astype(int)).max() <= 127
+        err = np.abs(orc.dequantize(cd) - M.astype(np.float64))
+        lsb = cd["r"].astype(np.float64)[:, None] * cd["s"].astype(np.float64)[None, :]
+        assert (err <= np.maximum(lsb * (0.5 + 1e-4), 2.0 ** -120)).all()
