@@ -21,6 +21,9 @@
  * Stored state (the "codec"; [news ¶5]: 1.19 bytes per value at
  * dk = dv = 128, C = 4):  H = deq + sum_c e_{idx_c} cv_c^T with
  * deq_ij = sq_ij * row_scale_i * col_scale_j,  sq int8 in [-127, 127].
+ * The int8 matrix is stored value-column-major: element (i, j) of H's
+ * quantized residual is sq[j*dk + i], so each value column's dk key-channel
+ * bytes are contiguous (the operand layout of the int8 matrix cores).
  * It stays fixed for a window of W tokens ([news ¶3]); the window's updates
  * live in an fp32 buffer (WY form, see lq_gdn_decode_step) and the state is
  * rebuilt and requantized once at the window's end (lq_gdn_window_flush).
@@ -74,7 +77,7 @@ typedef struct lq_dims {
 
 /* Device arrays of one layer's quantized state and window buffer.
  * gd = dk for LQ_DECAY_PER_KEY, 1 for LQ_DECAY_SCALAR.
- *   sq        int8  [B,H,dk,dv]   quantized residual
+ *   sq        int8  [B,H,dv,dk]   quantized residual, value-column-major
  *   row_scale fp32  [B,H,dk]      per-row scale (0 for an all-zero row)
  *   col_scale fp32  [B,H,dv]      per-column smoothing factor
  *   comp_idx  int32 [B,H,C]       compensator rows, ascending
@@ -151,8 +154,9 @@ int lq_gdn_window_flush(const lq_dims *d, const lq_state *st, int32_t n_buffered
 int lq_gdn_state_quantize(const lq_dims *d, const float *h, const lq_state *st, void *stream);
 
 /*
- * Writes the fp32 state the codec stands for into h_out [B,H,dk,dv]:
- * (sq_ij * row_scale_i) * col_scale_j, with compensator rows set to comp_val.
+ * Writes the fp32 state the codec stands for into h_out [B,H,dk,dv]
+ * (row-major): (sq_ij * row_scale_i) * col_scale_j, plus comp_val on the
+ * compensator rows.
  */
 int lq_gdn_state_dequantize(const lq_dims *d, const lq_state *st, float *h_out, void *stream);
 

@@ -9,18 +9,25 @@
 //     o = Hb^T q' + sum_{i<=n} a_i u_i,   q' = exp(g_n) o q - sum_{i<=n} a_i y_i,
 // and Hb^T q' = s o (sq^T (r o q')) + sum_c q'[idx_c] cv_c.
 //
-// One workgroup per (b, h).  Every global load the step needs is issued at
-// the top (the int8 state as 128-bit loads, the buffer rows, the inputs), so
-// the dependent chain buffer-dots -> q' -> int8 GEMV runs on data already
-// in flight.  Threads play three roles:
-//   * slot groups: TPS lanes per buffer slot compute rr_i = <k, E_i o k_i>
-//     and a_i = <q, E_i o k_i> (lane-group reductions);
-//   * channel threads t < DK own key channel t: y_n[t] and q'[t];
-//   * value threads DK <= t < DK+DV own value column j: u_n[j], the buffer
-//     part of o[j] and the final output;
-//   * all threads: the int8 GEMV, VEC bytes x PASSES rows each, partial sums
-//     reduced through LDS.
+// One workgroup per (b, h); at dk = dv = 128 it has 256 lanes and at most 64
+// VGPRs, so 8 workgroups share a CU and one dispatch covers B*H = 2048 heads
+// on 256 CUs.  Every load of the step is issued before the first barrier:
+//   * per-head vectors (q, k, v, row and column scales, per-key decay,
+//     compensator rows) and the buffered keys go straight to LDS
+//     (global_load_lds_dwordx4, no registers);
+//   * the int8 state goes to VGPRs as the A operands of int8 MFMAs: the state
+//     is stored value-column-major (sq[j][i]), so 16 consecutive key channels
+//     of one value column are one 16-byte load;
+//   * each channel lane holds its column of Y, each value lane its column of U.
+// Then:
+//   1. slot groups: rr_i = <k, E_i o k_i>, a_i = <q, E_i o k_i>
+//   2. channel lanes t < DK: y_n[t], q'[t], q''[t] = r[t] q'[t] and three int8
+//      digits of q'' per 64-channel block; value lanes: u_n[j], sum_i a_i u_i[j]
+//   3. int8 MFMA: sq^T x digits, recombined to fp32 (wave w owns its columns)
+//   4. value lanes: o[j] = s_j (sq^T q'')_j + compensators + buffer term.
 #include "lq_internal.h"
+
+#include <utility>
 
 namespace lq {
 namespace {
@@ -46,143 +53,220 @@ struct DecodeArgs {
     int pos;
 };
 
-template <int DK, int DV, int WM, bool KDA, int NT>
-__global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
-    static_assert(NT >= DK + DV, "one thread per key channel and per value column");
-    constexpr int GD = KDA ? DK : 1;
-    // int8 GEMV tiling
-    constexpr int VEC = (DK * DV / 16 >= NT) ? 16 : 4;   // bytes per thread per row
-    constexpr int CPR = DV / VEC;                         // chunks per row
-    constexpr int RPP = NT / CPR;                         // rows per pass
-    constexpr int PASSES = DK / RPP;
-    static_assert(NT % CPR == 0 && DK % RPP == 0 && PASSES >= 1, "GEMV tiling");
-    // buffer-dot tiling
-    constexpr int TPS = NT / WM;                          // lanes per slot
-    constexpr int CH = DK / TPS;                          // channels per lane
-    static_assert(TPS <= 64 && CH >= 1 && DK % TPS == 0, "slot-group tiling");
+constexpr int CMAX = 8;
 
-    __shared__ float s_rr[WM];
-    __shared__ float s_a[WM];
-    __shared__ float s_q2[DK];
-    __shared__ float s_qp[DK];
-    __shared__ __align__(16) float s_red[RPP][DV];
+template <int DK, int DV, int WM, bool KDA>
+struct Dec {
+    static_assert(DK == DV, "square heads");
+    static constexpr int NT = (DK + DV) < 64 ? 64 : DK + DV;
+    static constexpr int NW = NT / 64;
+    static constexpr int GD = KDA ? DK : 1;
+    // int8 MFMA GEMV: 16-column tiles, 64-channel K steps
+    static constexpr int NTILE = DV / 16;
+    static constexpr int TPW = (NTILE + NW - 1) / NW;    // tiles per wave
+    static constexpr int KS = (DK + 63) / 64;            // K steps (= channel waves)
+    // slot groups: TPS lanes per slot, CH channels per lane, SPR slots per
+    // round, ROUNDS rounds
+    static constexpr int TPS0 = NT / WM > 32 ? NT / WM : 32;
+    static constexpr int TPS = TPS0 < DK ? TPS0 : DK;
+    static constexpr int CH = DK / TPS;
+    static constexpr int SPR = NT / TPS;
+    static constexpr int ROUNDS = (WM + SPR - 1) / SPR;
+    static_assert(TPS <= 64 && CH >= 1 && DK % TPS == 0 && NT % TPS == 0, "slot tiling");
+    // LDS vector region: DK-float segments
+    //   q k v r s [alpha gprev] cv_0..cv_{CMAX-1} k_0..k_{WM-2}
+    static constexpr int SQ = 0, SK = 1, SV = 2, SR = 3, SS = 4, SA = 5, SG = 6;
+    static constexpr int SCV = KDA ? 7 : 5;
+    static constexpr int SKB = SCV + CMAX;
+    static constexpr int NSEG = SKB + (WM > 1 ? WM - 1 : 1);
+    static constexpr int SEGL = DK / 4;                  // lanes (16-byte chunks) per segment
+    static_assert(DK % 4 == 0 && 64 % SEGL == 0 && SCV * SEGL <= NT, "segments");
+    // waves per SIMD the register budget is sized for (8: all 8 workgroups of a
+    // CU resident; per-key decay needs more registers for its decay rows)
+    static constexpr int WPE = WM <= 16 ? (KDA ? 6 : 8) : 4;
+};
+
+template <int DK, int DV, int WM, bool KDA, int NB>
+__global__ __launch_bounds__((Dec<DK, DV, WM, KDA>::NT))
+__attribute__((amdgpu_waves_per_eu(Dec<DK, DV, WM, KDA>::WPE, Dec<DK, DV, WM, KDA>::WPE)))
+void decode_kernel(DecodeArgs a) {
+    using D = Dec<DK, DV, WM, KDA>;
+    constexpr int NT = D::NT, GD = D::GD, TPW = D::TPW, KS = D::KS, NTILE = D::NTILE;
+    constexpr int TPS = D::TPS, CH = D::CH, SPR = D::SPR, ROUNDS = D::ROUNDS;
+    constexpr int SEGL = D::SEGL;
+
+    __shared__ __align__(16) float s_vec[D::NSEG * DK];
+    __shared__ __align__(16) float s_rr[WM];
+    __shared__ __align__(16) float s_a[WM];
+    __shared__ __align__(16) float s_qp[DK];
+    __shared__ __align__(16) int8_t s_dig[3][KS * 64];
+    __shared__ __align__(16) float s_msc[KS];
+    __shared__ __align__(16) float s_gem[DV];
+    // dwords 0..7: compensator rows; 8: beta; 9: alpha (scalar decay); 10: g_{n-1} (scalar decay)
+    __shared__ __align__(16) int s_misc[16];
 
     const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const size_t head = blockIdx.x;
-    const int n = a.pos;
-    const int W = a.W;
-    const int C = a.C;
+    const int n = NB >= 0 ? NB : a.pos;
+    const int W = a.W, C = a.C;
 
-    const int8_t* __restrict__ sq = a.sq + head * (DK * DV);
-    const float* __restrict__ bk = a.bk + head * (size_t)W * DK;
-    const float* __restrict__ by = a.by + head * (size_t)W * DK;
-    const float* __restrict__ bu = a.bu + head * (size_t)W * DV;
-    const float* __restrict__ bg = a.bg + head * (size_t)W * GD;
-    const float* __restrict__ qv = a.q + head * DK;
-    const float* __restrict__ kv = a.k + head * DK;
-    const float* __restrict__ av = a.alpha + head * GD;
+    const float* __restrict__ bkr = a.bk + head * (size_t)W * DK;
+    const float* __restrict__ byr = a.by + head * (size_t)W * DK;
+    const float* __restrict__ bur = a.bu + head * (size_t)W * DV;
+    const float* __restrict__ bgr = a.bg + head * (size_t)W * GD;
 
-    // ---- issue loads: int8 state chunks -----------------------------------
-    using chunk_t = typename std::conditional<VEC == 16, uint4, uint32_t>::type;
-    chunk_t ch[PASSES];
-    const int g_row = t / CPR;
-    const int g_col = (t % CPR) * VEC;
+    // ---- per-head vectors, compensator rows and buffered keys -> LDS ----------------------
+    // Three contiguous copies, 16-byte chunk c of a region landing at region + 4c floats
+    // (lane l of a wave writes its wave's base + 16*l bytes).
+    {
+        // q k v r s [alpha gprev]: segment sg = t / SEGL, one chunk per lane
+        constexpr int NVS = D::SCV;
+        const int sg = t / SEGL, off = 4 * (t % SEGL);
+        const float* src = nullptr;
+        switch (sg) {
+            case D::SQ: src = a.q + head * DK; break;
+            case D::SK: src = a.k + head * DK; break;
+            case D::SV: src = a.v + head * DV; break;
+            case D::SR: src = a.r + head * DK; break;
+            case D::SS: src = a.s + head * DV; break;
+            default:
+                if constexpr (KDA) {
+                    if (sg == D::SA) src = a.alpha + head * DK;
+                    else if (sg == D::SG && n > 0) src = bgr + (size_t)(n - 1) * DK;
+                }
+        }
+        if (sg < NVS && src) lds_dma16(src + off, s_vec + 4 * 64 * w);
+        // compensator rows: C*DV contiguous floats
+        const int ccv = C * DV / 4;
+        if (t < ccv) lds_dma16(a.cv + head * (size_t)C * DV + 4 * t, s_vec + D::SCV * DK + 4 * 64 * w);
+        // buffered keys k_0 .. k_{n-1}: n*DK contiguous floats
+        const int ckb = n * DK / 4;
+        for (int base = 0; base < ckb; base += NT) {
+            const int c = base + t;
+            if (c < ckb) lds_dma16(bkr + 4 * c, s_vec + D::SKB * DK + 4 * (base + 64 * w));
+        }
+        if (w == 0) {
+            const void* src4 = nullptr;
+            if (lane < C) src4 = a.idx + head * C + lane;
+            else if (lane == 8) src4 = a.beta + head;
+            else if (!KDA && lane == 9) src4 = a.alpha + head;
+            else if (!KDA && lane == 10 && n > 0) src4 = bgr + (n - 1);
+            if (src4) lds_dma4(src4, s_misc);
+        }
+    }
+
+    // ---- int8 state -> VGPRs (MFMA A operands) ------------------------------------------
+    // lane l of wave w: column j = tile*16 + l%16, channels ks*64 + 16*(l/16) .. +15
+    v4i sqa[TPW][KS];
+    {
+        // Every tile and K step is real when the shape divides evenly; the loads
+        // are then unconditional, so no register merge waits on them.
+        constexpr bool FULL = (NTILE % D::NW == 0) && (DK % 64 == 0);
+        const int8_t* sq = a.sq + head * (DK * DV);
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-        ch[p] = *reinterpret_cast<const chunk_t*>(sq + (size_t)(p * RPP + g_row) * DV + g_col);
+        for (int tw = 0; tw < TPW; ++tw)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int tile = w * TPW + tw;
+                const int i0 = ks * 64 + 16 * (lane / 16);
+                if (FULL || (tile < NTILE && i0 < DK))
+                    sqa[tw][ks] = *reinterpret_cast<const v4i*>(sq + (size_t)(tile * 16 + lane % 16) * DK + i0);
+                else
+                    sqa[tw][ks] = v4i{0, 0, 0, 0};
+            }
+    }
 
-    // ---- slot-group loads ----------------------------------------------------
-    const int slot = t / TPS;
+    // ---- buffer rows -> VGPRs -------------------------------------------------------------
+    const int slot0 = t / TPS;
     const int c0 = (t % TPS) * CH;
-    float kq[CH], kk[CH], ks[CH], gs[CH], gp[CH], al[CH];
-    load_floats<CH>(qv + c0, kq);
-    load_floats<CH>(kv + c0, kk);
-    if (slot < n) {
-        load_floats<CH>(bk + (size_t)slot * DK + c0, ks);
-        if constexpr (KDA) load_floats<CH>(bg + (size_t)slot * DK + c0, gs);
-        else gs[0] = bg[slot];
+    // decay rows of the slot groups; the slot index is clamped into the buffer so
+    // the loads are unconditional (values of slots >= n are never used)
+    float gs[ROUNDS][KDA ? CH : 1];
+    float gslot[ROUNDS];
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+        const int slot = min(slot0 + rd * SPR, W - 1);
+        if constexpr (KDA) load_floats<CH>(bgr + (size_t)slot * DK + c0, gs[rd]);
+        else gslot[rd] = bgr[slot];
     }
-    if constexpr (KDA) {
-        load_floats<CH>(av + c0, al);
-        if (n > 0) load_floats<CH>(bg + (size_t)(n - 1) * DK + c0, gp);
-    }
-    const float beta = a.beta[head];
-    const float gprev_s = (!KDA && n > 0) ? bg[n - 1] : 0.0f;
-    const float gn_s = KDA ? 0.0f : gprev_s + logf(av[0]);
-
-    // ---- channel / value thread loads --------------------------------------
-    constexpr int CMAX = 8;
-    float col[WM > 1 ? WM - 1 : 1];
     const bool is_ch = t < DK;
     const bool is_val = t >= DK && t < DK + DV;
     const int j = t - DK;
-    float x_q = 0.0f, x_k = 0.0f, x_r = 0.0f, x_g = 0.0f;   // channel thread
-    float x_v = 0.0f, x_s = 0.0f;                           // value thread
-    float cvr[CMAX];
-    int cid[CMAX];
+    float col[WM > 1 ? WM - 1 : 1];
     if (is_ch) {
 #pragma unroll
         for (int i = 0; i < WM - 1; ++i)
-            if (i < n) col[i] = by[(size_t)i * DK + t];
-        x_q = qv[t];
-        x_k = kv[t];
-        x_r = a.r[head * DK + t];
-        if constexpr (KDA) x_g = (n > 0 ? bg[(size_t)(n - 1) * DK + t] : 0.0f) + logf(av[t]);
+            if (i < n) col[i] = byr[(size_t)i * DK + t];
     } else if (is_val) {
 #pragma unroll
         for (int i = 0; i < WM - 1; ++i)
-            if (i < n) col[i] = bu[(size_t)i * DV + j];
-        x_v = a.v[head * DV + j];
-        x_s = a.s[head * DV + j];
-#pragma unroll
-        for (int c = 0; c < CMAX; ++c)
-            if (c < C) {
-                cid[c] = a.idx[head * C + c];
-                cvr[c] = a.cv[(head * C + c) * (size_t)DV + j];
-            }
+            if (i < n) col[i] = bur[(size_t)i * DV + j];
     }
 
-    // ---- 1. buffer inner products -------------------------------------------
+    all_loads_barrier();
+
+    const float beta = __int_as_float(s_misc[8]);
+    float gn_s = 0.0f;
+    if constexpr (!KDA) gn_s = (n > 0 ? __int_as_float(s_misc[10]) : 0.0f) + logf(__int_as_float(s_misc[9]));
+
+    // ---- 1. buffer inner products ---------------------------------------------------------
     {
-        float rr = 0.0f, aa = 0.0f;
-        if (slot < n) {
-            if constexpr (KDA) {
+        float kq[CH], kk[CH];
+        load_floats<CH>(s_vec + D::SQ * DK + c0, kq);
+        load_floats<CH>(s_vec + D::SK * DK + c0, kk);
 #pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    const float gnc = (n > 0 ? gp[c] : 0.0f) + logf(al[c]);
-                    const float e = __expf(gnc - gs[c]);
-                    const float x = ks[c] * e;
-                    rr += kk[c] * x;
-                    aa += kq[c] * x;
-                }
-            } else {
-                const float e = __expf(gn_s - gs[0]);
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+            const int slot = slot0 + rd * SPR;
+            if (rd * SPR > n) break;                      // uniform: no slot <= n left
+            float rr = 0.0f, aa = 0.0f;
+            if (slot < n) {
+                float ks[CH];
+                load_floats<CH>(s_vec + (D::SKB + slot) * DK + c0, ks);
+                if constexpr (KDA) {
+                    float al[CH], gp[CH];
+                    load_floats<CH>(s_vec + D::SA * DK + c0, al);
+                    if (n > 0) load_floats<CH>(s_vec + D::SG * DK + c0, gp);
 #pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    rr += kk[c] * ks[c];
-                    aa += kq[c] * ks[c];
+                    for (int c = 0; c < CH; ++c) {
+                        const float gnc = (n > 0 ? gp[c] : 0.0f) + logf(al[c]);
+                        const float x = ks[c] * __expf(gnc - gs[rd][c]);
+                        rr += kk[c] * x;
+                        aa += kq[c] * x;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        rr += kk[c] * ks[c];
+                        aa += kq[c] * ks[c];
+                    }
+                    const float e = __expf(gn_s - gslot[rd]);
+                    rr *= e;
+                    aa *= e;
                 }
-                rr *= e;
-                aa *= e;
+            } else if (slot == n) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) aa += kq[c] * kk[c];
             }
-        } else if (slot == n) {
-#pragma unroll
-            for (int c = 0; c < CH; ++c) aa += kq[c] * kk[c];
-        }
-        rr = group_sum<TPS>(rr);
-        aa = group_sum<TPS>(aa);
-        if ((t % TPS) == 0 && slot <= n) {
-            s_rr[slot] = rr;
-            s_a[slot] = aa;
+            rr = group_sum<TPS>(rr);
+            aa = group_sum<TPS>(aa);
+            if ((t % TPS) == 0 && slot <= n) {
+                s_rr[slot] = rr;
+                s_a[slot] = aa;
+            }
         }
     }
     lds_barrier();
 
-    // ---- 2. WY append and transformed query ---------------------------------
-    float wsum = 0.0f;   // value threads: sum_{i<=n} a_i u_i[j]
+    // ---- 2. WY append, transformed query and its int8 digits ---------------------------------
+    float wsum = 0.0f;
+    float q2 = 0.0f;
     if (is_ch) {
-        const float qc = x_q, kc = x_k;
-        const float gn = KDA ? x_g : gn_s;
+        const float qc = s_vec[D::SQ * DK + t], kc = s_vec[D::SK * DK + t];
+        float gn;
+        if constexpr (KDA) gn = (n > 0 ? s_vec[D::SG * DK + t] : 0.0f) + logf(s_vec[D::SA * DK + t]);
+        else gn = gn_s;
         const float en = __expf(gn);
         float ay = en * kc, aq = en * qc;
 #pragma unroll
@@ -193,16 +277,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
             }
         const float yn = beta * ay;
         const float qp = aq - s_a[n] * yn;
-        float* byw = a.by + head * (size_t)W * DK + (size_t)n * DK;
-        float* bkw = a.bk + head * (size_t)W * DK + (size_t)n * DK;
-        byw[t] = yn;
-        bkw[t] = kc;
+        a.by[head * (size_t)W * DK + (size_t)n * DK + t] = yn;
+        a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = kc;
         if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = gn;
         else if (t == 0) a.bg[head * (size_t)W + n] = gn;
         s_qp[t] = qp;
-        s_q2[t] = x_r * qp;
+        q2 = s_vec[D::SR * DK + t] * qp;
     } else if (is_val) {
-        float au = x_v;
+        float au = s_vec[D::SV * DK + j];
 #pragma unroll
         for (int i = 0; i < WM - 1; ++i)
             if (i < n) {
@@ -213,60 +295,93 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         wsum += s_a[n] * un;
         a.bu[head * (size_t)W * DV + (size_t)n * DV + j] = un;
     }
-    lds_barrier();
-
-    // ---- 3. int8 GEMV: partial sums of sq^T (r o q') ------------------------
-    {
-        float acc[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const float x = s_q2[p * RPP + g_row];
-            if constexpr (VEC == 16) {
-                const uint32_t w4[4] = {ch[p].x, ch[p].y, ch[p].z, ch[p].w};
-#pragma unroll
-                for (int wi = 0; wi < 4; ++wi)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[4 * wi + e] += x * sbyte(w4[wi], e);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] += x * sbyte(ch[p], e);
-            }
-        }
-        store_floats<VEC>(&s_red[g_row][g_col], acc);
+    if (w < KS) {
+        // this wave's 64 channels form one block: scale M = max |q''|, digits of q''
+        const float m = group_max<64>(fabsf(q2));
+        const float inv = m > 0.0f ? 127.0f / m : 0.0f;
+        int d0, d1, d2;
+        digits3(q2, inv, d0, d1, d2);
+        s_dig[0][t] = (int8_t)d0;
+        s_dig[1][t] = (int8_t)d1;
+        s_dig[2][t] = (int8_t)d2;
+        if (lane == 0) s_msc[w] = m * (1.0f / 127.0f);
     }
     lds_barrier();
 
-    // ---- 4. output ------------------------------------------------------------
-    if (is_val) {
-        float gem = 0.0f;
+    // ---- 3. int8 MFMA: (sq^T q'') for this wave's column tiles --------------------------------
+    {
+        const int dgt = lane % 16;                    // B column = digit index (0..2), rest zero
+        const float wd = dgt == 0 ? 1.0f : dgt == 1 ? kDigitW1 : dgt == 2 ? kDigitW2 : 0.0f;
+        float fk[KS];
+        v4i bop[KS];
 #pragma unroll
-        for (int g = 0; g < RPP; ++g) gem += s_red[g][j];
-        float out = x_s * gem + wsum;
+        for (int ks = 0; ks < KS; ++ks) {
+            fk[ks] = wd * s_msc[ks];
+            bop[ks] = dgt < 3 ? *reinterpret_cast<const v4i*>(&s_dig[dgt][ks * 64 + 16 * (lane / 16)])
+                              : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int tw = 0; tw < TPW; ++tw) {
+            const int tile = w * TPW + tw;
+            if (tile >= NTILE) break;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const v4i dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(sqa[tw][ks], bop[ks],
+                                                                     v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] += (float)dd[v] * fk[ks];
+            }
+            // the digit-0 lane gathers digits 1 and 2 from the next two lanes
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] += dpp<DPP_SHL1>(acc[v]) + dpp<DPP_SHL2>(acc[v]);
+            if (dgt == 0)
+                *reinterpret_cast<float4*>(&s_gem[tile * 16 + 4 * (lane / 16)]) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    }
+    lds_barrier();
+
+    // ---- 4. output ------------------------------------------------------------------------------
+    if (is_val) {
+        float out = s_vec[D::SS * DK + j] * s_gem[j] + wsum;
 #pragma unroll
         for (int c = 0; c < CMAX; ++c)
-            if (c < C) out += s_qp[cid[c]] * cvr[c];
+            if (c < C) out += s_qp[s_misc[c]] * s_vec[(D::SCV + c) * DK + j];
         a.o[head * DV + j] = out;
     }
 }
 
-template <int DK, int WM, bool KDA>
-hipError_t launch_t(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
-    constexpr int NT = (2 * DK < 64) ? 64 : 2 * DK;
+template <int DK, int WM, bool KDA, int NB>
+hipError_t launch_nb(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
+    constexpr int NT = Dec<DK, DK, WM, KDA>::NT;
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
-    hipLaunchKernelGGL((decode_kernel<DK, DK, WM, KDA, NT>), dim3(grid), dim3(NT), 0, s, args);
+    hipLaunchKernelGGL((decode_kernel<DK, DK, WM, KDA, NB>), dim3(grid), dim3(NT), 0, s, args);
     return hipGetLastError();
+}
+
+// dk = 128, W <= 16: one kernel per window position (no runtime guards).
+template <bool KDA, int... NBS>
+hipError_t launch_fixed(const lq_dims& d, const DecodeArgs& args, hipStream_t s,
+                        std::integer_sequence<int, NBS...>) {
+    hipError_t e = hipErrorInvalidValue;
+    ((args.pos == NBS ? (e = launch_nb<128, 16, KDA, NBS>(d, args, s), 0) : 0), ...);
+    return e;
 }
 
 template <int DK>
 hipError_t launch_dk(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
     const bool kda = d.decay_mode == LQ_DECAY_PER_KEY;
     switch (wbucket(d.W)) {
-        case 4: return kda ? launch_t<DK, 4, true>(d, args, s) : launch_t<DK, 4, false>(d, args, s);
-        case 8: return kda ? launch_t<DK, 8, true>(d, args, s) : launch_t<DK, 8, false>(d, args, s);
-        case 16: return kda ? launch_t<DK, 16, true>(d, args, s) : launch_t<DK, 16, false>(d, args, s);
-        default: return kda ? launch_t<DK, 32, true>(d, args, s) : launch_t<DK, 32, false>(d, args, s);
+        case 4: return kda ? launch_nb<DK, 4, true, -1>(d, args, s) : launch_nb<DK, 4, false, -1>(d, args, s);
+        case 8: return kda ? launch_nb<DK, 8, true, -1>(d, args, s) : launch_nb<DK, 8, false, -1>(d, args, s);
+        case 16:
+            if constexpr (DK == 128)
+                return kda ? launch_fixed<true>(d, args, s, std::make_integer_sequence<int, 16>{})
+                           : launch_fixed<false>(d, args, s, std::make_integer_sequence<int, 16>{});
+            else
+                return kda ? launch_nb<DK, 16, true, -1>(d, args, s) : launch_nb<DK, 16, false, -1>(d, args, s);
+        default: return kda ? launch_nb<DK, 32, true, -1>(d, args, s) : launch_nb<DK, 32, false, -1>(d, args, s);
     }
 }
 

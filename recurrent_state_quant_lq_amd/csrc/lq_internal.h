@@ -21,36 +21,84 @@ hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const float
                                   const float* k, const float* v, const float* alpha,
                                   const float* beta, float* o, hipStream_t s);
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
-// device helpers
+// barriers
 // ---------------------------------------------------------------------------
 
 // Workgroup barrier that orders LDS traffic only: global loads issued before
-// it stay in flight across it.
+// it may stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Waits for every outstanding load of this wave (LDS copies included), then a
+// full workgroup barrier; no memory access moves across it.
+__device__ __forceinline__ void all_loads_barrier() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8
+constexpr int DPP_MIRROR = 0x140;       // lane i <- lane 15-i within 16
+constexpr int DPP_SHL1 = 0x101;         // lane i <- lane i+1 within 16
+constexpr int DPP_SHL2 = 0x102;         // lane i <- lane i+2 within 16
+
+__device__ __forceinline__ float swz_xor16(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
 // Sum / max over aligned groups of G lanes (G a power of two <= 64); every
-// lane of the group receives the result.
+// lane of a group receives the result.  After the two quad steps all lanes
+// of a quad agree, so the mirror steps pair whole quads, then whole halves.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) x += __shfl_xor(x, m, 64);
+    if constexpr (G >= 2) x += dpp<DPP_XOR1>(x);
+    if constexpr (G >= 4) x += dpp<DPP_XOR2>(x);
+    if constexpr (G >= 8) x += dpp<DPP_HALF_MIRROR>(x);
+    if constexpr (G >= 16) x += dpp<DPP_MIRROR>(x);
+    if constexpr (G >= 32) x += swz_xor16(x);
+    if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
     return x;
 }
 
 template <int G>
 __device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+    if constexpr (G >= 2) x = fmaxf(x, dpp<DPP_XOR1>(x));
+    if constexpr (G >= 4) x = fmaxf(x, dpp<DPP_XOR2>(x));
+    if constexpr (G >= 8) x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+    if constexpr (G >= 16) x = fmaxf(x, dpp<DPP_MIRROR>(x));
+    if constexpr (G >= 32) x = fmaxf(x, swz_xor16(x));
+    if constexpr (G >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
     return x;
 }
 
-// N consecutive floats from an address aligned to 4*N bytes when N is a
-// multiple of 4 (or 2), as 128-bit (64-bit) loads.
+// ---------------------------------------------------------------------------
+// memory
+// ---------------------------------------------------------------------------
+
+// N consecutive floats as 128-bit (64-bit) accesses when N allows it; the
+// address must be aligned to the access size.
 template <int N>
 __device__ __forceinline__ void load_floats(const float* __restrict__ p, float (&x)[N]) {
     if constexpr (N % 4 == 0) {
@@ -87,9 +135,49 @@ __device__ __forceinline__ void store_floats(float* __restrict__ p, const float 
     }
 }
 
+// Global -> LDS without registers.  Lane l of the wave writes
+// lds_wave_base + 16*l (dma16) or + 4*l (dma4) bytes; lds_wave_base must be
+// wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                     16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                     4, 0, 0);
+}
+
 // Signed byte e (0..3) of a 32-bit word, as float.
 __device__ __forceinline__ float sbyte(uint32_t w, int e) {
     return (float)(int32_t)(int8_t)(uint8_t)(w >> (8 * e));
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
+           ((uint32_t)(d & 255) << 24);
+}
+
+// ---------------------------------------------------------------------------
+// three-digit int8 expansion for the int8 MFMA products
+// ---------------------------------------------------------------------------
+// With inv = 127 / M (M >= max |x| of the block), x = (M/127)(d0 + d1/254 +
+// d2/254^2) to within (M/127)*2^-16, i.e. to fp32 precision relative to the
+// block's largest element.  Products of the digits with int8 state bytes sum
+// exactly in int32, so the three partial sums recombine to an fp32-accurate
+// product with the int8 matrix.
+constexpr float kDigitW1 = 1.0f / 254.0f;
+constexpr float kDigitW2 = 1.0f / (254.0f * 254.0f);
+
+__device__ __forceinline__ void digits3(float x, float inv, int& d0, int& d1, int& d2) {
+    const float u = x * inv;
+    const float f0 = fminf(fmaxf(rintf(u), -127.0f), 127.0f);
+    const float r1 = (u - f0) * 254.0f;
+    const float f1 = fminf(fmaxf(rintf(r1), -127.0f), 127.0f);
+    const float r2 = (r1 - f1) * 254.0f;
+    const float f2 = fminf(fmaxf(rintf(r2), -127.0f), 127.0f);
+    d0 = (int)f0;
+    d1 = (int)f1;
+    d2 = (int)f2;
 }
 
 // Window-size bucket a kernel is instantiated for.

@@ -112,7 +112,8 @@ def _raise(fn, rc):
 
 @dataclass
 class LayerState:
-    """Device tensors of one layer's codec and window buffer (torch-owned)."""
+    """Device tensors of one layer's codec and window buffer (torch-owned).
+    ``sq`` is value-column-major [B,H,dv,dk] as the library stores it."""
     dims: lq_dims
     sq: torch.Tensor
     row_scale: torch.Tensor
@@ -129,7 +130,7 @@ class LayerState:
         B, H, dk, dv, W, C = d.B, d.H, d.dk, d.dv, d.W, d.C
         gd = dk if d.decay_mode == LQ_DECAY_PER_KEY else 1
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
-        return LayerState(d, z((B, H, dk, dv), torch.int8), z((B, H, dk), torch.float32),
+        return LayerState(d, z((B, H, dv, dk), torch.int8), z((B, H, dk), torch.float32),
                           z((B, H, dv), torch.float32), z((B, H, max(C, 1)), torch.int32),
                           z((B, H, max(C, 1), dv), torch.float32),
                           z((B, H, W, dk), torch.float32), z((B, H, W, dk), torch.float32),
@@ -139,7 +140,7 @@ class LayerState:
         d = self.dims
         B, H, dk, dv, W, C = d.B, d.H, d.dk, d.dv, d.W, d.C
         gd = dk if d.decay_mode == LQ_DECAY_PER_KEY else 1
-        _check(self.sq, "sq", (B, H, dk, dv), torch.int8)
+        _check(self.sq, "sq", (B, H, dv, dk), torch.int8)
         _check(self.row_scale, "row_scale", (B, H, dk), torch.float32)
         _check(self.col_scale, "col_scale", (B, H, dv), torch.float32)
         _check(self.comp_idx, "comp_idx", (B, H, max(C, 1)), torch.int32)
@@ -156,16 +157,19 @@ class LayerState:
                            "buf_k", "buf_y", "buf_u", "buf_g")])
 
     def codec(self) -> dict:
-        """Host copies of the codec arrays (comp arrays cut to C)."""
+        """Host copies of the codec arrays, int8 matrix row-major [B,H,dk,dv]
+        (comp arrays cut to C)."""
         C = self.dims.C
-        return dict(sq=self.sq.cpu().numpy(), r=self.row_scale.cpu().numpy(),
+        return dict(sq=self.sq.transpose(-1, -2).contiguous().cpu().numpy(),
+                    r=self.row_scale.cpu().numpy(),
                     s=self.col_scale.cpu().numpy(), idx=self.comp_idx[..., :C].cpu().numpy(),
                     cv=self.comp_val[..., :C, :].cpu().numpy())
 
     def load_codec(self, cd: dict):
-        """Uploads host codec arrays ([B,H,...], comp arrays with C entries)."""
+        """Uploads host codec arrays ([B,H,...], int8 matrix row-major
+        [B,H,dk,dv], comp arrays with C entries)."""
         C = self.dims.C
-        self.sq.copy_(torch.as_tensor(cd["sq"]))
+        self.sq.copy_(torch.as_tensor(cd["sq"]).transpose(-1, -2))
         self.row_scale.copy_(torch.as_tensor(cd["r"]))
         self.col_scale.copy_(torch.as_tensor(cd["s"]))
         if C:

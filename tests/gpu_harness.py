@@ -59,7 +59,7 @@ def codec_equal(gpu: dict, orc: dict) -> bool:
 
 def upload_head_codec(st: lq.LayerState, b: int, h: int, cd: dict):
     C = st.dims.C
-    st.sq[b, h].copy_(torch.from_numpy(cd["sq"]))
+    st.sq[b, h].copy_(torch.from_numpy(np.ascontiguousarray(cd["sq"].T)))
     st.row_scale[b, h].copy_(torch.from_numpy(cd["r"]))
     st.col_scale[b, h].copy_(torch.from_numpy(cd["s"]))
     if C:
@@ -69,7 +69,7 @@ def upload_head_codec(st: lq.LayerState, b: int, h: int, cd: dict):
 
 def head_codec(st: lq.LayerState, b: int, h: int) -> dict:
     C = st.dims.C
-    return dict(sq=st.sq[b, h].cpu().numpy(), r=st.row_scale[b, h].cpu().numpy(),
+    return dict(sq=np.ascontiguousarray(st.sq[b, h].cpu().numpy().T), r=st.row_scale[b, h].cpu().numpy(),
                 s=st.col_scale[b, h].cpu().numpy(), idx=st.comp_idx[b, h, :C].cpu().numpy(),
                 cv=st.comp_val[b, h, :C].cpu().numpy())
 
