@@ -12,11 +12,12 @@
 //     M = U - Y Hb                     (N x dv,   contraction over dk)
 //     H = Gamma Hb + Kt^T M            (dk x dv,  contraction over N)
 // with Kt[i][c] = exp(g_{N-1}[c] - g_i[c]) k_i[c] and Gamma = diag exp(g_{N-1}).
-//   * Y Hb = ((Y o r) sq) o s + sum_c Y[:, idx_c] cv_c^T: the int8 state is
-//     the B operand of v_mfma_i32_16x16x64_i8 as stored (value-column-major
-//     sq[j][i]: 16 consecutive key channels of a column are one load) and
-//     Y o r enters as three int8 digits per slot (exact int32 sums, recombined
-//     in fp32).  Each wave owns whole column tiles, so no cross-wave sums.
+//   * Y Hb = ((Y o r) sq) o s + Y[:, idx] cv: the int8 state is the B operand
+//     of v_mfma_i32_16x16x64_i8 as stored (value-column-major sq[j][i]: 16
+//     consecutive key channels of a column are one load) and Y o r enters as
+//     three int8 digits per slot (exact int32 sums, recombined in fp32).  The
+//     compensator term is one fp32 MFMA per tile whose K dimension runs over
+//     the compensator rows.  Each wave owns whole column tiles.
 //   * Kt^T M is dense fp32 on v_mfma_f32_16x16x4_f32.
 //
 // Register layout ("D layout") of H in one workgroup: NW waves; lane l
@@ -42,6 +43,8 @@ namespace {
 constexpr float kTiny = 0x1p-120f;
 constexpr int CMAX = 8;
 
+typedef unsigned long long u64;
+
 struct CodecOut {
     int8_t* sq;
     float* r;
@@ -62,6 +65,8 @@ struct FS {
     static constexpr int TPW = CT / NW > 0 ? CT / NW : 1;   // contraction-1 tiles per wave
     static constexpr int KS = (DK + 63) / 64;
     static_assert(DK % 16 == 0 && RB % NW == 0 && (CT % NW == 0 || CT < NW), "tile shape");
+    // every wave's rows lie in one 64-row half
+    static_assert(16 * RBW <= 64 && 64 % (16 * RBW) == 0, "row halves");
 };
 
 template <int DK, int DV>
@@ -84,14 +89,25 @@ struct RowBytes<4> {
     static __device__ float get(const uint32_t& x, int k) { return sbyte(x, k); }
 };
 
+__device__ __forceinline__ u64 ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Bits [0, n) set; n may be <= 0 or >= 64.
+__device__ __forceinline__ u64 low_bits(int n) {
+    return n <= 0 ? 0ull : n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+}
+
+// Number of set bits of the 128-bit mask (lo, hi) below row `row`.
+__device__ __forceinline__ int bits_below(u64 lo, u64 hi, int row) {
+    return __popcll(lo & low_bits(row)) + __popcll(hi & low_bits(row - 64));
+}
+
 // LDS used by the codec stage.
 template <int DK, int DV, int NW>
 struct CodecLds {
     float m[DK];                 // row magnitudes
-    int pos[DK];                 // compensator slot of a row, or -1
-    unsigned long long ball[(DK + 63) / 64];
-    float cm[NW][DV];            // per-wave column maxima
+    float cm[NW * 4][DV];        // column maxima per (wave, lane group)
     float sinv[DV];              // 1 / col_scale
+    float cvt[DV][CMAX];         // compensator rows (column-major), staged for the stores
 };
 
 // Codec of the state held in D layout (H is overwritten).  Writes sq
@@ -101,8 +117,11 @@ template <int DK, int DV, int RBW, int CT, int NW>
 __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const CodecOut& out,
                             float* __restrict__ h_out, int C, int smooth) {
     constexpr int RPL = FS<DK, DV>::RPL;
+    constexpr int NT = 64 * NW;
     const int t = threadIdx.x;
-    const int lane = t & 63, w = t >> 6, li = lane & 15, lg = lane >> 4;
+    const int lane = t & 63, li = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int row0 = row_of<DK, DV>(w, lg, 0, 0);
 
     if (h_out) {
 #pragma unroll
@@ -112,125 +131,167 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                 float x[CT];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) x[ct] = H[rb][ct][v];
-                store_floats<CT>(h_out + (size_t)row_of<DK, DV>(w, lg, rb, v) * DV + li * CT, x);
+                store_floats<CT>(h_out + (size_t)(row0 + rb * 4 + v) * DV + li * CT, x);
             }
     }
     // row magnitudes
+    {
+        float m[RPL];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float mx = 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) mx = fmaxf(mx, fabsf(H[rb][ct][v]));
+                m[rb * 4 + v] = group_absmax<16>(mx);
+            }
+        if (li == 0) store_floats<RPL>(&L.m[row0], m);
+    }
+    lds_barrier();
+
+    // The C largest rows, ties to the lower row: C rounds of a wave argmax
+    // over the magnitudes' bit patterns (every wave computes the same set).
+    u64 lo = 0, hi = 0;
+    {
+        bool ta = lane >= DK, tb = lane + 64 >= DK;     // taken or absent
+        uint32_t ma = ta ? 0u : __float_as_uint(L.m[lane]);
+        uint32_t mb = tb ? 0u : __float_as_uint(L.m[lane + 64]);
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c)
+            if (c < C) {
+                const uint32_t mx = wave_umax(umax(ma, mb));
+                u64 ca = ballot(!ta && ma == mx), cb = ballot(!tb && mb == mx);
+                if ((ca | cb) == 0) {            // unreachable for valid rows: lowest free row
+                    ca = ballot(!ta);
+                    cb = ballot(!tb);
+                }
+                const int r = ca ? __builtin_ctzll(ca) : 64 + __builtin_ctzll(cb);
+                if (r < 64)
+                    lo |= 1ull << r;
+                else
+                    hi |= 1ull << (r - 64);
+                if (lane == r) {
+                    ta = true;
+                    ma = 0u;
+                }
+                if (lane + 64 == r) {
+                    tb = true;
+                    mb = 0u;
+                }
+            }
+    }
+    // their positions: ascending row order
+    if (w == 0) {
+        u64 l2 = lo, h2 = hi;
+        int mine = 0;
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c)
+            if (c < C) {
+                const int r = l2 ? __builtin_ctzll(l2) : 64 + __builtin_ctzll(h2);
+                if (l2)
+                    l2 &= l2 - 1ull;
+                else
+                    h2 &= h2 - 1ull;
+                if (lane == c) mine = r;
+            }
+        if (lane < C) out.idx[lane] = mine;
+    }
+    // compensator rows to LDS, residual rows zeroed
+    {
+        const u64 half = (w * 16 * RBW >= 64) ? hi : lo;
+        const uint32_t bits = (uint32_t)(half >> (row0 & 63)) & ((1u << RPL) - 1u);
+        if (ballot(bits != 0)) {
+            const int base = bits_below(lo, hi, row0);
+#pragma unroll
+            for (int k = 0; k < RPL; ++k)
+                if ((bits >> k) & 1u) {
+                    float* dst = &L.cvt[li * CT][base + __popc(bits & ((1u << k) - 1u))];
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) dst[ct * CMAX] = H[k / 4][ct][k % 4];
+                }
+        }
+        // zeroed by a 0/1 factor, branch-free (a -0 it may leave has
+        // magnitude 0 and rounds to byte 0 like +0)
+#pragma unroll
+        for (int k = 0; k < RPL; ++k) {
+            const float keep = ((bits >> k) & 1u) ? 0.0f : 1.0f;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) H[k / 4][ct][k % 4] = H[k / 4][ct][k % 4] * keep;
+        }
+    }
+    // column maxima of the residual, per lane group
+    {
+        float cm[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) mx = fmaxf(mx, fabsf(H[rb][ct][v]));
+            cm[ct] = mx;
+        }
+        store_floats<CT>(&L.cm[w * 4 + lg][li * CT], cm);
+    }
+    lds_barrier();
+    if (t < DV) {
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int i = 0; i < NW * 4; ++i) mx = umax(mx, __float_as_uint(L.cm[i][t]));
+        const float m = __uint_as_float(mx);
+        const float sj = (smooth && m >= kTiny) ? m : 1.0f;
+        out.s[t] = sj;
+        L.sinv[t] = 1.0f / sj;
+    }
+    for (int e = t; e < C * (DV / 4); e += NT) {
+        const int p = e / (DV / 4), j = 4 * (e % (DV / 4));
+        reinterpret_cast<float4*>(out.cv)[e] =
+            make_float4(L.cvt[j][p], L.cvt[j + 1][p], L.cvt[j + 2][p], L.cvt[j + 3][p]);
+    }
+    lds_barrier();
+    // smoothing and row maxima
+    float inv[CT];
+    load_floats<CT>(&L.sinv[li * CT], inv);
+    float rho[RPL];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             float mx = 0.0f;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) mx = fmaxf(mx, fabsf(H[rb][ct][v]));
-            mx = group_max<16>(mx);
-            if (li == 0) L.m[row_of<DK, DV>(w, lg, rb, v)] = mx;
-        }
-    lds_barrier();
-    // the C largest rows (ties: lower row), then their ascending positions
-    if (t < DK) {
-        const float mt = L.m[t];
-        int rank = 0;
-#pragma unroll 8
-        for (int i = 0; i < DK; i += 4) {
-            const float4 m4 = *reinterpret_cast<const float4*>(&L.m[i]);
-            rank += (m4.x > mt) || (m4.x == mt && i < t);
-            rank += (m4.y > mt) || (m4.y == mt && i + 1 < t);
-            rank += (m4.z > mt) || (m4.z == mt && i + 2 < t);
-            rank += (m4.w > mt) || (m4.w == mt && i + 3 < t);
-        }
-        const unsigned long long b = __ballot(rank < C);
-        if (lane == 0) L.ball[w] = b;
-    }
-    lds_barrier();
-    if (t < DK) {
-        const unsigned long long b = L.ball[w];
-        int p = -1;
-        if ((b >> lane) & 1ull) {
-            p = __popcll(b & ((1ull << lane) - 1ull));
-            for (int ww = 0; ww < w; ++ww) p += __popcll(L.ball[ww]);
-            out.idx[p] = t;
-        }
-        L.pos[t] = p;
-    }
-    lds_barrier();
-    // compensator rows out, residual rows zeroed
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int p = L.pos[row_of<DK, DV>(w, lg, rb, v)];
-            if (p >= 0) {
-                float x[CT];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    x[ct] = H[rb][ct][v];
-                    H[rb][ct][v] = 0.0f;
-                }
-                store_floats<CT>(out.cv + (size_t)p * DV + li * CT, x);
-            }
-        }
-    // column maxima of the residual
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, fabsf(H[rb][ct][v]));
-        mx = fmaxf(mx, swz_xor16(mx));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        if (lg == 0) L.cm[w][li * CT + ct] = mx;
-    }
-    lds_barrier();
-    if (t < DV) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) mx = fmaxf(mx, L.cm[i][t]);
-        const float sj = (smooth && mx >= kTiny) ? mx : 1.0f;
-        out.s[t] = sj;
-        L.sinv[t] = 1.0f / sj;
-    }
-    lds_barrier();
-    // smoothing, row scales
-    float inv[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) inv[ct] = L.sinv[li * CT + ct];
-    float lam[RBW][4];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float rho = 0.0f;
-#pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 H[rb][ct][v] = H[rb][ct][v] * inv[ct];
-                rho = fmaxf(rho, fabsf(H[rb][ct][v]));
+                mx = fmaxf(mx, fabsf(H[rb][ct][v]));
             }
-            rho = group_max<16>(rho);
-            const bool live = rho >= kTiny;
-            lam[rb][v] = live ? 127.0f / rho : 0.0f;
-            if (li == 0) out.r[row_of<DK, DV>(w, lg, rb, v)] = live ? rho / 127.0f : 0.0f;
+            rho[rb * 4 + v] = group_absmax<16>(mx);
         }
-    // rounding; one column's RPL bytes per store
-    const int row0 = row_of<DK, DV>(w, lg, 0, 0);
+    // row scales: lane li of a row group divides for row row0 + li % RPL,
+    // the 16 lanes then share the RPL multipliers
+    float lam[RPL];
+    {
+        float my = rho[0];
+#pragma unroll
+        for (int k = 1; k < RPL; ++k) my = (li % RPL == k) ? rho[k] : my;
+        const bool live = my >= kTiny;
+        const float lmy = live ? 127.0f / my : 0.0f;
+        if (li < RPL) out.r[row0 + li] = live ? my / 127.0f : 0.0f;
+        row_bcast_all<RPL>(lmy, lam);
+    }
+    // rounding through the offset form; one column's RPL bytes per store.
+    // The clamp to +-127 never binds: |Y| <= rho and lam = RN(127/rho) give
+    // |Y * lam| <= 127 (1 + 2^-24)^2, which rounds to at most 127.
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-        int b[RBW][4];
+        uint32_t z[RPL];
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float x = rintf(H[rb][ct][v] * lam[rb][v]);
-                x = fminf(fmaxf(x, -127.0f), 127.0f);
-                b[rb][v] = (int)x;
-            }
+        for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
         int8_t* dst = out.sq + (size_t)(li * CT + ct) * DK + row0;
         if constexpr (RPL == 8)
-            *reinterpret_cast<uint2*>(dst) = make_uint2(pack4(b[0][0], b[0][1], b[0][2], b[0][3]),
-                                                        pack4(b[1][0], b[1][1], b[1][2], b[1][3]));
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low4(z[0], z[1], z[2], z[3]),
+                                                        pack_low4(z[4], z[5], z[6], z[7]));
         else
-            *reinterpret_cast<uint32_t*>(dst) = pack4(b[0][0], b[0][1], b[0][2], b[0][3]);
+            *reinterpret_cast<uint32_t*>(dst) = pack_low4(z[0], z[1], z[2], z[3]);
     }
 }
 
@@ -251,31 +312,69 @@ struct FlushArgs {
     int smooth;
 };
 
+// Rows 0..NPAD-1 of a [rows][D] fp32 block (row index clamped to rmax) into
+// LDS dst[NPAD][D]; 16-byte pieces, one kilobyte per wave-wide copy, copies
+// spread over the NW waves.
+template <int NPAD, int D, int NW>
+__device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst, int w, int lane) {
+    constexpr int NCOPY = NPAD * D / 256;
+    static_assert((NPAD * D) % 256 == 0, "block of whole copies");
+#pragma unroll
+    for (int i = 0; i < (NCOPY + NW - 1) / NW; ++i) {
+        const int cp = i * NW + w;
+        if (cp < NCOPY) {
+            const int e = cp * 256 + 4 * lane;
+            lds_dma16(src + (size_t)min(e / D, rmax) * D + e % D, dst + cp * 256);
+        }
+    }
+}
+
+// Workgroup LDS of the flush kernel (byte offsets; the codec area reuses the
+// Y and digit blocks, dead once the first contraction is done).
+template <int DK, int DV, int NPAD, bool KDA>
+struct FlushLds {
+    static constexpr int KS = (DK + 63) / 64;
+    static constexpr int RS = 0;                                   // r | s | cv rows
+    static constexpr int MISC = RS + (2 + CMAX) * DK * 4;          // idx
+    static constexpr int GS = MISC + 64;                           // scalar log-decays
+    static constexpr int UM = GS + 4 * 32;                         // U, then M
+    static constexpr int KB = UM + NPAD * DV * 4;                  // keys
+    static constexpr int GB = KB + NPAD * DK * 4;                  // per-key log-decays
+    static constexpr int YB = GB + (KDA ? NPAD * DK * 4 : 0);      // Y, then codec
+    static constexpr int DA = YB + NPAD * DK * 4;                  // digits
+    static constexpr int YSC = DA + 3 * NPAD * KS * 64;
+    static constexpr int BYTES = YSC + NPAD * 4;
+    static_assert(sizeof(CodecLds<DK, DV, 4>) <= YSC - YB, "codec area");
+};
+
 template <int DK, int DV, int WM, bool KDA>
 __global__ __launch_bounds__((FS<DK, DV>::NT))
-__attribute__((amdgpu_waves_per_eu(WM <= 16 ? 4 : 2, WM <= 16 ? 4 : 2)))
+__attribute__((amdgpu_waves_per_eu(WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2), WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2))))
 void flush_kernel(FlushArgs a) {
     using S = FS<DK, DV>;
     constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, NT = S::NT, RPL = S::RPL;
     constexpr int TPW = S::TPW, KS = S::KS;
     constexpr int NPAD = WM <= 16 ? 16 : 32;   // slots padded to the MFMA size
     constexpr int MB = NPAD / 16;
-    constexpr int GD = KDA ? DK : 1;
     constexpr int LPS = NT / NPAD;             // lanes per slot in the digit stage
     constexpr int CHD = DK / LPS;              // channels per lane in the digit stage
     static_assert(NT % NPAD == 0 && DK % LPS == 0 && CHD % 4 == 0, "digit tiling");
     using RBy = RowBytes<RPL>;
+    using LY = FlushLds<DK, DV, NPAD, KDA>;
 
-    __shared__ __align__(16) float s_rs[(2 + CMAX) * DK];  // r, s, compensator rows
-    __shared__ __align__(16) int s_misc[16];               // idx[0..7]
-    __shared__ __align__(16) int8_t s_dA[3][NPAD][KS * 64];
-    __shared__ __align__(16) float s_ysc[NPAD];
-    __shared__ __align__(16) float s_yc[CMAX][NPAD];
-    __shared__ __align__(16) float s_M[NPAD][DV];
-    __shared__ __align__(16) CodecLds<DK, DV, NW> L;
-    float* s_r = s_rs;
-    float* s_s = s_rs + DK;
-    float* s_cv = s_rs + 2 * DK;                            // [CMAX][DV]
+    __shared__ __align__(16) char smem[LY::BYTES];
+    float* s_r = reinterpret_cast<float*>(smem + LY::RS);
+    float* s_s = s_r + DK;
+    float* s_cv = s_r + 2 * DK;                                    // [CMAX][DV]
+    int* s_idx = reinterpret_cast<int*>(smem + LY::MISC);
+    float* s_gs = reinterpret_cast<float*>(smem + LY::GS);         // [NPAD] (scalar decay)
+    float* s_UM = reinterpret_cast<float*>(smem + LY::UM);         // [NPAD][DV]
+    float* s_K = reinterpret_cast<float*>(smem + LY::KB);          // [NPAD][DK]
+    float* s_G = reinterpret_cast<float*>(smem + LY::GB);          // [NPAD][DK] (per-key decay)
+    float* s_Y = reinterpret_cast<float*>(smem + LY::YB);          // [NPAD][DK]
+    int8_t* s_dA = reinterpret_cast<int8_t*>(smem + LY::DA);       // [3][NPAD][KS*64]
+    float* s_ysc = reinterpret_cast<float*>(smem + LY::YSC);       // [NPAD]
+    auto& L = *reinterpret_cast<CodecLds<DK, DV, NW>*>(smem + LY::YB);
 
     const int t = threadIdx.x;
     const int lane = t & 63, li = lane & 15, lg = lane >> 4;
@@ -284,14 +383,11 @@ void flush_kernel(FlushArgs a) {
     const int W = a.W, C = a.C, N = a.N;
 
     const int8_t* sq = a.sq + head * (DK * DV);
-    const float* bk = a.bk + head * (size_t)W * DK;
-    const float* by = a.by + head * (size_t)W * DK;
-    const float* bu = a.bu + head * (size_t)W * DV;
-    const float* bg = a.bg + head * (size_t)W * GD;
 
-    // ---- loads --------------------------------------------------------------------------------
-    // r, s, compensator rows -> LDS (DK/4 lanes per vector of 16-byte chunks)
+    // ---- loads (all unconditional; buffer rows clamped to W-1, slots >= N
+    //      masked after the barrier) -----------------------------------------------------------------
     {
+        // r, s, compensator rows (DK/4 lanes per vector of 16-byte pieces)
         constexpr int SEGL = DK / 4, SPI = 64 / SEGL;
         const int nseg = 2 + C;
         const int my = lane / SEGL;
@@ -305,16 +401,15 @@ void flush_kernel(FlushArgs a) {
                                : sg < nseg ? a.cv + (head * C + (sg - 2)) * (size_t)DV : nullptr;
                 if (my == q) src = p;
             }
-            if (src) lds_dma16(src + 4 * (lane % SEGL), s_rs + s0 * DK);
+            if (src) lds_dma16(src + 4 * (lane % SEGL), s_r + s0 * DK);
         }
-        if (w == 0 && lane < C) lds_dma4(a.idx + head * C + lane, s_misc);
+        if (w == 0 && lane < C) lds_dma4(a.idx + head * C + lane, s_idx);
+        if (!KDA && w == NW - 1 && lane < NPAD) lds_dma4(a.bg + head * W + min(lane, W - 1), s_gs);
+        dma_rows<NPAD, DV, NW>(a.bu + head * (size_t)W * DV, W - 1, s_UM, w, lane);
+        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane);
+        dma_rows<NPAD, DK, NW>(a.by + head * (size_t)W * DK, W - 1, s_Y, w, lane);
+        if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, W - 1, s_G, w, lane);
     }
-    // digit stage inputs: Y[slot][c0 .. c0+CHD)
-    // (loads below are unconditional, slot indices clamped into the buffer; the
-    // values of slots >= N are masked after the barrier)
-    const int dslot = t / LPS, dc0 = (t % LPS) * CHD;
-    float yv[CHD];
-    load_floats<CHD>(by + (size_t)min(dslot, W - 1) * DK + dc0, yv);
     // contraction-1 B operands: column j = tile*16 + li, channels ks*64 + 16*lg .. +15
     v4i bq[TPW][KS];
     constexpr bool FULL = (CT % NW == 0) && (DK % 64 == 0);
@@ -329,116 +424,98 @@ void flush_kernel(FlushArgs a) {
             else
                 bq[tw][ks] = v4i{0, 0, 0, 0};
         }
-    // contraction-1 outputs need U[slot][j] at (slot = mb*16 + 4*lg + v, j = tile*16 + li)
-    float uv[MB][TPW][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int tw = 0; tw < TPW; ++tw)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int slot = min(mb * 16 + 4 * lg + v, W - 1);
-                const int tile = min(w * TPW + tw, CT - 1);
-                uv[mb][tw][v] = bu[(size_t)slot * DV + tile * 16 + li];
-            }
     // D-layout bytes of the base state: column li*CT + ct, this lane's RPL rows
     const int row0 = row_of<DK, DV>(w, lg, 0, 0);
     typename RBy::T hb[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
         hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + (size_t)(li * CT + ct) * DK + row0);
-    // window log-decay of this lane's rows
-    float gam[RBW][4];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            gam[rb][v] = KDA ? bg[(size_t)(N - 1) * DK + row_of<DK, DV>(w, lg, rb, v)] : bg[N - 1];
-    // contraction-2 A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg
-    float ka[RBW][NPAD / 4], kg[RBW][NPAD / 4], gl[RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-        const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
-        gl[rb] = KDA ? bg[(size_t)(N - 1) * DK + rowa] : bg[N - 1];
-#pragma unroll
-        for (int ks = 0; ks < NPAD / 4; ++ks) {
-            const int slot = min(4 * ks + lg, W - 1);
-            ka[rb][ks] = bk[(size_t)slot * DK + rowa];
-            kg[rb][ks] = KDA ? bg[(size_t)slot * DK + rowa] : bg[slot];
-        }
-    }
     all_loads_barrier();
 
-    // Kt (decayed keys) of the contraction-2 A operands; slots >= N are zero
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int ks = 0; ks < NPAD / 4; ++ks)
-            ka[rb][ks] = 4 * ks + lg < N ? __expf(gl[rb] - kg[rb][ks]) * ka[rb][ks] : 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int tw = 0; tw < TPW; ++tw)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (mb * 16 + 4 * lg + v >= N) uv[mb][tw][v] = 0.0f;
-    if (dslot >= N) {
-#pragma unroll
-        for (int c = 0; c < CHD; ++c) yv[c] = 0.0f;
-    }
-
-    // ---- digits of (Y o r), per slot --------------------------------------------------------------
+    // ---- digits of (Y o r), per slot; compensator operands ----------------------------------------
     {
-        float p[CHD];
+        const int dslot = t / LPS, dc0 = (t % LPS) * CHD;
+        float yv[CHD], rv[CHD];
+        load_floats<CHD>(s_Y + dslot * DK + dc0, yv);
+        load_floats<CHD>(s_r + dc0, rv);
+        const bool live = dslot < N;
         float mx = 0.0f;
 #pragma unroll
         for (int c = 0; c < CHD; ++c) {
-            p[c] = yv[c] * s_r[dc0 + c];
-            mx = fmaxf(mx, fabsf(p[c]));
+            yv[c] = live ? yv[c] * rv[c] : 0.0f;
+            mx = fmaxf(mx, fabsf(yv[c]));
         }
-        mx = group_max<LPS>(mx);
+        mx = group_absmax<LPS>(mx);
         const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
-        int dg[3][CHD];
+        uint32_t dg[3][CHD];
 #pragma unroll
-        for (int c = 0; c < CHD; ++c) digits3(p[c], inv, dg[0][c], dg[1][c], dg[2][c]);
+        for (int c = 0; c < CHD; ++c) digits3_words(yv[c], inv, dg[0][c], dg[1][c], dg[2][c]);
 #pragma unroll
         for (int d = 0; d < 3; ++d)
 #pragma unroll
             for (int c = 0; c < CHD; c += 4)
-                *reinterpret_cast<uint32_t*>(&s_dA[d][dslot][dc0 + c]) =
-                    pack4(dg[d][c], dg[d][c + 1], dg[d][c + 2], dg[d][c + 3]);
+                *reinterpret_cast<uint32_t*>(&s_dA[(d * NPAD + dslot) * (KS * 64) + dc0 + c]) =
+                    pack_low4(dg[d][c], dg[d][c + 1], dg[d][c + 2], dg[d][c + 3]);
         if (t % LPS == 0) s_ysc[dslot] = mx * (1.0f / 127.0f);
-        for (int c = 0; c < C; ++c) {
-            const int rc = s_misc[c] - dc0;
-#pragma unroll
-            for (int cc = 0; cc < CHD; ++cc)
-                if (rc == cc) s_yc[c][dslot] = yv[cc];
-        }
         // channels past DK in the last K step stay zero
         if constexpr (KS * 64 > DK) {
             constexpr int PADC = KS * 64 - DK;
             for (int e = t; e < 3 * NPAD * PADC; e += NT)
-                s_dA[e / (NPAD * PADC)][(e % (NPAD * PADC)) / PADC][DK + e % PADC] = 0;
+                s_dA[(e / PADC) * (KS * 64) + DK + e % PADC] = 0;
+        }
+    }
+    // compensator A operands Y[slot][idx_c] (slot = mb*16 + li, c = 4*kc + lg)
+    constexpr int KC = CMAX / 4;
+    float ya[MB][KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        const int c = 4 * kc + lg;
+        const int ic = c < C ? s_idx[c] & (DK - 1) : 0;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int slot = mb * 16 + li;
+            ya[mb][kc] = (c < C && slot < N) ? s_Y[slot * DK + ic] : 0.0f;
         }
     }
     lds_barrier();
 
-    // ---- M = U - Y Hb for this wave's column tiles (int8 MFMA) --------------------------------
+    // ---- M = U - Y Hb for this wave's column tiles ----------------------------------------------------
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         v4i acc[3][TPW];
+        v4f cc[TPW];
 #pragma unroll
-        for (int d = 0; d < 3; ++d)
+        for (int tw = 0; tw < TPW; ++tw) {
+            const int tile = min(w * TPW + tw, CT - 1);
 #pragma unroll
-            for (int tw = 0; tw < TPW; ++tw) acc[d][tw] = v4i{0, 0, 0, 0};
+            for (int v = 0; v < 4; ++v) {
+                const int slot = mb * 16 + 4 * lg + v;
+                cc[tw][v] = slot < N ? -s_UM[slot * DV + tile * 16 + li] : 0.0f;
+            }
+#pragma unroll
+            for (int d = 0; d < 3; ++d) acc[d][tw] = v4i{0, 0, 0, 0};
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int d = 0; d < 3; ++d) {
-                const v4i aop = *reinterpret_cast<const v4i*>(&s_dA[d][mb * 16 + li][ks * 64 + 16 * lg]);
+                const v4i aop =
+                    *reinterpret_cast<const v4i*>(&s_dA[(d * NPAD + mb * 16 + li) * (KS * 64) + ks * 64 + 16 * lg]);
 #pragma unroll
                 for (int tw = 0; tw < TPW; ++tw)
                     acc[d][tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bq[tw][ks], acc[d][tw], 0, 0, 0);
+            }
+        // cc = Y[:, idx] cv - U
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+            if (4 * kc < C) {
+                const int c = 4 * kc + lg;
+#pragma unroll
+                for (int tw = 0; tw < TPW; ++tw) {
+                    const int tile = min(w * TPW + tw, CT - 1);
+                    const float b = c < C ? s_cv[c * DV + tile * 16 + li] : 0.0f;
+                    cc[tw] = __builtin_amdgcn_mfma_f32_16x16x4f32(ya[mb][kc], b, cc[tw], 0, 0, 0);
+                }
             }
 #pragma unroll
         for (int tw = 0; tw < TPW; ++tw) {
@@ -449,55 +526,96 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int slot = mb * 16 + 4 * lg + v;
-                float m = 0.0f;
-                if (slot < N) {
-                    const float yq = s_ysc[slot] * ((float)acc[0][tw][v] + (float)acc[1][tw][v] * kDigitW1 +
-                                                    (float)acc[2][tw][v] * kDigitW2);
-                    float comp = 0.0f;
-                    for (int c = 0; c < C; ++c) comp += s_yc[c][slot] * s_cv[c * DV + jj];
-                    m = uv[mb][tw][v] - (sj * yq + comp);
-                }
-                s_M[slot][jj] = m;
+                const float yq = s_ysc[slot] * ((float)acc[0][tw][v] + (float)acc[1][tw][v] * kDigitW1 +
+                                                (float)acc[2][tw][v] * kDigitW2);
+                s_UM[slot * DV + jj] = -(sj * yq + cc[tw][v]);
             }
         }
     }
-    lds_barrier();
 
     // ---- H = Gamma Hb + Kt^T M (fp32 MFMA, accumulating in place) -------------------------------
+    // contraction-2 A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg
+    float ka[RBW][NPAD / 4];
+    if constexpr (KDA) {
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
+            const float gl = s_G[(N - 1) * DK + rowa];
+#pragma unroll
+            for (int ks = 0; ks < NPAD / 4; ++ks) {
+                const int slot = 4 * ks + lg;
+                ka[rb][ks] = slot < N ? __expf(gl - s_G[slot * DK + rowa]) * s_K[slot * DK + rowa] : 0.0f;
+            }
+        }
+    } else {
+        const float gl = s_gs[N - 1];
+#pragma unroll
+        for (int ks = 0; ks < NPAD / 4; ++ks) {
+            const int slot = 4 * ks + lg;
+            const float e = __expf(gl - s_gs[slot]);
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
+                ka[rb][ks] = slot < N ? e * s_K[slot * DK + rowa] : 0.0f;
+            }
+        }
+    }
     v4f H[RBW][CT];
     {
-        float sc[CT];
+        float sc[CT], rr[RPL], gm[RPL];
+        load_floats<CT>(s_s + li * CT, sc);
+        load_floats<RPL>(s_r + row0, rr);
+        if constexpr (KDA) {
+            load_floats<RPL>(s_G + (N - 1) * DK + row0, gm);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) sc[ct] = s_s[li * CT + ct];
+            for (int k = 0; k < RPL; ++k) gm[k] = __expf(gm[k]);
+        } else {
+            const float g = __expf(s_gs[N - 1]);
+#pragma unroll
+            for (int k = 0; k < RPL; ++k) gm[k] = g;
+        }
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = row_of<DK, DV>(w, lg, rb, v);
-                const float rr = s_r[row];
-                const float g = __expf(gam[rb][v]);
-                float x[CT];
+                const float rg = rr[rb * 4 + v] * gm[rb * 4 + v];
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) x[ct] = (RBy::get(hb[ct], rb * 4 + v) * rr) * sc[ct];
-                for (int c = 0; c < C; ++c)
-                    if (s_misc[c] == row) {
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) x[ct] += s_cv[c * DV + li * CT + ct];
-                    }
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) H[rb][ct][v] = g * x[ct];
+                for (int ct = 0; ct < CT; ++ct) H[rb][ct][v] = (RBy::get(hb[ct], rb * 4 + v) * rg) * sc[ct];
             }
+    }
+    // compensator rows: H += Gamma P^T cv, one K step per 4 rows with
+    // A[rowa][c] = gamma(rowa) [rowa == idx_c] and B[c][col] = cv_c[col]
 #pragma unroll
-        for (int ks = 0; ks < NPAD / 4; ++ks) {
-            if (4 * ks < N) {
-                float bm[CT];
-                load_floats<CT>(&s_M[4 * ks + lg][li * CT], bm);
+    for (int kc = 0; kc < KC; ++kc)
+        if (4 * kc < C) {
+            const int c = 4 * kc + lg;
+            const bool cl = c < C;
+            const int ic = cl ? s_idx[c] : -1;
+            float bcv[CT];
+            load_floats<CT>(s_cv + (cl ? c : 0) * DV + li * CT, bcv);
 #pragma unroll
-                for (int rb = 0; rb < RBW; ++rb)
+            for (int ct = 0; ct < CT; ++ct) bcv[ct] = cl ? bcv[ct] : 0.0f;
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[rb][ks], bm[ct], H[rb][ct], 0, 0, 0);
+            for (int rb = 0; rb < RBW; ++rb) {
+                const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
+                const float g = KDA ? __expf(s_G[(N - 1) * DK + rowa]) : __expf(s_gs[N - 1]);
+                const float av = ic == rowa ? g : 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bcv[ct], H[rb][ct], 0, 0, 0);
             }
+        }
+    lds_barrier();   // M complete
+#pragma unroll
+    for (int ks = 0; ks < NPAD / 4; ++ks) {
+        if (4 * ks < N) {
+            float bm[CT];
+            load_floats<CT>(&s_UM[(4 * ks + lg) * DV + li * CT], bm);
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[rb][ks], bm[ct], H[rb][ct], 0, 0, 0);
         }
     }
 
@@ -561,7 +679,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
     __shared__ int s_pos[DK];
     for (int i = t; i < DK; i += 256) s_pos[i] = -1;
     __syncthreads();
-    if (t < a.C) s_pos[a.idx[head * a.C + t]] = t;
+    if (t < a.C) s_pos[a.idx[head * a.C + t] & (DK - 1)] = t;
     __syncthreads();
     const int8_t* sq = a.sq + head * (DK * DV);
     const float* r = a.r + head * DK;

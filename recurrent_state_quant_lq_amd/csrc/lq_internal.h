@@ -63,6 +63,14 @@ constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8
 constexpr int DPP_MIRROR = 0x140;       // lane i <- lane 15-i within 16
 constexpr int DPP_SHL1 = 0x101;         // lane i <- lane i+1 within 16
 constexpr int DPP_SHL2 = 0x102;         // lane i <- lane i+2 within 16
+constexpr int DPP_ROW_BCAST = 0x150;    // + k: every lane of a 16-lane row <- lane k of that row
+
+// x of lane k of this lane's 16-lane row, for k = 0..N-1, into out[k].
+template <int N, int K = 0>
+__device__ __forceinline__ void row_bcast_all(float x, float* out) {
+    out[K] = dpp<DPP_ROW_BCAST + K>(x);
+    if constexpr (K + 1 < N) row_bcast_all<N, K + 1>(x, out);
+}
 
 __device__ __forceinline__ float swz_xor16(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
@@ -91,6 +99,52 @@ __device__ __forceinline__ float group_max(float x) {
     if constexpr (G >= 32) x = fmaxf(x, swz_xor16(x));
     if constexpr (G >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
     return x;
+}
+
+// Maxima of NON-NEGATIVE floats handled as their bit patterns: for x, y >= 0
+// (zeros, subnormals, normals, +inf) x < y exactly when bits(x) < bits(y), and
+// the unsigned max folds into one v_max_u32 with a DPP source per step.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+template <int G>
+__device__ __forceinline__ uint32_t group_umax(uint32_t x) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "groups within a 16-lane row");
+    if constexpr (G >= 2) x = umax(x, (uint32_t)dpp_i<DPP_XOR1>((int)x));
+    if constexpr (G >= 4) x = umax(x, (uint32_t)dpp_i<DPP_XOR2>((int)x));
+    if constexpr (G >= 8) x = umax(x, (uint32_t)dpp_i<DPP_HALF_MIRROR>((int)x));
+    if constexpr (G >= 16) x = umax(x, (uint32_t)dpp_i<DPP_MIRROR>((int)x));
+    return x;
+}
+
+// Wave-uniform unsigned maximum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+    x = group_umax<16>(x);
+    const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+    return umax(umax(a, b), umax(c, d));
+}
+
+// Max of |x| over aligned groups of G lanes, as a float (every lane of a
+// group receives it).
+template <int G>
+__device__ __forceinline__ float group_absmax(float x) {
+    return __uint_as_float(group_umax<G>(__float_as_uint(x) & 0x7fffffffu));
+}
+
+// ---------------------------------------------------------------------------
+// rounding to int8 through the 1.5 * 2^23 offset
+// ---------------------------------------------------------------------------
+// For |y| <= 2^22, y + 1.5*2^23 rounded to fp32 (round to nearest, ties to
+// even) is 1.5*2^23 + rint(y) exactly, and the low byte of its bit pattern is
+// rint(y) as a two's-complement byte once the sum is clamped to
+// 1.5*2^23 +- 127.
+constexpr float kRoundOff = 12582912.0f;   // 1.5 * 2^23
+
+// Four low bytes (a first) into one word.
+__device__ __forceinline__ uint32_t pack_low4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);    // a.b0 | b.b0 << 8
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);               // ab.lo16 | cd.lo16 << 16
 }
 
 // ---------------------------------------------------------------------------
@@ -178,6 +232,22 @@ __device__ __forceinline__ void digits3(float x, float inv, int& d0, int& d1, in
     d0 = (int)f0;
     d1 = (int)f1;
     d2 = (int)f2;
+}
+
+// The same three digits as offset words (the low byte of each is the digit).
+// |x * inv| <= 127 rounds to |d0| <= 127 and each remainder stays within
+// 254 * 0.5 = 127, so no clamping is needed.
+__device__ __forceinline__ void digits3_words(float x, float inv, uint32_t& w0, uint32_t& w1,
+                                              uint32_t& w2) {
+    const float u = x * inv;
+    const float z0 = u + kRoundOff;
+    const float r1 = (u - (z0 - kRoundOff)) * 254.0f;
+    const float z1 = r1 + kRoundOff;
+    const float r2 = (r1 - (z1 - kRoundOff)) * 254.0f;
+    const float z2 = r2 + kRoundOff;
+    w0 = __float_as_uint(z0);
+    w1 = __float_as_uint(z1);
+    w2 = __float_as_uint(z2);
 }
 
 // Window-size bucket a kernel is instantiated for.
