@@ -14,8 +14,13 @@ quantized by its quantizer.
 
 Printed (one JSON line): tokens/s through one layer (B * W * L tokens per
 step), the decode kernel's roofline (algorithmic bytes over its per-launch
-duration measured with HIP events on the launch stream), the flush's, and the
-CPU oracle timed on a bounded sample of the same workload.
+duration: the kernel's own execution interval, from the library's timing hook
+of start/stop HIP events on the launch stream), the flush's, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Profile summaries (text under profiles/) from rocprofv3 output:
+    python bench.py --trace-summary OUT.md  STATS.csv  -- "<command that made it>"
+    python bench.py --pmc-summary   OUT.md  FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR -- "<commands>"
 """
 from __future__ import annotations
 
@@ -82,9 +87,118 @@ def read_traffic(wl, hsh: str):
     return None
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    return name.replace("lq::(anonymous namespace)::", "").split("(lq")[0].strip()
+
+
+def trace_summary(out_md: str, stats_csv: str, command: str):
+    """Per-kernel average durations from rocprofv3 --kernel-trace --stats."""
+    rows = _csv_rows(stats_csv)
+    lines = [f"# Kernel durations: {os.path.basename(out_md)[:-3]}", "",
+             "Command (from the repository root; rocprofv3 writes `*_kernel_stats.csv`):", "",
+             "```", command, "```", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    dec, fl = [], []
+    other = 0
+    for r in rows:
+        if "lq::" not in r["Name"]:
+            other += int(r["Calls"])
+            continue
+        nm = _short(r["Name"])
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{nm}` | {r['Calls']} | {avg:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
+                     f"{float(r['MaxNs']) / 1e3:.3f} |")
+        if "decode_kernel" in nm:
+            dec.append((int(r["Calls"]), avg))
+        if "flush_kernel" in nm:
+            fl.append((int(r["Calls"]), avg))
+    summ = {}
+    if dec:
+        summ["decode_avg_launch_us"] = round(sum(c * a for c, a in dec) / sum(c for c, _ in dec), 3)
+        summ["decode_instantiations"] = len(dec)
+    if fl:
+        summ["flush_avg_launch_us"] = round(sum(c * a for c, a in fl) / sum(c for c, _ in fl), 3)
+    lines += ["", f"({other} launches of the harness's own torch kernels not listed.)", "",
+              "Average over all decode launches (every window slot equally often):", "",
+              json.dumps(summ), ""]
+    open(out_md, "w").write("\n".join(lines))
+    print(json.dumps(summ))
+
+
+def _pmc_per_dispatch(d: str, counter: str, pat: str):
+    """Mean per-dispatch value of `counter` over dispatches whose kernel name
+    contains `pat` (rocprofv3 --pmc CSV)."""
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in _csv_rows(f):
+            if r["Counter_Name"] == counter and pat in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def pmc_summary(out_md: str, fetch_dir: str, write_dir: str, cal_fetch: str, cal_write: str,
+                command: str):
+    """HBM traffic per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the counter reads for a plain device copy
+    of known size."""
+    wl_bytes = 1 << 30                      # --copy-calib: 1 GiB read + 1 GiB written per copy
+    # the copy dispatches are the largest ones in the calibration run
+    def largest(d, c):
+        import glob
+        best = 0.0
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in _csv_rows(f):
+                if r["Counter_Name"] == c:
+                    best = max(best, float(r["Counter_Value"]))
+        return best
+    cf, cw = largest(cal_fetch, "FETCH_SIZE"), largest(cal_write, "WRITE_SIZE")
+    f_fetch = wl_bytes / (cf * 1024.0)
+    f_write = wl_bytes / (cw * 1024.0)
+    df, ndf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "decode_kernel")
+    dw, ndw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "decode_kernel")
+    ff, nff = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "flush_kernel")
+    fw, nfw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "flush_kernel")
+    dec_bytes = df * 1024.0 * f_fetch + dw * 1024.0 * f_write
+    fl_bytes = (ff * 1024.0 * f_fetch + fw * 1024.0 * f_write) if ff is not None else None
+    from recurrent_state_quant_lq_amd.configs import PRESETS
+    wl = PRESETS["gdn_batched"]
+    alg = sum(decode_bytes(wl, n) for n in range(wl.W)) / wl.W
+    rec = {"kernel_hash": kernel_hash(), "hbm_bytes_per_launch": int(dec_bytes),
+           "algorithmic_bytes_per_launch": int(alg), "traffic_over_algorithmic": round(dec_bytes / alg, 4),
+           "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
+           "flush_hbm_bytes_per_launch": int(fl_bytes) if fl_bytes else None,
+           "flush_algorithmic_bytes": flush_bytes(wl, wl.W)}
+    lines = [f"# HBM traffic: {os.path.basename(out_md)[:-3]}", "",
+             "Commands (from the repository root, one counter per run):", "", "```", command, "```", "",
+             "| quantity | value |", "|---|---:|",
+             f"| copy calibration: FETCH_SIZE KiB per 1 GiB copy | {cf:.0f} (factor {f_fetch:.4f}) |",
+             f"| copy calibration: WRITE_SIZE KiB per 1 GiB copy | {cw:.0f} (factor {f_write:.4f}) |",
+             f"| decode: FETCH_SIZE KiB per dispatch (mean of {ndf}) | {df:.1f} |",
+             f"| decode: WRITE_SIZE KiB per dispatch (mean of {ndw}) | {dw:.1f} |",
+             f"| decode: scaled HBM bytes per launch | {dec_bytes:.0f} |",
+             f"| decode: algorithmic bytes per launch (slot mean) | {alg:.0f} |"]
+    if fl_bytes:
+        lines += [f"| flush: FETCH_SIZE / WRITE_SIZE KiB per dispatch | {ff:.1f} / {fw:.1f} |",
+                  f"| flush: scaled HBM bytes per launch | {fl_bytes:.0f} |",
+                  f"| flush: algorithmic bytes per launch | {flush_bytes(wl, wl.W)} |"]
+    lines += ["", "Record read by bench.py (valid while the decode kernel source hashes to kernel_hash):",
+              "", json.dumps(rec), ""]
+    open(out_md, "w").write("\n".join(lines))
+    print(json.dumps(rec))
+
+
 def cpu_baseline(wl, windows: int, threads: int):
     """The oracle (plain C, as it is) on the host: the windowed int8 scheme
-    for all B*H heads of one layer over `windows` windows."""
+    for all B*H heads of one layer, `windows` consecutive windows per head
+    (each head's codec carried from window to window; the window's W tokens
+    are reused)."""
     import numpy as np
     import oracle as O
     from recurrent_state_quant_lq_amd import inputs
@@ -94,12 +208,13 @@ def cpu_baseline(wl, windows: int, threads: int):
     H0 = (rng.standard_normal((wl.dk, wl.dv)) * 0.1).astype(np.float32)
     cd0 = O.quantize(H0, wl.C, wl.smooth)
     heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
-    per_head = {bh: {k: np.ascontiguousarray(np.concatenate([v[:, bh[0], bh[1]]] * windows))
-                     for k, v in tok.items()} for bh in heads}
 
     def one(bh):
-        O.run_head(wl.dk, wl.dv, wl.per_key, wl.W, wl.C, wl.smooth, route=0, use_codec=True,
-                   tok=per_head[bh], codec=cd0)
+        t = O.head_tokens(tok, bh[0], bh[1])
+        cd = cd0
+        for _ in range(windows):
+            cd = O.run_head(wl.dk, wl.dv, wl.per_key, wl.W, wl.C, wl.smooth, route=0, use_codec=True,
+                            tok=t, codec=cd)[1]
 
     from concurrent.futures import ThreadPoolExecutor
     t0 = time.perf_counter()
@@ -112,6 +227,18 @@ def cpu_baseline(wl, windows: int, threads: int):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] in ("--trace-summary", "--pmc-summary"):
+        argv = sys.argv[2:]
+        cmd = ""
+        if "--" in argv:
+            k = argv.index("--")
+            cmd = " ".join(argv[k + 1:])
+            argv = argv[:k]
+        if sys.argv[1] == "--trace-summary":
+            trace_summary(argv[0], argv[1], cmd)
+        else:
+            pmc_summary(argv[0], argv[1], argv[2], argv[3], argv[4], cmd)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
@@ -120,7 +247,7 @@ def main():
     ap.add_argument("--workload", default="gdn_batched")
     ap.add_argument("--W", type=int, default=0, help="override the window length")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-windows", type=int, default=8)
+    ap.add_argument("--cpu-windows", type=int, default=128)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (for PMC calibration)")
     args = ap.parse_args()
@@ -176,22 +303,14 @@ def main():
     o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step():
         for n in range(W):
             for l in range(L):
                 tk = ring[l]
-                if ev is not None:
-                    ev[0][n][l].record()
                 lq.lq_gdn_decode_step(layers[l], n, tk["q"][n], tk["k"][n], tk["v"][n],
                                       tk["alpha"][n], tk["beta"][n], o)
-                if ev is not None:
-                    ev[1][n][l].record()
         for l in range(L):
-            if ev is not None:
-                ev[2][l].record()
             lq.lq_gdn_window_flush(layers[l], W)
-            if ev is not None:
-                ev[3][l].record()
 
     for _ in range(args.warmup):
         step()
@@ -210,21 +329,23 @@ def main():
     tokens_per_step = wl.B * W * L
     value = tokens_per_step / (ms * 1e-3)
 
-    # ---- per-launch kernel durations (HIP events on the launch stream) ----------
-    E = lambda: torch.cuda.Event(enable_timing=True)
+    # ---- per-launch kernel durations ---------------------------------------------
+    # The library's timing hook gives each launch a start/stop event pair bound
+    # to the kernel's own execution interval (hipExtLaunchKernelGGL on the launch
+    # stream), the interval rocprofv3's kernel trace reports.
     reps = max(2, min(8, args.steps))
     dec_ms = [0.0] * W
     fl_ms = 0.0
     for _ in range(reps):
-        ev = ([[E() for _ in range(L)] for _ in range(W)], [[E() for _ in range(L)] for _ in range(W)],
-              [E() for _ in range(L)], [E() for _ in range(L)])
-        step(ev)
-        torch.cuda.synchronize()
-        for n in range(W):
-            for l in range(L):
-                dec_ms[n] += ev[0][n][l].elapsed_time(ev[1][n][l])
-        for l in range(L):
-            fl_ms += ev[2][l].elapsed_time(ev[3][l])
+        lq.lq_timing_enable(True)
+        step()
+        lq.lq_timing_enable(False)
+        fam, t_ms = lq.lq_timing_collect(W * L + L)
+        want = [lq.LQ_KERNEL_DECODE] * (W * L) + [lq.LQ_KERNEL_FLUSH] * L
+        assert fam == want, "unexpected launch sequence"
+        for i in range(W * L):
+            dec_ms[i // L] += t_ms[i]
+        fl_ms += sum(t_ms[W * L:])
     launches = reps * L
     dec_avg_us = [1e3 * x / launches for x in dec_ms]
     dec_bytes = [decode_bytes(wl, n) for n in range(W)]

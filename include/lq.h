@@ -187,6 +187,31 @@ int lq_last_hip_error(void);
 /* LQ_OK if every entry point accepts the shape d (same checks they run). */
 int lq_check_dims(const lq_dims *d);
 
+/*
+ * Kernel timing (measurement support, not part of the method).  While
+ * enabled, every kernel the library launches carries a start/stop event pair
+ * that records the kernel's own execution interval (hipExtLaunchKernelGGL),
+ * so the durations exclude launch gaps and host overhead.  Kernel families:
+ */
+enum {
+    LQ_KERNEL_DECODE = 0,       /* lq_gdn_decode_step */
+    LQ_KERNEL_FLUSH = 1,        /* lq_gdn_window_flush */
+    LQ_KERNEL_QUANTIZE = 2,     /* lq_gdn_state_quantize */
+    LQ_KERNEL_DEQUANTIZE = 3,   /* lq_gdn_state_dequantize */
+    LQ_KERNEL_FP32_RECURRENCE = 4
+};
+
+/* on = 1: drop earlier records and start recording (at most 65536 launches;
+ * later ones run untimed); on = 0: stop recording.  Process-wide; not for
+ * concurrent use from several host threads. */
+int lq_timing_enable(int32_t on);
+
+/* Waits for the recorded launches, writes the first min(max_records, n) of
+ * them in launch order (family[i], ms[i] = kernel duration in milliseconds;
+ * host arrays, may be NULL if max_records = 0), sets *count = n and drops the
+ * records.  Errors: LQ_ERR_NULL, LQ_ERR_HIP. */
+int lq_timing_collect(int32_t max_records, int32_t *family, float *ms, int32_t *count);
+
 #ifdef __cplusplus
 }
 #endif

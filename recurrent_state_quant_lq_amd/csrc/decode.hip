@@ -356,8 +356,7 @@ template <int DK, int WM, bool KDA, int NB>
 hipError_t launch_nb(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
     constexpr int NT = Dec<DK, DK, WM, KDA>::NT;
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
-    hipLaunchKernelGGL((decode_kernel<DK, DK, WM, KDA, NB>), dim3(grid), dim3(NT), 0, s, args);
-    return hipGetLastError();
+    return launch_kernel(LQ_KERNEL_DECODE, decode_kernel<DK, DK, WM, KDA, NB>, dim3(grid), dim3(NT), s, args);
 }
 
 // dk = 128, W <= 16: one kernel per window position (no runtime guards).

@@ -696,9 +696,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
 
 template <int DK, int WM, bool KDA>
 hipError_t flush_t(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
-    hipLaunchKernelGGL((flush_kernel<DK, DK, WM, KDA>), dim3((unsigned)d.B * (unsigned)d.H),
-                       dim3(FS<DK, DK>::NT), 0, s, args);
-    return hipGetLastError();
+    return launch_kernel(LQ_KERNEL_FLUSH, flush_kernel<DK, DK, WM, KDA>, dim3((unsigned)d.B * (unsigned)d.H),
+                         dim3(FS<DK, DK>::NT), s, args);
 }
 
 template <int DK>
@@ -725,22 +724,20 @@ hipError_t launch_quantize(const lq_dims& d, const float* h, const lq_state& st,
     QuantArgs args{h, st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val, d.C, d.smooth};
     const dim3 grid((unsigned)d.B * (unsigned)d.H);
     switch (d.dk) {
-        case 16: hipLaunchKernelGGL((quantize_kernel<16, 16>), grid, dim3(FS<16, 16>::NT), 0, s, args); break;
-        case 64: hipLaunchKernelGGL((quantize_kernel<64, 64>), grid, dim3(FS<64, 64>::NT), 0, s, args); break;
-        default: hipLaunchKernelGGL((quantize_kernel<128, 128>), grid, dim3(FS<128, 128>::NT), 0, s, args); break;
+        case 16: return launch_kernel(LQ_KERNEL_QUANTIZE, quantize_kernel<16, 16>, grid, dim3(FS<16, 16>::NT), s, args);
+        case 64: return launch_kernel(LQ_KERNEL_QUANTIZE, quantize_kernel<64, 64>, grid, dim3(FS<64, 64>::NT), s, args);
+        default: return launch_kernel(LQ_KERNEL_QUANTIZE, quantize_kernel<128, 128>, grid, dim3(FS<128, 128>::NT), s, args);
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* h_out, hipStream_t s) {
     DequantArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val, h_out, d.C};
     const dim3 grid((unsigned)d.B * (unsigned)d.H);
     switch (d.dk) {
-        case 16: hipLaunchKernelGGL((dequantize_kernel<16, 16>), grid, dim3(256), 0, s, args); break;
-        case 64: hipLaunchKernelGGL((dequantize_kernel<64, 64>), grid, dim3(256), 0, s, args); break;
-        default: hipLaunchKernelGGL((dequantize_kernel<128, 128>), grid, dim3(256), 0, s, args); break;
+        case 16: return launch_kernel(LQ_KERNEL_DEQUANTIZE, dequantize_kernel<16, 16>, grid, dim3(256), s, args);
+        case 64: return launch_kernel(LQ_KERNEL_DEQUANTIZE, dequantize_kernel<64, 64>, grid, dim3(256), s, args);
+        default: return launch_kernel(LQ_KERNEL_DEQUANTIZE, dequantize_kernel<128, 128>, grid, dim3(256), s, args);
     }
-    return hipGetLastError();
 }
 
 }  // namespace lq

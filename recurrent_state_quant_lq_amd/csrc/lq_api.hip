@@ -2,6 +2,10 @@
 // Every check runs before any HIP call; on an error nothing is enqueued.
 #include "lq_internal.h"
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 namespace {
 
 thread_local int g_last_hip = 0;
@@ -69,7 +73,70 @@ int finish(hipError_t e) {
     return LQ_OK;
 }
 
+// ---- kernel timing -----------------------------------------------------------------------------
+constexpr size_t kMaxTimed = 65536;
+
+struct TimedLaunch {
+    int family;
+    hipEvent_t start, stop;
+};
+
+std::mutex g_tmu;
+std::atomic<bool> g_timing{false};
+std::vector<TimedLaunch> g_timed;                          // this recording, in launch order
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_pool;     // reused event pairs
+
 }  // namespace
+
+bool lq::timing_slot(int family, hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_timing.load(std::memory_order_relaxed)) return false;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_timed.size() >= kMaxTimed) return false;
+    if (g_timed.size() == g_pool.size()) {
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipEventCreate(&a) != hipSuccess) return false;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return false;
+        }
+        g_pool.emplace_back(a, b);
+    }
+    const auto& pr = g_pool[g_timed.size()];
+    g_timed.push_back({family, pr.first, pr.second});
+    *start = pr.first;
+    *stop = pr.second;
+    return true;
+}
+
+extern "C" {
+
+int lq_timing_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (on) g_timed.clear();
+    g_timing.store(on != 0);
+    return LQ_OK;
+}
+
+int lq_timing_collect(int32_t max_records, int32_t* family, float* ms, int32_t* count) {
+    if (!count || (max_records > 0 && (!family || !ms))) return LQ_ERR_NULL;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    const int32_t n = (int32_t)g_timed.size();
+    for (int32_t i = 0; i < n; ++i) {
+        hipError_t e = hipEventSynchronize(g_timed[i].stop);
+        if (e != hipSuccess) return finish(e);
+        if (i < max_records) {
+            float t = 0.0f;
+            if ((e = hipEventElapsedTime(&t, g_timed[i].start, g_timed[i].stop)) != hipSuccess) return finish(e);
+            family[i] = g_timed[i].family;
+            ms[i] = t;
+        }
+    }
+    g_timed.clear();
+    *count = n;
+    return LQ_OK;
+}
+
+}  // extern "C"
 
 extern "C" {
 

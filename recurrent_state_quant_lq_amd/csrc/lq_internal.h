@@ -1,6 +1,7 @@
 // Internal declarations shared by the HIP sources of liblq.so (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,6 +21,22 @@ hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* h_out,
 hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const float* q,
                                   const float* k, const float* v, const float* alpha,
                                   const float* beta, float* o, hipStream_t s);
+
+// Kernel timing (lq_timing_*): when recording is on, hands out the event
+// pair of the next launch of `family` and returns true.
+bool timing_slot(int family, hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through here.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(int family, void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s,
+                         Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (timing_slot(family, &e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    return hipGetLastError();
+}
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));

@@ -122,10 +122,10 @@ __global__ __launch_bounds__(NT) void fp32_rec_kernel(RecArgs a) {
 }
 
 template <int DK, bool KDA>
-void rec_t(const lq_dims& d, const RecArgs& args, hipStream_t s) {
+hipError_t rec_t(const lq_dims& d, const RecArgs& args, hipStream_t s) {
     constexpr int NT = DK >= 64 ? 256 : 64;
-    hipLaunchKernelGGL((fp32_rec_kernel<DK, DK, KDA, NT>), dim3((unsigned)d.B * (unsigned)d.H),
-                       dim3(NT), 0, s, args);
+    return launch_kernel(LQ_KERNEL_FP32_RECURRENCE, fp32_rec_kernel<DK, DK, KDA, NT>,
+                         dim3((unsigned)d.B * (unsigned)d.H), dim3(NT), s, args);
 }
 
 }  // namespace
@@ -136,11 +136,10 @@ hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const float
     RecArgs args{h, q, k, v, alpha, beta, o, T, (size_t)d.B * (size_t)d.H};
     const bool kda = d.decay_mode == LQ_DECAY_PER_KEY;
     switch (d.dk) {
-        case 16: kda ? rec_t<16, true>(d, args, s) : rec_t<16, false>(d, args, s); break;
-        case 64: kda ? rec_t<64, true>(d, args, s) : rec_t<64, false>(d, args, s); break;
-        default: kda ? rec_t<128, true>(d, args, s) : rec_t<128, false>(d, args, s); break;
+        case 16: return kda ? rec_t<16, true>(d, args, s) : rec_t<16, false>(d, args, s);
+        case 64: return kda ? rec_t<64, true>(d, args, s) : rec_t<64, false>(d, args, s);
+        default: return kda ? rec_t<128, true>(d, args, s) : rec_t<128, false>(d, args, s);
     }
-    return hipGetLastError();
 }
 
 }  // namespace lq

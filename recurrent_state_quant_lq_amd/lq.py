@@ -25,7 +25,10 @@ LQ_DECAY_SCALAR, LQ_DECAY_PER_KEY = 0, 1
 # every symbol include/lq.h declares
 EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_state_quantize",
            "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_state_bytes",
-           "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims")
+           "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims",
+           "lq_timing_enable", "lq_timing_collect")
+LQ_KERNEL_DECODE, LQ_KERNEL_FLUSH, LQ_KERNEL_QUANTIZE, LQ_KERNEL_DEQUANTIZE, \
+    LQ_KERNEL_FP32_RECURRENCE = range(5)
 
 
 class lq_dims(ct.Structure):
@@ -74,6 +77,11 @@ def load() -> ct.CDLL:
         L.lq_status_str.argtypes = [ct.c_int]
         L.lq_status_str.restype = ct.c_char_p
         L.lq_last_hip_error.argtypes = []
+        L.lq_timing_enable.argtypes = [ct.c_int32]
+        L.lq_timing_enable.restype = ct.c_int
+        L.lq_timing_collect.argtypes = [ct.c_int32, ct.POINTER(ct.c_int32), ct.POINTER(ct.c_float),
+                                        ct.POINTER(ct.c_int32)]
+        L.lq_timing_collect.restype = ct.c_int
         _lib = L
     return _lib
 
@@ -247,3 +255,18 @@ def lq_buffer_bytes(d: lq_dims) -> int:
 
 def lq_check_dims(d: lq_dims) -> int:
     return int(load().lq_check_dims(ct.byref(d)))
+
+
+def lq_timing_enable(on: bool = True):
+    _raise("lq_timing_enable", load().lq_timing_enable(1 if on else 0))
+
+
+def lq_timing_collect(max_records: int = 65536):
+    """Per-launch kernel durations recorded since lq_timing_enable(True), in
+    launch order: (families, milliseconds) as lists; drops the records."""
+    fam = (ct.c_int32 * max_records)()
+    ms = (ct.c_float * max_records)()
+    n = ct.c_int32(0)
+    _raise("lq_timing_collect", load().lq_timing_collect(max_records, fam, ms, ct.byref(n)))
+    k = min(n.value, max_records)
+    return list(fam[:k]), list(ms[:k])

@@ -134,3 +134,16 @@ def test_status_strings():
         assert L.lq_status_str(s)
     assert L.lq_status_str(1234) == b"unknown status"
     assert L.lq_last_hip_error() == 0
+
+
+def test_timing_hook_host_side():
+    """Recording on/off and collecting with no launches touch no GPU."""
+    L = ct.CDLL(lq.LIB_PATH)
+    L.lq_timing_collect.argtypes = [ct.c_int32, ct.c_void_p, ct.c_void_p, ct.c_void_p]
+    n = ct.c_int32(-1)
+    assert L.lq_timing_enable(1) == lq.LQ_OK
+    assert L.lq_timing_collect(0, None, None, ct.byref(n)) == lq.LQ_OK
+    assert n.value == 0
+    assert L.lq_timing_collect(4, None, None, ct.byref(n)) == lq.LQ_ERR_NULL
+    assert L.lq_timing_collect(0, None, None, None) == lq.LQ_ERR_NULL
+    assert L.lq_timing_enable(0) == lq.LQ_OK

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle as O
-from recurrent_state_quant_lq_amd import lq
+from recurrent_state_quant_lq_amd import inputs, lq
 from recurrent_state_quant_lq_amd.configs import PRESETS
 
 pytestmark = pytest.mark.gpu
@@ -279,3 +279,25 @@ def test_window_full_is_rejected():
         lq.lq_gdn_decode_step(st, 4, z, z, z, torch.ones((1, 1), device="cuda"),
                               torch.zeros((1, 1), device="cuda"), z)
     assert e.value.status == lq.LQ_ERR_WINDOW_FULL
+
+
+def test_timing_hook_records_each_launch():
+    """The timing hook records decode and flush launches in order, with
+    positive kernel durations, and nothing while it is off."""
+    d = lq.make_dims(2, 4, 128, 128, 16, 4, 0, 1)
+    st = lq.LayerState.allocate(d)
+    st.col_scale.fill_(1.0)
+    tok = {k: torch.from_numpy(v).cuda() for k, v in
+           inputs.host_tokens(5, 3, 2, 4, 128, 128, per_key=False, beta_lo=0.1, beta_hi=0.9).items()}
+    o = torch.empty((2, 4, 128), device="cuda")
+    lq.lq_timing_enable(True)
+    for n in range(3):
+        lq.lq_gdn_decode_step(st, n, tok["q"][n], tok["k"][n], tok["v"][n], tok["alpha"][n],
+                              tok["beta"][n], o)
+    lq.lq_gdn_window_flush(st, 3)
+    lq.lq_timing_enable(False)
+    lq.lq_gdn_window_flush(st, 0)
+    fam, ms = lq.lq_timing_collect()
+    assert fam == [lq.LQ_KERNEL_DECODE] * 3 + [lq.LQ_KERNEL_FLUSH]
+    assert all(0.0 < x < 100.0 for x in ms), ms
+    assert lq.lq_timing_collect() == ([], [])
