@@ -157,27 +157,6 @@ void decode_kernel(DecodeArgs a) {
         }
     }
 
-    // ---- int8 state -> VGPRs (MFMA A operands) ------------------------------------------
-    // lane l of wave w: column j = tile*16 + l%16, channels ks*64 + 16*(l/16) .. +15
-    v4i sqa[TPW][KS];
-    {
-        // Every tile and K step is real when the shape divides evenly; the loads
-        // are then unconditional, so no register merge waits on them.
-        constexpr bool FULL = (NTILE % D::NW == 0) && (DK % 64 == 0);
-        const int8_t* sq = a.sq + head * (DK * DV);
-#pragma unroll
-        for (int tw = 0; tw < TPW; ++tw)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int tile = w * TPW + tw;
-                const int i0 = ks * 64 + 16 * (lane / 16);
-                if (FULL || (tile < NTILE && i0 < DK))
-                    sqa[tw][ks] = *reinterpret_cast<const v4i*>(sq + (size_t)(tile * 16 + lane % 16) * DK + i0);
-                else
-                    sqa[tw][ks] = v4i{0, 0, 0, 0};
-            }
-    }
-
     // ---- buffer rows -> VGPRs -------------------------------------------------------------
     const int slot0 = t / TPS;
     const int c0 = (t % TPS) * CH;
@@ -205,7 +184,31 @@ void decode_kernel(DecodeArgs a) {
             if (i < n) col[i] = bur[(size_t)i * DV + j];
     }
 
-    all_loads_barrier();
+    // ---- int8 state -> VGPRs (MFMA A operands), issued last ---------------------------------
+    // lane l of wave w: column j = tile*16 + l%16, channels ks*64 + 16*(l/16) .. +15.
+    // Every tile and K step is real when the shape divides evenly; the loads are
+    // then unconditional, and the first barrier waits for everything but these
+    // TPW*KS loads, which stream in while the buffer phases run.
+    constexpr bool FULL = (NTILE % D::NW == 0) && (DK % 64 == 0);
+    __builtin_amdgcn_sched_barrier(0);
+    v4i sqa[TPW][KS];
+    {
+        const int8_t* sq = a.sq + head * (DK * DV);
+#pragma unroll
+        for (int tw = 0; tw < TPW; ++tw)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int tile = w * TPW + tw;
+                const int i0 = ks * 64 + 16 * (lane / 16);
+                if (FULL || (tile < NTILE && i0 < DK))
+                    sqa[tw][ks] = *reinterpret_cast<const v4i*>(sq + (size_t)(tile * 16 + lane % 16) * DK + i0);
+                else
+                    sqa[tw][ks] = v4i{0, 0, 0, 0};
+            }
+    }
+
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_keep_loads<FULL ? TPW * KS : 0>();
 
     const float beta = __int_as_float(s_misc[8]);
     float gn_s = 0.0f;
@@ -262,6 +265,7 @@ void decode_kernel(DecodeArgs a) {
     // ---- 2. WY append, transformed query and its int8 digits ---------------------------------
     float wsum = 0.0f;
     float q2 = 0.0f;
+    float st_y = 0.0f, st_k = 0.0f, st_g = 0.0f, st_u = 0.0f;   // slot n, stored after the GEMV
     if (is_ch) {
         const float qc = s_vec[D::SQ * DK + t], kc = s_vec[D::SK * DK + t];
         float gn;
@@ -277,10 +281,9 @@ void decode_kernel(DecodeArgs a) {
             }
         const float yn = beta * ay;
         const float qp = aq - s_a[n] * yn;
-        a.by[head * (size_t)W * DK + (size_t)n * DK + t] = yn;
-        a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = kc;
-        if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = gn;
-        else if (t == 0) a.bg[head * (size_t)W + n] = gn;
+        st_y = yn;
+        st_k = kc;
+        st_g = gn;
         s_qp[t] = qp;
         q2 = s_vec[D::SR * DK + t] * qp;
     } else if (is_val) {
@@ -293,7 +296,7 @@ void decode_kernel(DecodeArgs a) {
             }
         const float un = beta * au;
         wsum += s_a[n] * un;
-        a.bu[head * (size_t)W * DV + (size_t)n * DV + j] = un;
+        st_u = un;
     }
     if (w < KS) {
         // this wave's 64 channels form one block: scale M = max |q''|, digits of q''
@@ -342,7 +345,17 @@ void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
 
-    // ---- 4. output ------------------------------------------------------------------------------
+    // ---- 4. slot n and the output ------------------------------------------------------------
+    // (the slot stores come after the GEMV so its wait for the state loads does
+    // not also wait for them)
+    if (is_ch) {
+        a.by[head * (size_t)W * DK + (size_t)n * DK + t] = st_y;
+        a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = st_k;
+        if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = st_g;
+        else if (t == 0) a.bg[head * (size_t)W + n] = st_g;
+    } else if (is_val) {
+        a.bu[head * (size_t)W * DV + (size_t)n * DV + j] = st_u;
+    }
     if (is_val) {
         float out = s_vec[D::SS * DK + j] * s_gem[j] + wsum;
 #pragma unroll

@@ -53,14 +53,22 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Waits for every outstanding load of this wave (LDS copies included), then a
-// full workgroup barrier; no memory access moves across it.
-__device__ __forceinline__ void all_loads_barrier() {
-    __builtin_amdgcn_s_waitcnt(0);
+// Waits until at most N vector-memory operations of this wave are still
+// outstanding (loads complete in issue order, LDS copies included), then a
+// workgroup barrier with full fences (no memory access moves across it).  The
+// N most recently issued loads stay in flight across the barrier; the
+// compiler waits for them where their registers are used.
+template <int N>
+__device__ __forceinline__ void barrier_keep_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14));   // vmcnt(N) expcnt(0) lgkmcnt(0)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
+
+// Waits for every outstanding load of this wave, then a full barrier.
+__device__ __forceinline__ void all_loads_barrier() { barrier_keep_loads<0>(); }
 
 // ---------------------------------------------------------------------------
 // cross-lane
