@@ -43,12 +43,12 @@ PMC_FILE = os.path.join(ROOT, "profiles", "decode_step_gdn_b64_h32_d128_w16_pmc.
 def decode_bytes(wl, n: int) -> int:
     """Algorithmic HBM bytes of one decode launch at window slot n: the codec
     (int8 state, scales, compensators), the token inputs and output, the n
-    buffered slots read and slot n written."""
+    buffered slots (k_i, m_i, g_i) read and slot n written."""
     dk, dv, C = wl.dk, wl.dv, wl.C
     a = dk if wl.per_key else 1
     codec = dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4)
     io = 4 * (2 * dk + dv + a + 1) + 4 * dv
-    slot = 4 * (2 * dk + dv + a)
+    slot = 4 * (dk + dv + a)
     return wl.B * wl.H * (codec + io + (n + 1) * slot)
 
 
@@ -58,12 +58,12 @@ def flush_bytes(wl, N: int) -> int:
     dk, dv, C = wl.dk, wl.dv, wl.C
     a = dk if wl.per_key else 1
     codec = dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4)
-    return wl.B * wl.H * (2 * codec + N * 4 * (2 * dk + dv + a))
+    return wl.B * wl.H * (2 * codec + N * 4 * (dk + dv + a))
 
 
 def flush_flops(wl, N: int) -> int:
-    """The two contractions of the rebuild: 2 * (N*dk*dv) multiply-adds."""
-    return wl.B * wl.H * 4 * N * wl.dk * wl.dv
+    """The rebuild's contraction Kt^T M: N*dk*dv multiply-adds."""
+    return wl.B * wl.H * 2 * N * wl.dk * wl.dv
 
 
 def kernel_hash() -> str:

@@ -25,16 +25,17 @@
  * quantized residual is sq[j*dk + i], so each value column's dk key-channel
  * bytes are contiguous (the operand layout of the int8 matrix cores).
  * It stays fixed for a window of W tokens ([news ¶3]); the window's updates
- * live in an fp32 buffer (WY form, see lq_gdn_decode_step) and the state is
- * rebuilt and requantized once at the window's end (lq_gdn_window_flush).
+ * live in an fp32 buffer (see lq_gdn_decode_step) and the state is rebuilt
+ * and requantized once at the window's end (lq_gdn_window_flush).
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers, owned by the caller, contiguous
  *     row-major in the shapes given, 16-byte aligned, except beta and the
  *     scalar-mode alpha (one float per head), which need 4-byte alignment
- *     only.  The library allocates
- *     nothing, keeps no global state except the last HIP error code (per
- *     thread), never synchronises, and is re-entrant.
+ *     only.  The library allocates no device memory, keeps no global state
+ *     except the last HIP error code (per thread) and, while kernel timing is
+ *     on, its timing records; it never synchronises (except
+ *     lq_timing_collect) and the compute entry points are re-entrant.
  *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
  *     asynchronously on it.
  *   - Return value: LQ_OK or an LQ_ERR_* code.  Argument checks run first and
@@ -82,9 +83,9 @@ typedef struct lq_dims {
  *   col_scale fp32  [B,H,dv]      per-column smoothing factor
  *   comp_idx  int32 [B,H,C]       compensator rows, ascending
  *   comp_val  fp32  [B,H,C,dv]    compensator rows' values (exact fp32)
- *   buf_k     fp32  [B,H,W,dk]    window buffer: keys
- *   buf_y     fp32  [B,H,W,dk]    window buffer: WY left factors y_n
- *   buf_u     fp32  [B,H,W,dv]    window buffer: WY value terms u_n
+ *   buf_k     fp32  [B,H,W,dk]    window buffer: keys k_n
+ *   buf_m     fp32  [B,H,W,dv]    window buffer: m_n = u_n - Hb^T y_n (see
+ *                                 lq_gdn_decode_step)
  *   buf_g     fp32  [B,H,W,gd]    window buffer: window-local cumulative log decay
  * comp_idx/comp_val may be NULL when C = 0. */
 typedef struct lq_state {
@@ -94,8 +95,7 @@ typedef struct lq_state {
     int32_t *comp_idx;
     float *comp_val;
     float *buf_k;
-    float *buf_y;
-    float *buf_u;
+    float *buf_m;
     float *buf_g;
 } lq_state;
 
@@ -106,14 +106,18 @@ typedef struct lq_state {
  * real tokens.
  *
  * pos = n = number of tokens already buffered in this window (0..W-1).
- * Appends slot n to the buffer (g_n = g_{n-1} + log alpha, g_{-1} = 0;
- * E_i = exp(g_n - g_i);  rr_i = <k, E_i o k_i>;
- * y_n = beta (exp(g_n) o k - sum_{i<n} rr_i y_i);
- * u_n = beta (v - sum_{i<n} rr_i u_i)) and writes
- *     o = Hb^T q' + sum_{i<=n} a_i u_i,   a_i = <q, E_i o k_i>,
- *     q' = exp(g_n) o q - sum_{i<=n} a_i y_i,
- * which is exactly H_n^T q for the state H_n reached from the window-base
- * state Hb (the dequantized codec) by the window's n+1 delta-rule steps.
+ * With Hb the window-base state (the dequantized codec, fixed for the
+ * window), g_n = g_{n-1} + log alpha (g_{-1} = 0), E_i = exp(g_n - g_i),
+ * rr_i = <k, E_i o k_i> and a_i = <q, E_i o k_i> (a_n = <q, k>), the step
+ * appends slot n = (k, g_n, m_n),
+ *     m_n = beta (v - Hb^T (exp(g_n) o k) - sum_{i<n} rr_i m_i),
+ * and writes
+ *     o = Hb^T (exp(g_n) o q) + sum_{i<=n} a_i m_i,
+ * which is exactly H_n^T q for the state H_n reached from Hb by the window's
+ * n+1 delta-rule steps.  (In the WY form of those steps,
+ * H_n = A_n Hb + sum_i (E_i o k_i) u_i^T with A_n = Gamma_n - sum_i
+ * (E_i o k_i) y_i^T; the buffer keeps m_i = u_i - Hb^T y_i, i.e. the WY
+ * factors projected once through the fixed Hb.)
  *   q, k  fp32 [B,H,dk];  v, o fp32 [B,H,dv];  beta fp32 [B,H];
  *   alpha fp32 [B,H] (scalar mode) or [B,H,dk] (per-key mode), in (0, 1].
  * Reads the codec and buffer slots 0..n-1; writes buffer slot n and o.
@@ -126,8 +130,8 @@ int lq_gdn_decode_step(const lq_dims *d, const lq_state *st, int32_t pos,
 /*
  * Window boundary for every (b, h) ([news ¶3]: the state is rebuilt and
  * quantized once at the boundary; [forum] techniques 2-3, [news ¶4]).
- * From the codec and n_buffered slots (0..W) it rebuilds
- *     H = Gamma Hb + sum_i (E_{N-1,i} o k_i) (u_i - Hb^T y_i)^T
+ * From the codec and n_buffered = N slots (0..W) it rebuilds
+ *     H = Gamma Hb + sum_{i<N} (E_{N-1,i} o k_i) m_i^T
  * (Gamma = diag exp(g_{N-1})), then requantizes it in place:
  *   1. m_i = max_j |H_ij|; the C rows with the largest m_i (ties: lower row)
  *      become compensator tokens, comp_idx ascending, comp_val = exact rows;
@@ -175,7 +179,8 @@ int lq_gdn_fp32_recurrence(const lq_dims *d, float *h, int32_t T,
  * B*H*(dk*dv + 4dk + 4dv + C*(4dv + 4)); 0 if d is NULL or invalid. */
 size_t lq_state_bytes(const lq_dims *d);
 
-/* Bytes of one layer's window buffer (buf_k, buf_y, buf_u, buf_g); 0 if invalid. */
+/* Bytes of one layer's window buffer (buf_k, buf_m, buf_g), i.e.
+ * B*H*W*4*(dk + dv + gd); 0 if invalid. */
 size_t lq_buffer_bytes(const lq_dims *d);
 
 /* Static description of a status code (never NULL). */

@@ -4,27 +4,37 @@
 // output is computed from the fixed low-bit state plus high-precision
 // buffered updates; the compensator tokens share the update path of real
 // tokens.  News article ("A linear-attention method cuts state ...",
-// paragraph 3): no update is skipped.  With the window-base state Hb and the
-// buffer (k_i, y_i, u_i, g_i), slot n's output is
-//     o = Hb^T q' + sum_{i<=n} a_i u_i,   q' = exp(g_n) o q - sum_{i<=n} a_i y_i,
-// and Hb^T q' = s o (sq^T (r o q')) + sum_c q'[idx_c] cv_c.
+// paragraph 3): no update is skipped.
 //
-// One workgroup per (b, h); at dk = dv = 128 it has 256 lanes and at most 64
-// VGPRs, so 8 workgroups share a CU and one dispatch covers B*H = 2048 heads
-// on 256 CUs.  Every load of the step is issued before the first barrier:
+// Buffer form.  With the window-base state Hb (fixed for the window) and the
+// window-local log-decays g, slot i of the buffer holds k_i, g_i and
+//     m_i = beta_i (v_i - Hb^T (e^{g_i} o k_i) - sum_{l<i} rr_{i,l} m_l),
+//     rr_{i,l} = <k_i, E_{i,l} o k_l>,  E_{i,l} = exp(g_i - g_l).
+// (m_i = u_i - Hb^T y_i for the WY factors y_i, u_i of the window's delta-rule
+// updates: projecting y_i through the fixed Hb once, when the slot is made,
+// leaves one dv-vector per slot instead of two.)  The output of slot n is
+//     o = Hb^T (e^{g_n} o q) + sum_{i<=n} a_i m_i,   a_i = <q, E_{n,i} o k_i>,
+// exactly H_n^T q for the state reached from Hb by the window's n+1 steps,
+// and Hb^T x = s o (sq^T (r o x)) + sum_c x[idx_c] cv_c.
+//
+// One workgroup per (b, h): dk channel lanes and dv value lanes (256 at
+// d = 128) with at most 64 VGPRs, so 8 workgroups share a CU and one dispatch
+// covers B*H = 2048 heads on 256 CUs.  Loads, all issued up front:
 //   * per-head vectors (q, k, v, row and column scales, per-key decay,
 //     compensator rows) and the buffered keys go straight to LDS
 //     (global_load_lds_dwordx4, no registers);
-//   * the int8 state goes to VGPRs as the A operands of int8 MFMAs: the state
-//     is stored value-column-major (sq[j][i]), so 16 consecutive key channels
-//     of one value column are one 16-byte load;
-//   * each channel lane holds its column of Y, each value lane its column of U.
+//   * each value lane loads its column of the buffered m_i;
+//   * the int8 state goes to VGPRs last, as the A operands of int8 MFMAs (it
+//     is stored value-column-major, sq[j][i]: 16 consecutive key channels of
+//     one value column are one 16-byte load); the first barrier waits for
+//     everything else, so phase A runs while it streams in.
 // Then:
-//   1. slot groups: rr_i = <k, E_i o k_i>, a_i = <q, E_i o k_i>
-//   2. channel lanes t < DK: y_n[t], q'[t], q''[t] = r[t] q'[t] and three int8
-//      digits of q'' per 64-channel block; value lanes: u_n[j], sum_i a_i u_i[j]
-//   3. int8 MFMA: sq^T x digits, recombined to fp32 (wave w owns its columns)
-//   4. value lanes: o[j] = s_j (sq^T q'')_j + compensators + buffer term.
+//   A. channel lanes: the int8 digits of r o e^g o q and r o e^g o k per
+//      64-channel block; all lanes, in slot groups: rr_i = <k, E_i o k_i>,
+//      a_i = <q, E_i o k_i>; slot n's key and log-decay are stored
+//   B. int8 MFMA: sq^T x digits for both vectors at once (wave w owns its
+//      column tiles); value lanes: sum_i rr_i m_i and sum_i a_i m_i
+//   C. value lanes: Hb^T q~, Hb^T k~ with the compensator rows, m_n and o.
 #include "lq_internal.h"
 
 #include <utility>
@@ -39,8 +49,7 @@ struct DecodeArgs {
     const int32_t* idx;
     const float* cv;
     float* bk;
-    float* by;
-    float* bu;
+    float* bm;
     float* bg;
     const float* q;
     const float* k;
@@ -98,10 +107,10 @@ void decode_kernel(DecodeArgs a) {
     __shared__ __align__(16) float s_vec[D::NSEG * DK];
     __shared__ __align__(16) float s_rr[WM];
     __shared__ __align__(16) float s_a[WM];
-    __shared__ __align__(16) float s_qp[DK];
-    __shared__ __align__(16) int8_t s_dig[3][KS * 64];
-    __shared__ __align__(16) float s_msc[KS];
-    __shared__ __align__(16) float s_gem[DV];
+    __shared__ __align__(16) float s_en[KDA ? DK : 1];       // e^{g_n} per key channel
+    __shared__ __align__(16) int8_t s_dig[6][KS * 64];       // digits of q~'' (0..2), k~'' (3..5)
+    __shared__ __align__(16) float s_msc[2][KS];
+    __shared__ __align__(16) float s_gem[2][DV];             // sq^T q~'', sq^T k~''
     // dwords 0..7: compensator rows; 8: beta; 9: alpha (scalar decay); 10: g_{n-1} (scalar decay)
     __shared__ __align__(16) int s_misc[16];
 
@@ -113,8 +122,7 @@ void decode_kernel(DecodeArgs a) {
     const int W = a.W, C = a.C;
 
     const float* __restrict__ bkr = a.bk + head * (size_t)W * DK;
-    const float* __restrict__ byr = a.by + head * (size_t)W * DK;
-    const float* __restrict__ bur = a.bu + head * (size_t)W * DV;
+    const float* __restrict__ bmr = a.bm + head * (size_t)W * DV;
     const float* __restrict__ bgr = a.bg + head * (size_t)W * GD;
 
     // ---- per-head vectors, compensator rows and buffered keys -> LDS ----------------------
@@ -173,22 +181,18 @@ void decode_kernel(DecodeArgs a) {
     const bool is_ch = t < DK;
     const bool is_val = t >= DK && t < DK + DV;
     const int j = t - DK;
-    float col[WM > 1 ? WM - 1 : 1];
-    if (is_ch) {
+    float mcol[WM > 1 ? WM - 1 : 1];              // value lane j: m_i[j], i < n
+    if (is_val) {
 #pragma unroll
         for (int i = 0; i < WM - 1; ++i)
-            if (i < n) col[i] = byr[(size_t)i * DK + t];
-    } else if (is_val) {
-#pragma unroll
-        for (int i = 0; i < WM - 1; ++i)
-            if (i < n) col[i] = bur[(size_t)i * DV + j];
+            if (i < n) mcol[i] = bmr[(size_t)i * DV + j];
     }
 
     // ---- int8 state -> VGPRs (MFMA A operands), issued last ---------------------------------
     // lane l of wave w: column j = tile*16 + l%16, channels ks*64 + 16*(l/16) .. +15.
     // Every tile and K step is real when the shape divides evenly; the loads are
     // then unconditional, and the first barrier waits for everything but these
-    // TPW*KS loads, which stream in while the buffer phases run.
+    // TPW*KS loads, which stream in while phase A runs.
     constexpr bool FULL = (NTILE % D::NW == 0) && (DK % 64 == 0);
     __builtin_amdgcn_sched_barrier(0);
     v4i sqa[TPW][KS];
@@ -206,7 +210,6 @@ void decode_kernel(DecodeArgs a) {
                     sqa[tw][ks] = v4i{0, 0, 0, 0};
             }
     }
-
     __builtin_amdgcn_sched_barrier(0);
     barrier_keep_loads<FULL ? TPW * KS : 0>();
 
@@ -214,7 +217,43 @@ void decode_kernel(DecodeArgs a) {
     float gn_s = 0.0f;
     if constexpr (!KDA) gn_s = (n > 0 ? __int_as_float(s_misc[10]) : 0.0f) + logf(__int_as_float(s_misc[9]));
 
-    // ---- 1. buffer inner products ---------------------------------------------------------
+    // ---- A. digits of r o e^g o q and r o e^g o k; slot n's key and decay; dot products ----
+    float xq = 0.0f, xk = 0.0f;                   // r o e^g o q, r o e^g o k (channel lanes)
+    if (is_ch) {
+        const float qc = s_vec[D::SQ * DK + t], kc = s_vec[D::SK * DK + t], rc = s_vec[D::SR * DK + t];
+        float gn;
+        if constexpr (KDA) gn = (n > 0 ? s_vec[D::SG * DK + t] : 0.0f) + logf(s_vec[D::SA * DK + t]);
+        else gn = gn_s;
+        const float en = __expf(gn);
+        xq = rc * (en * qc);
+        xk = rc * (en * kc);
+        a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = kc;
+        if constexpr (KDA) {
+            a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = gn;
+            s_en[t] = en;
+        } else if (t == 0) {
+            a.bg[head * (size_t)W + n] = gn;
+        }
+    }
+    if (w < KS) {
+        // wave w's 64 lanes are one 64-channel block (lanes past dk hold zeros):
+        // scale M = max |x|, three int8 digits per channel
+        const float mq = __uint_as_float(wave_umax(__float_as_uint(xq) & 0x7fffffffu));
+        const float mk = __uint_as_float(wave_umax(__float_as_uint(xk) & 0x7fffffffu));
+        uint32_t d0, d1, d2;
+        digits3_words(xq, mq > 0.0f ? 127.0f / mq : 0.0f, d0, d1, d2);
+        s_dig[0][t] = (int8_t)d0;
+        s_dig[1][t] = (int8_t)d1;
+        s_dig[2][t] = (int8_t)d2;
+        digits3_words(xk, mk > 0.0f ? 127.0f / mk : 0.0f, d0, d1, d2);
+        s_dig[3][t] = (int8_t)d0;
+        s_dig[4][t] = (int8_t)d1;
+        s_dig[5][t] = (int8_t)d2;
+        if (lane == 0) {
+            s_msc[0][w] = mq * (1.0f / 127.0f);
+            s_msc[1][w] = mk * (1.0f / 127.0f);
+        }
+    }
     {
         float kq[CH], kk[CH];
         load_floats<CH>(s_vec + D::SQ * DK + c0, kq);
@@ -262,65 +301,19 @@ void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
 
-    // ---- 2. WY append, transformed query and its int8 digits ---------------------------------
-    float wsum = 0.0f;
-    float q2 = 0.0f;
-    float st_y = 0.0f, st_k = 0.0f, st_g = 0.0f, st_u = 0.0f;   // slot n, stored after the GEMV
-    if (is_ch) {
-        const float qc = s_vec[D::SQ * DK + t], kc = s_vec[D::SK * DK + t];
-        float gn;
-        if constexpr (KDA) gn = (n > 0 ? s_vec[D::SG * DK + t] : 0.0f) + logf(s_vec[D::SA * DK + t]);
-        else gn = gn_s;
-        const float en = __expf(gn);
-        float ay = en * kc, aq = en * qc;
-#pragma unroll
-        for (int i = 0; i < WM - 1; ++i)
-            if (i < n) {
-                ay -= s_rr[i] * col[i];
-                aq -= s_a[i] * col[i];
-            }
-        const float yn = beta * ay;
-        const float qp = aq - s_a[n] * yn;
-        st_y = yn;
-        st_k = kc;
-        st_g = gn;
-        s_qp[t] = qp;
-        q2 = s_vec[D::SR * DK + t] * qp;
-    } else if (is_val) {
-        float au = s_vec[D::SV * DK + j];
-#pragma unroll
-        for (int i = 0; i < WM - 1; ++i)
-            if (i < n) {
-                au -= s_rr[i] * col[i];
-                wsum += s_a[i] * col[i];
-            }
-        const float un = beta * au;
-        wsum += s_a[n] * un;
-        st_u = un;
-    }
-    if (w < KS) {
-        // this wave's 64 channels form one block: scale M = max |q''|, digits of q''
-        const float m = group_max<64>(fabsf(q2));
-        const float inv = m > 0.0f ? 127.0f / m : 0.0f;
-        int d0, d1, d2;
-        digits3(q2, inv, d0, d1, d2);
-        s_dig[0][t] = (int8_t)d0;
-        s_dig[1][t] = (int8_t)d1;
-        s_dig[2][t] = (int8_t)d2;
-        if (lane == 0) s_msc[w] = m * (1.0f / 127.0f);
-    }
-    lds_barrier();
-
-    // ---- 3. int8 MFMA: (sq^T q'') for this wave's column tiles --------------------------------
+    // ---- B. int8 MFMA: sq^T of both digit sets for this wave's column tiles; buffer sums -----
     {
-        const int dgt = lane % 16;                    // B column = digit index (0..2), rest zero
-        const float wd = dgt == 0 ? 1.0f : dgt == 1 ? kDigitW1 : dgt == 2 ? kDigitW2 : 0.0f;
+        // B columns 0..2: digits of q~'', 3..5: digits of k~'', rest zero
+        const int dgt = lane % 16;
+        const int vec = dgt >= 3 ? 1 : 0;
+        const int dd = dgt - 3 * vec;
+        const float wd = dgt >= 6 ? 0.0f : dd == 0 ? 1.0f : dd == 1 ? kDigitW1 : kDigitW2;
         float fk[KS];
         v4i bop[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            fk[ks] = wd * s_msc[ks];
-            bop[ks] = dgt < 3 ? *reinterpret_cast<const v4i*>(&s_dig[dgt][ks * 64 + 16 * (lane / 16)])
+            fk[ks] = wd * s_msc[vec][ks];
+            bop[ks] = dgt < 6 ? *reinterpret_cast<const v4i*>(&s_dig[dgt][ks * 64 + 16 * (lane / 16)])
                               : v4i{0, 0, 0, 0};
         }
 #pragma unroll
@@ -330,38 +323,47 @@ void decode_kernel(DecodeArgs a) {
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const v4i dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(sqa[tw][ks], bop[ks],
-                                                                     v4i{0, 0, 0, 0}, 0, 0, 0);
+                const v4i dv4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(sqa[tw][ks], bop[ks],
+                                                                      v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] += (float)dd[v] * fk[ks];
+                for (int v = 0; v < 4; ++v) acc[v] += (float)dv4[v] * fk[ks];
             }
-            // the digit-0 lane gathers digits 1 and 2 from the next two lanes
+            // the digit-0 lanes of each vector (0 and 3) gather digits 1 and 2
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] += dpp<DPP_SHL1>(acc[v]) + dpp<DPP_SHL2>(acc[v]);
-            if (dgt == 0)
-                *reinterpret_cast<float4*>(&s_gem[tile * 16 + 4 * (lane / 16)]) =
+            if (dd == 0 && dgt < 6)
+                *reinterpret_cast<float4*>(&s_gem[vec][tile * 16 + 4 * (lane / 16)]) =
                     make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
+    float sr = 0.0f, sa = 0.0f;
+    if (is_val) {
+#pragma unroll
+        for (int i = 0; i < WM - 1; ++i)
+            if (i < n) {
+                sr += s_rr[i] * mcol[i];
+                sa += s_a[i] * mcol[i];
+            }
+    }
     lds_barrier();
 
-    // ---- 4. slot n and the output ------------------------------------------------------------
-    // (the slot stores come after the GEMV so its wait for the state loads does
-    // not also wait for them)
-    if (is_ch) {
-        a.by[head * (size_t)W * DK + (size_t)n * DK + t] = st_y;
-        a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = st_k;
-        if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = st_g;
-        else if (t == 0) a.bg[head * (size_t)W + n] = st_g;
-    } else if (is_val) {
-        a.bu[head * (size_t)W * DV + (size_t)n * DV + j] = st_u;
-    }
+    // ---- C. m_n and the output ------------------------------------------------------------------
     if (is_val) {
-        float out = s_vec[D::SS * DK + j] * s_gem[j] + wsum;
+        const float sj = s_vec[D::SS * DK + j];
+        const float eg = KDA ? 0.0f : __expf(gn_s);
+        float hq = sj * s_gem[0][j], hk = sj * s_gem[1][j];
 #pragma unroll
         for (int c = 0; c < CMAX; ++c)
-            if (c < C) out += s_qp[s_misc[c]] * s_vec[(D::SCV + c) * DK + j];
-        a.o[head * DV + j] = out;
+            if (c < C) {
+                const int ic = s_misc[c] & (DK - 1);
+                const float e = KDA ? s_en[ic] : eg;
+                const float cvj = s_vec[(D::SCV + c) * DK + j];
+                hq += (e * s_vec[D::SQ * DK + ic]) * cvj;
+                hk += (e * s_vec[D::SK * DK + ic]) * cvj;
+            }
+        const float mn = beta * (s_vec[D::SV * DK + j] - hk - sr);
+        a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
+        a.o[head * DV + j] = hq + sa + s_a[n] * mn;
     }
 }
 
@@ -403,7 +405,7 @@ hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const fl
                          const float* k, const float* v, const float* alpha, const float* beta,
                          float* o, hipStream_t s) {
     DecodeArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
-                    st.buf_k, st.buf_y, st.buf_u, st.buf_g,
+                    st.buf_k, st.buf_m, st.buf_g,
                     q, k, v, alpha, beta, o, d.W, d.C, pos};
     switch (d.dk) {
         case 16: return launch_dk<16>(d, args, s);

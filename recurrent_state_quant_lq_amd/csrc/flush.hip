@@ -8,17 +8,13 @@
 // high-precision compensator tokens and the residual is smoothed before
 // quantization.
 //
-// Reconstruction from the window-base state Hb and N buffered slots:
-//     M = U - Y Hb                     (N x dv,   contraction over dk)
+// Reconstruction from the window-base state Hb and N buffered slots
+// (k_i, g_i, m_i; m_i = u_i - Hb^T y_i, see decode.hip):
 //     H = Gamma Hb + Kt^T M            (dk x dv,  contraction over N)
-// with Kt[i][c] = exp(g_{N-1}[c] - g_i[c]) k_i[c] and Gamma = diag exp(g_{N-1}).
-//   * Y Hb = ((Y o r) sq) o s + Y[:, idx] cv: the int8 state is the B operand
-//     of v_mfma_i32_16x16x64_i8 as stored (value-column-major sq[j][i]: 16
-//     consecutive key channels of a column are one load) and Y o r enters as
-//     three int8 digits per slot (exact int32 sums, recombined in fp32).  The
-//     compensator term is one fp32 MFMA per tile whose K dimension runs over
-//     the compensator rows.  Each wave owns whole column tiles.
-//   * Kt^T M is dense fp32 on v_mfma_f32_16x16x4_f32.
+// with Kt[i][c] = exp(g_{N-1}[c] - g_i[c]) k_i[c], M = [m_0; ...; m_{N-1}] and
+// Gamma = diag exp(g_{N-1}).  Gamma Hb is dequantized into the accumulators
+// of v_mfma_f32_16x16x4_f32; the compensator rows Gamma P^T cv are one more
+// fp32 MFMA K step whose K dimension runs over the compensator rows.
 //
 // Register layout ("D layout") of H in one workgroup: NW waves; lane l
 // (li = l % 16, lg = l / 16) of wave w holds, for v4 register (rb, ct),
@@ -302,8 +298,7 @@ struct FlushArgs {
     int32_t* idx;
     float* cv;
     const float* bk;
-    const float* by;
-    const float* bu;
+    const float* bm;
     const float* bg;
     float* h_out;
     int W;
@@ -329,22 +324,17 @@ __device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst,
     }
 }
 
-// Workgroup LDS of the flush kernel (byte offsets; the codec area reuses the
-// Y and digit blocks, dead once the first contraction is done).
+// Workgroup LDS of the flush kernel (byte offsets).
 template <int DK, int DV, int NPAD, bool KDA>
 struct FlushLds {
-    static constexpr int KS = (DK + 63) / 64;
     static constexpr int RS = 0;                                   // r | s | cv rows
     static constexpr int MISC = RS + (2 + CMAX) * DK * 4;          // idx
     static constexpr int GS = MISC + 64;                           // scalar log-decays
-    static constexpr int UM = GS + 4 * 32;                         // U, then M
-    static constexpr int KB = UM + NPAD * DV * 4;                  // keys
+    static constexpr int MB = GS + 4 * 32;                         // buffered m rows
+    static constexpr int KB = MB + NPAD * DV * 4;                  // buffered keys
     static constexpr int GB = KB + NPAD * DK * 4;                  // per-key log-decays
-    static constexpr int YB = GB + (KDA ? NPAD * DK * 4 : 0);      // Y, then codec
-    static constexpr int DA = YB + NPAD * DK * 4;                  // digits
-    static constexpr int YSC = DA + 3 * NPAD * KS * 64;
-    static constexpr int BYTES = YSC + NPAD * 4;
-    static_assert(sizeof(CodecLds<DK, DV, 4>) <= YSC - YB, "codec area");
+    static constexpr int CODEC = GB + (KDA ? NPAD * DK * 4 : 0);   // codec stage
+    static constexpr int BYTES = CODEC + (int)sizeof(CodecLds<DK, DV, (DK / 16 < 4 ? DK / 16 : 4)>);
 };
 
 template <int DK, int DV, int WM, bool KDA>
@@ -352,15 +342,11 @@ __global__ __launch_bounds__((FS<DK, DV>::NT))
 __attribute__((amdgpu_waves_per_eu(WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2), WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2))))
 void flush_kernel(FlushArgs a) {
     using S = FS<DK, DV>;
-    constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, NT = S::NT, RPL = S::RPL;
-    constexpr int TPW = S::TPW, KS = S::KS;
+    constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, RPL = S::RPL;
     constexpr int NPAD = WM <= 16 ? 16 : 32;   // slots padded to the MFMA size
-    constexpr int MB = NPAD / 16;
-    constexpr int LPS = NT / NPAD;             // lanes per slot in the digit stage
-    constexpr int CHD = DK / LPS;              // channels per lane in the digit stage
-    static_assert(NT % NPAD == 0 && DK % LPS == 0 && CHD % 4 == 0, "digit tiling");
     using RBy = RowBytes<RPL>;
     using LY = FlushLds<DK, DV, NPAD, KDA>;
+    constexpr int KC = CMAX / 4;
 
     __shared__ __align__(16) char smem[LY::BYTES];
     float* s_r = reinterpret_cast<float*>(smem + LY::RS);
@@ -368,13 +354,10 @@ void flush_kernel(FlushArgs a) {
     float* s_cv = s_r + 2 * DK;                                    // [CMAX][DV]
     int* s_idx = reinterpret_cast<int*>(smem + LY::MISC);
     float* s_gs = reinterpret_cast<float*>(smem + LY::GS);         // [NPAD] (scalar decay)
-    float* s_UM = reinterpret_cast<float*>(smem + LY::UM);         // [NPAD][DV]
+    float* s_M = reinterpret_cast<float*>(smem + LY::MB);          // [NPAD][DV]
     float* s_K = reinterpret_cast<float*>(smem + LY::KB);          // [NPAD][DK]
     float* s_G = reinterpret_cast<float*>(smem + LY::GB);          // [NPAD][DK] (per-key decay)
-    float* s_Y = reinterpret_cast<float*>(smem + LY::YB);          // [NPAD][DK]
-    int8_t* s_dA = reinterpret_cast<int8_t*>(smem + LY::DA);       // [3][NPAD][KS*64]
-    float* s_ysc = reinterpret_cast<float*>(smem + LY::YSC);       // [NPAD]
-    auto& L = *reinterpret_cast<CodecLds<DK, DV, NW>*>(smem + LY::YB);
+    auto& L = *reinterpret_cast<CodecLds<DK, DV, NW>*>(smem + LY::CODEC);
 
     const int t = threadIdx.x;
     const int lane = t & 63, li = lane & 15, lg = lane >> 4;
@@ -384,8 +367,8 @@ void flush_kernel(FlushArgs a) {
 
     const int8_t* sq = a.sq + head * (DK * DV);
 
-    // ---- loads (all unconditional; buffer rows clamped to W-1, slots >= N
-    //      masked after the barrier) -----------------------------------------------------------------
+    // ---- loads (unconditional; buffer rows clamped to W-1, slots >= N masked
+    //      after the barrier) ------------------------------------------------------------------------
     {
         // r, s, compensator rows (DK/4 lanes per vector of 16-byte pieces)
         constexpr int SEGL = DK / 4, SPI = 64 / SEGL;
@@ -405,25 +388,10 @@ void flush_kernel(FlushArgs a) {
         }
         if (w == 0 && lane < C) lds_dma4(a.idx + head * C + lane, s_idx);
         if (!KDA && w == NW - 1 && lane < NPAD) lds_dma4(a.bg + head * W + min(lane, W - 1), s_gs);
-        dma_rows<NPAD, DV, NW>(a.bu + head * (size_t)W * DV, W - 1, s_UM, w, lane);
+        dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, W - 1, s_M, w, lane);
         dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane);
-        dma_rows<NPAD, DK, NW>(a.by + head * (size_t)W * DK, W - 1, s_Y, w, lane);
         if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, W - 1, s_G, w, lane);
     }
-    // contraction-1 B operands: column j = tile*16 + li, channels ks*64 + 16*lg .. +15
-    v4i bq[TPW][KS];
-    constexpr bool FULL = (CT % NW == 0) && (DK % 64 == 0);
-#pragma unroll
-    for (int tw = 0; tw < TPW; ++tw)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int tile = w * TPW + tw;
-            const int i0 = ks * 64 + 16 * lg;
-            if (FULL || (tile < CT && i0 < DK))
-                bq[tw][ks] = *reinterpret_cast<const v4i*>(sq + (size_t)(tile * 16 + li) * DK + i0);
-            else
-                bq[tw][ks] = v4i{0, 0, 0, 0};
-        }
     // D-layout bytes of the base state: column li*CT + ct, this lane's RPL rows
     const int row0 = row_of<DK, DV>(w, lg, 0, 0);
     typename RBy::T hb[CT];
@@ -432,109 +400,8 @@ void flush_kernel(FlushArgs a) {
         hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + (size_t)(li * CT + ct) * DK + row0);
     all_loads_barrier();
 
-    // ---- digits of (Y o r), per slot; compensator operands ----------------------------------------
-    {
-        const int dslot = t / LPS, dc0 = (t % LPS) * CHD;
-        float yv[CHD], rv[CHD];
-        load_floats<CHD>(s_Y + dslot * DK + dc0, yv);
-        load_floats<CHD>(s_r + dc0, rv);
-        const bool live = dslot < N;
-        float mx = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CHD; ++c) {
-            yv[c] = live ? yv[c] * rv[c] : 0.0f;
-            mx = fmaxf(mx, fabsf(yv[c]));
-        }
-        mx = group_absmax<LPS>(mx);
-        const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
-        uint32_t dg[3][CHD];
-#pragma unroll
-        for (int c = 0; c < CHD; ++c) digits3_words(yv[c], inv, dg[0][c], dg[1][c], dg[2][c]);
-#pragma unroll
-        for (int d = 0; d < 3; ++d)
-#pragma unroll
-            for (int c = 0; c < CHD; c += 4)
-                *reinterpret_cast<uint32_t*>(&s_dA[(d * NPAD + dslot) * (KS * 64) + dc0 + c]) =
-                    pack_low4(dg[d][c], dg[d][c + 1], dg[d][c + 2], dg[d][c + 3]);
-        if (t % LPS == 0) s_ysc[dslot] = mx * (1.0f / 127.0f);
-        // channels past DK in the last K step stay zero
-        if constexpr (KS * 64 > DK) {
-            constexpr int PADC = KS * 64 - DK;
-            for (int e = t; e < 3 * NPAD * PADC; e += NT)
-                s_dA[(e / PADC) * (KS * 64) + DK + e % PADC] = 0;
-        }
-    }
-    // compensator A operands Y[slot][idx_c] (slot = mb*16 + li, c = 4*kc + lg)
-    constexpr int KC = CMAX / 4;
-    float ya[MB][KC];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        const int c = 4 * kc + lg;
-        const int ic = c < C ? s_idx[c] & (DK - 1) : 0;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int slot = mb * 16 + li;
-            ya[mb][kc] = (c < C && slot < N) ? s_Y[slot * DK + ic] : 0.0f;
-        }
-    }
-    lds_barrier();
-
-    // ---- M = U - Y Hb for this wave's column tiles ----------------------------------------------------
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        v4i acc[3][TPW];
-        v4f cc[TPW];
-#pragma unroll
-        for (int tw = 0; tw < TPW; ++tw) {
-            const int tile = min(w * TPW + tw, CT - 1);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int slot = mb * 16 + 4 * lg + v;
-                cc[tw][v] = slot < N ? -s_UM[slot * DV + tile * 16 + li] : 0.0f;
-            }
-#pragma unroll
-            for (int d = 0; d < 3; ++d) acc[d][tw] = v4i{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int d = 0; d < 3; ++d) {
-                const v4i aop =
-                    *reinterpret_cast<const v4i*>(&s_dA[(d * NPAD + mb * 16 + li) * (KS * 64) + ks * 64 + 16 * lg]);
-#pragma unroll
-                for (int tw = 0; tw < TPW; ++tw)
-                    acc[d][tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bq[tw][ks], acc[d][tw], 0, 0, 0);
-            }
-        // cc = Y[:, idx] cv - U
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-            if (4 * kc < C) {
-                const int c = 4 * kc + lg;
-#pragma unroll
-                for (int tw = 0; tw < TPW; ++tw) {
-                    const int tile = min(w * TPW + tw, CT - 1);
-                    const float b = c < C ? s_cv[c * DV + tile * 16 + li] : 0.0f;
-                    cc[tw] = __builtin_amdgcn_mfma_f32_16x16x4f32(ya[mb][kc], b, cc[tw], 0, 0, 0);
-                }
-            }
-#pragma unroll
-        for (int tw = 0; tw < TPW; ++tw) {
-            const int tile = w * TPW + tw;
-            if (tile >= CT) break;
-            const int jj = tile * 16 + li;
-            const float sj = s_s[jj];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int slot = mb * 16 + 4 * lg + v;
-                const float yq = s_ysc[slot] * ((float)acc[0][tw][v] + (float)acc[1][tw][v] * kDigitW1 +
-                                                (float)acc[2][tw][v] * kDigitW2);
-                s_UM[slot * DV + jj] = -(sj * yq + cc[tw][v]);
-            }
-        }
-    }
-
     // ---- H = Gamma Hb + Kt^T M (fp32 MFMA, accumulating in place) -------------------------------
-    // contraction-2 A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg
+    // A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg (0 past N)
     float ka[RBW][NPAD / 4];
     if constexpr (KDA) {
 #pragma unroll
@@ -605,12 +472,16 @@ void flush_kernel(FlushArgs a) {
                     H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bcv[ct], H[rb][ct], 0, 0, 0);
             }
         }
-    lds_barrier();   // M complete
+    // window terms: B = M rows (rows past N are zero; the buffer may hold
+    // anything there)
 #pragma unroll
     for (int ks = 0; ks < NPAD / 4; ++ks) {
         if (4 * ks < N) {
+            const bool live = 4 * ks + lg < N;
             float bm[CT];
-            load_floats<CT>(&s_UM[(4 * ks + lg) * DV + li * CT], bm);
+            load_floats<CT>(&s_M[(4 * ks + lg) * DV + li * CT], bm);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) bm[ct] = live ? bm[ct] : 0.0f;
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -712,7 +583,7 @@ hipError_t flush_dk(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
 hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, float* h_out,
                         hipStream_t s) {
     FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
-                   st.buf_k, st.buf_y, st.buf_u, st.buf_g, h_out, d.W, d.C, n_buffered, d.smooth};
+                   st.buf_k, st.buf_m, st.buf_g, h_out, d.W, d.C, n_buffered, d.smooth};
     switch (d.dk) {
         case 16: return flush_dk<16>(d, args, s);
         case 64: return flush_dk<64>(d, args, s);

@@ -48,7 +48,7 @@ int check_state(const lq_dims* d, const lq_state* st, bool with_buffer) {
         if (!aligned16(p)) return LQ_ERR_ALIGN;
     if (d->C > 0 && (!aligned16(st->comp_idx) || !aligned16(st->comp_val))) return LQ_ERR_ALIGN;
     if (with_buffer) {
-        const void* buf[] = {st->buf_k, st->buf_y, st->buf_u, st->buf_g};
+        const void* buf[] = {st->buf_k, st->buf_m, st->buf_g};
         for (const void* p : buf)
             if (!p) return LQ_ERR_NULL;
         for (const void* p : buf)
@@ -204,7 +204,7 @@ size_t lq_buffer_bytes(const lq_dims* d) {
     if (check_dims(d) != LQ_OK) return 0;
     const size_t heads = (size_t)d->B * d->H;
     const size_t gd = d->decay_mode == LQ_DECAY_PER_KEY ? d->dk : 1;
-    return heads * (size_t)d->W * 4 * (2 * (size_t)d->dk + d->dv + gd);
+    return heads * (size_t)d->W * 4 * ((size_t)d->dk + d->dv + gd);
 }
 
 const char* lq_status_str(int status) {

@@ -37,7 +37,7 @@ class lq_dims(ct.Structure):
 
 class lq_state(ct.Structure):
     _fields_ = [(n, ct.c_void_p) for n in ("sq", "row_scale", "col_scale", "comp_idx", "comp_val",
-                                           "buf_k", "buf_y", "buf_u", "buf_g")]
+                                           "buf_k", "buf_m", "buf_g")]
 
 
 class LQError(RuntimeError):
@@ -129,8 +129,7 @@ class LayerState:
     comp_idx: torch.Tensor
     comp_val: torch.Tensor
     buf_k: torch.Tensor
-    buf_y: torch.Tensor
-    buf_u: torch.Tensor
+    buf_m: torch.Tensor
     buf_g: torch.Tensor
 
     @staticmethod
@@ -141,8 +140,8 @@ class LayerState:
         return LayerState(d, z((B, H, dv, dk), torch.int8), z((B, H, dk), torch.float32),
                           z((B, H, dv), torch.float32), z((B, H, max(C, 1)), torch.int32),
                           z((B, H, max(C, 1), dv), torch.float32),
-                          z((B, H, W, dk), torch.float32), z((B, H, W, dk), torch.float32),
-                          z((B, H, W, dv), torch.float32), z((B, H, W, gd), torch.float32))
+                          z((B, H, W, dk), torch.float32), z((B, H, W, dv), torch.float32),
+                          z((B, H, W, gd), torch.float32))
 
     def check(self, with_buffer=True):
         d = self.dims
@@ -155,14 +154,13 @@ class LayerState:
         _check(self.comp_val, "comp_val", (B, H, max(C, 1), dv), torch.float32)
         if with_buffer:
             _check(self.buf_k, "buf_k", (B, H, W, dk), torch.float32)
-            _check(self.buf_y, "buf_y", (B, H, W, dk), torch.float32)
-            _check(self.buf_u, "buf_u", (B, H, W, dv), torch.float32)
+            _check(self.buf_m, "buf_m", (B, H, W, dv), torch.float32)
             _check(self.buf_g, "buf_g", (B, H, W, gd), torch.float32)
 
     def c_state(self) -> lq_state:
         return lq_state(*[_ptr(getattr(self, n)) for n in
                           ("sq", "row_scale", "col_scale", "comp_idx", "comp_val",
-                           "buf_k", "buf_y", "buf_u", "buf_g")])
+                           "buf_k", "buf_m", "buf_g")])
 
     def codec(self) -> dict:
         """Host copies of the codec arrays, int8 matrix row-major [B,H,dk,dv]

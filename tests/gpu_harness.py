@@ -5,7 +5,8 @@ Per window both sides start from the ORACLE's codec bytes.  The HIP path runs
 the window's decode steps and the flush; then, for each sampled head:
   * o_t (every step) against the oracle's window outputs, norm-wise:
     max_j |do_j| / max_j |o_j| <= O_TOL;
-  * the WY buffer the kernels wrote against the oracle's buffer;
+  * the buffer the kernels wrote (k_i, g_i, m_i = u_i - Hb^T y_i) against the
+    same rows formed from the oracle's WY buffer;
   * the fp32 state the flush handed to its rounding step (h_out) against the
     oracle's fp64 state;
   * the flush's codec bytes against the oracle's codec OF THAT SAME fp32
@@ -55,6 +56,14 @@ def codec_equal(gpu: dict, orc: dict) -> bool:
         if g.shape != o.shape or g.tobytes() != o.tobytes():
             return False
     return True
+
+
+def oracle_buffer(cd: dict, buf: dict, N: int) -> dict:
+    """The library's buffer rows from the oracle's WY buffer of one window:
+    keys, log-decays and m_i = u_i - Hb^T y_i (Hb: the window-base state the
+    codec stands for), all fp64."""
+    Hb = O.dequantize(cd)
+    return dict(k=buf["k"][:N], g=buf["g"][:N], m=buf["u"][:N] - buf["y"][:N] @ Hb)
 
 
 def upload_head_codec(st: lq.LayerState, b: int, h: int, cd: dict):
@@ -169,7 +178,7 @@ def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smoot
             lq.lq_gdn_decode_step(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
                                   tk["beta"][n], o)
             outs[n].copy_(o)
-        bufs = ({k: getattr(st, "buf_" + k).clone() for k in ("k", "y", "u", "g")}
+        bufs = ({k: getattr(st, "buf_" + k).clone() for k in ("k", "m", "g")}
                 if check_buffers else None)
         lq.lq_gdn_window_flush(st, N, h_out)
         torch.cuda.synchronize()
@@ -180,9 +189,10 @@ def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smoot
             hg = h_out[b, h].cpu().numpy()
             rep.h_err = max(rep.h_err, float(np.abs(hg - res["H"]).max() / max(np.abs(res["H"]).max(), 1e-30)))
             if check_buffers:
-                for key in ("k", "y", "u", "g"):
+                ob = oracle_buffer(codec[(b, h)], res["buf"], N)
+                for key in ("k", "m", "g"):
                     g = bufs[key][b, h, :N].cpu().numpy()
-                    rep.buf_err = max(rep.buf_err, rel_err(g, res["buf"][key][:N]))
+                    rep.buf_err = max(rep.buf_err, rel_err(g, ob[key]))
             gc = head_codec(st, b, h)
             if not codec_equal(gc, O.quantize(hg, d.C, d.smooth)):
                 rep.bytes_exact = False

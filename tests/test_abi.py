@@ -43,9 +43,10 @@ def test_sizes():
     L = lq.load()
     d = _dims()
     assert L.lq_state_bytes(ct.byref(d)) == 6 * 19472
-    assert L.lq_buffer_bytes(ct.byref(d)) == 6 * 16 * 4 * (128 + 128 + 128 + 1)
+    # per slot: k (dk) + m (dv) + one log-decay (scalar) or dk of them (per key)
+    assert L.lq_buffer_bytes(ct.byref(d)) == 6 * 16 * 4 * (128 + 128 + 1)
     dk = _dims(decay_mode=1)
-    assert L.lq_buffer_bytes(ct.byref(dk)) == 6 * 16 * 4 * (4 * 128)
+    assert L.lq_buffer_bytes(ct.byref(dk)) == 6 * 16 * 4 * (3 * 128)
     assert L.lq_state_bytes(None) == 0
     assert L.lq_state_bytes(ct.byref(_dims(dk=0))) == 0
 
@@ -64,7 +65,7 @@ def test_check_dims(kw, status):
 
 
 def _fake_state(C=4, misalign=None, null=None):
-    names = ("sq", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_k", "buf_y", "buf_u", "buf_g")
+    names = ("sq", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_k", "buf_m", "buf_g")
     vals = []
     for i, n in enumerate(names):
         p = 0x100000 * (i + 1)
@@ -93,7 +94,7 @@ def test_decode_argument_errors():
     assert call(ct.byref(d), ct.byref(st), -1, *args) == lq.LQ_ERR_POS
     assert call(ct.byref(d), ct.byref(st), 0, A, A, None, A, A, A) == lq.LQ_ERR_NULL
     assert call(ct.byref(d), ct.byref(st), 0, A, B4, A, A, A, A) == lq.LQ_ERR_ALIGN
-    for n in ("sq", "buf_y", "comp_val"):
+    for n in ("sq", "buf_m", "comp_val"):
         assert call(ct.byref(d), ct.byref(_fake_state(null=n)), 0, *args) == lq.LQ_ERR_NULL
         assert call(ct.byref(d), ct.byref(_fake_state(misalign=n)), 0, *args) == lq.LQ_ERR_ALIGN
     # beta and the scalar-mode alpha need only 4-byte alignment

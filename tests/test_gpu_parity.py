@@ -206,8 +206,7 @@ def test_canaries_and_untouched_slots():
     spec = dict(sq=((B, H, dk, dk), torch.int8), row_scale=((B, H, dk), torch.float32),
                 col_scale=((B, H, dk), torch.float32), comp_idx=((B, H, C), torch.int32),
                 comp_val=((B, H, C, dk), torch.float32), buf_k=((B, H, W, dk), torch.float32),
-                buf_y=((B, H, W, dk), torch.float32), buf_u=((B, H, W, dk), torch.float32),
-                buf_g=((B, H, W, dk), torch.float32))
+                buf_m=((B, H, W, dk), torch.float32), buf_g=((B, H, W, dk), torch.float32))
     for name, (shape, dt) in spec.items():
         arrays[name] = _guarded(shape, dt, 7)
     st = lq.LayerState(d, *[arrays[n][1] for n in spec])
@@ -220,10 +219,10 @@ def test_canaries_and_untouched_slots():
     ob, o = _guarded((B, H, dk), torch.float32, 7)
     hb, hout = _guarded((B, H, dk, dk), torch.float32, 7)
     for n in range(6):
-        before = {k: getattr(st, "buf_" + k).clone() for k in ("k", "y", "u", "g")}
+        before = {k: getattr(st, "buf_" + k).clone() for k in ("k", "m", "g")}
         lq.lq_gdn_decode_step(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o)
         torch.cuda.synchronize()
-        for k in ("k", "y", "u", "g"):
+        for k in ("k", "m", "g"):
             after = getattr(st, "buf_" + k)
             keep = [i for i in range(W) if i != n]
             assert torch.equal(after[:, :, keep], before[k][:, :, keep]), (k, n)

@@ -180,3 +180,38 @@ def test_windowing_beats_per_token_quantization(orc):
 
     naive, leap = err(1, 0, 0), err(16, 4, 1)
     assert leap < 0.5 * naive
+
+
+def test_projected_buffer_form(orc):
+    """The buffer form the kernels keep, checked on the oracle's WY buffer:
+    with m_i = u_i - Hb^T y_i,
+        m_n = beta_n (v_n - Hb^T (e^{g_n} o k_n) - sum_{i<n} rr_{n,i} m_i),
+        o_n = Hb^T (e^{g_n} o q_n) + sum_{i<=n} a_{n,i} m_i,
+    rr_{n,i} = <k_n, E_{n,i} o k_i>, a_{n,i} = <q_n, E_{n,i} o k_i>, in fp64,
+    for scalar and per-key decay."""
+    import numpy as np
+    from recurrent_state_quant_lq_amd import inputs
+    for per_key in (False, True):
+        dk = dv = 16
+        W, C = 6, 2
+        tok = inputs.host_tokens(77, W, 1, 1, dk, dv, per_key=per_key, beta_lo=0.1, beta_hi=0.9)
+        tok = orc.head_tokens(tok, 0, 0)
+        rng = np.random.default_rng(5)
+        cd = orc.quantize((rng.standard_normal((dk, dv)) * 0.3).astype(np.float32), C, 1)
+        res = orc.window(cd, tok, per_key, W, C, 1)
+        Hb = orc.dequantize(cd)
+        b = res["buf"]
+        m = b["u"] - b["y"] @ Hb
+        for n in range(W):
+            g = b["g"][n]
+            E = np.exp(g[None, :] - b["g"][:n + 1]) if per_key else np.exp(g - b["g"][:n + 1])
+            kt = E * b["k"][:n + 1]                                   # E_{n,i} o k_i
+            k = tok["k"][n].astype(np.float64)
+            q = tok["q"][n].astype(np.float64)
+            rr = kt[:n] @ k
+            a = kt @ q
+            eg = np.exp(g)
+            want_m = float(tok["beta"][n]) * (tok["v"][n] - Hb.T @ (eg * k) - rr @ m[:n])
+            np.testing.assert_allclose(m[n], want_m, rtol=0, atol=1e-12 * max(1.0, np.abs(m).max()))
+            o = Hb.T @ (eg * q) + a @ m[:n + 1]
+            np.testing.assert_allclose(o, res["o"][n], rtol=0, atol=1e-12 * max(1.0, np.abs(o).max()))
