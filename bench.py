@@ -15,12 +15,16 @@ quantized by its quantizer.
 Printed (one JSON line): tokens/s through one layer (B * W * L tokens per
 step), the decode kernel's roofline (algorithmic bytes over its per-launch
 duration: the kernel's own execution interval, from the library's timing hook
-of start/stop HIP events on the launch stream), the flush's, and the CPU
-oracle timed on a bounded sample of the same workload.
+of start/stop HIP events on the launch stream), the flush's, the CPU oracle
+timed on a bounded sample of the same workload, and (`comparisons`) the same
+workload through a dense fp32-state decode step and through per-token int8
+requantization, with the output error of both int8 schemes against the fp32
+recurrence on a sample of heads.
 
 Profile summaries (text under profiles/) from rocprofv3 output:
     python bench.py --trace-summary OUT.md  STATS.csv  -- "<command that made it>"
     python bench.py --pmc-summary   OUT.md  FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR -- "<commands>"
+    python bench.py --counter-summary OUT.md DIR [DIR ...] -- "<commands>"
 """
 from __future__ import annotations
 
@@ -194,6 +198,155 @@ def pmc_summary(out_md: str, fetch_dir: str, write_dir: str, cal_fetch: str, cal
     print(json.dumps(rec))
 
 
+def counter_summary(out_md: str, dirs, command: str):
+    """Per-dispatch means of every SQ counter rocprofv3 --pmc collected, for
+    the decode and flush kernels, also divided by SQ_WAVES (per wave)."""
+    import glob
+    import collections
+    acc = collections.defaultdict(list)
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in _csv_rows(f):
+                nm = r["Kernel_Name"]
+                fam = "decode" if "decode_kernel" in nm else "flush" if "flush_kernel" in nm else None
+                if fam:
+                    acc[(fam, r["Counter_Name"])].append(float(r["Counter_Value"]))
+    fams = sorted({f for f, _ in acc})
+    ctrs = sorted({c for _, c in acc})
+    lines = [f"# SQ counters: {os.path.basename(out_md)[:-3]}", "",
+             "Commands (from the repository root; one counter set per run):", "", "```", command, "```", "",
+             "Means per dispatch over all dispatches of each kernel family; per wave = / SQ_WAVES. "
+             "SQ_*_CYCLES counters count in units of 4 cycles on this GPU.", "",
+             "| counter | " + " | ".join(f"{f} / dispatch | {f} / wave" for f in fams) + " |",
+             "|---|" + "---:|---:|" * len(fams)]
+    rec = {}
+    for c in ctrs:
+        row = [c]
+        for f in fams:
+            v = acc.get((f, c))
+            waves = acc.get((f, "SQ_WAVES"))
+            if not v:
+                row += ["", ""]
+                continue
+            m = sum(v) / len(v)
+            pw = m / (sum(waves) / len(waves)) if waves else float("nan")
+            row += [f"{m:.0f}", f"{pw:.1f}"]
+            rec[f"{f}:{c}:per_wave"] = round(pw, 2)
+        lines.append("| " + " | ".join(row) + " |")
+    lines += ["", json.dumps(rec), ""]
+    open(out_md, "w").write("\n".join(lines))
+    print(json.dumps(rec))
+
+
+def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
+    """The same workload through (1) a dense fp32-state decode step (the
+    library's fp32 recurrence, one token per launch: reads and writes the
+    64 KB fp32 state of every head) and (2) per-token int8 requantization
+    (W = 1, no compensators, no smoothing), plus the output error of both int8
+    schemes against the fp32 recurrence on a sample of heads."""
+    import torch
+    from recurrent_state_quant_lq_amd import lq
+    W = wl.W
+    B, H, dk, dv = wl.B, wl.H, wl.dk, wl.dv
+    o = torch.empty((B, H, dv), dtype=torch.float32, device=h0.device)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(run, n_tokens):
+        run()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(steps):
+            run()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        return n_tokens / (ms * 1e-3), ms
+
+    def kernel_us(run, fam):
+        lq.lq_timing_enable(True)
+        run()
+        lq.lq_timing_enable(False)
+        f, t = lq.lq_timing_collect()
+        sel = [x for ff, x in zip(f, t) if ff == fam]
+        return 1e3 * sum(sel) / max(1, len(sel))
+
+    out = {}
+    # (1) fp32 state: L layers of [B,H,dk,dv] fp32 states, one token per launch
+    hs = [h0.clone() for _ in range(L)]
+
+    def fp32_step():
+        for n in range(W):
+            for l in range(L):
+                tk = ring[l]
+                lq.lq_gdn_fp32_recurrence(d, hs[l], 1, tk["q"][n:n + 1], tk["k"][n:n + 1], tk["v"][n:n + 1],
+                                          tk["alpha"][n:n + 1], tk["beta"][n:n + 1], o.unsqueeze(0))
+    tps, ms = timed(fp32_step, B * W * L)
+    us = kernel_us(fp32_step, lq.LQ_KERNEL_FP32_RECURRENCE)
+    fp32_bytes = B * H * (2 * 4 * dk * dv + 4 * (2 * dk + dv + (dk if wl.per_key else 1) + 1) + 4 * dv)
+    out["fp32_state_decode"] = {
+        "tokens_per_s": round(tps, 1), "ms_per_step": round(ms, 4), "avg_launch_us": round(us, 3),
+        "hbm_GBps": round(fp32_bytes / (us * 1e-6) / 1e9, 1),
+        "speedup_int8_path_tokens_per_s": round(lq_value / tps, 3),
+        "speedup_int8_decode_kernel": round(us / lq_decode_us, 3)}
+    del hs
+    torch.cuda.empty_cache()
+    # (2) per-token int8: decode at slot 0 then flush, every token
+    d1 = lq.make_dims(B, H, dk, dv, 1, 0, d.decay_mode, 0)
+    lay1 = [lq.LayerState.allocate(d1, h0.device) for _ in range(L)]
+    for st in lay1:
+        lq.lq_gdn_state_quantize(st, h0)
+
+    def naive_step():
+        for n in range(W):
+            for l in range(L):
+                tk = ring[l]
+                lq.lq_gdn_decode_step(lay1[l], 0, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                      tk["beta"][n], o)
+                lq.lq_gdn_window_flush(lay1[l], 1)
+    tps1, ms1 = timed(naive_step, B * W * L)
+    out["per_token_int8"] = {"tokens_per_s": round(tps1, 1), "ms_per_step": round(ms1, 4),
+                             "speedup_windowed_vs_per_token": round(lq_value / tps1, 3)}
+    del lay1
+    torch.cuda.empty_cache()
+    out["fidelity"] = fidelity(wl, d, h0)
+    return out
+
+
+def fidelity(wl, d, h0, Bs: int = 8, T: int = 64):
+    """Output error against the fp32 recurrence (norm-wise per token and head:
+    max_j |do_j| / max_j |o_j|) over T tokens from the prefilled state, for
+    the windowed scheme (W, C, smoothing) and for per-token int8 (W = 1, C = 0,
+    no smoothing), on the first Bs batch rows."""
+    import torch
+    from recurrent_state_quant_lq_amd import inputs, lq
+    H, dk, dv = wl.H, wl.dk, wl.dv
+    dev = h0.device
+    h = h0[:Bs].clone()          # the reference advances its own copy in place
+    tok = inputs.device_tokens(wl.seed * 31 + 5, T, Bs, H, dk, dv, per_key=wl.per_key,
+                               beta_lo=wl.beta_lo, beta_hi=wl.beta_hi, device=dev)
+    dref = lq.make_dims(Bs, H, dk, dv, wl.W, wl.C, d.decay_mode, wl.smooth)
+    o_ref = torch.empty((T, Bs, H, dv), dtype=torch.float32, device=dev)
+    lq.lq_gdn_fp32_recurrence(dref, h, T, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], o_ref)
+
+    def run(W, C, smooth):
+        dq = lq.make_dims(Bs, H, dk, dv, W, C, d.decay_mode, smooth)
+        st = lq.LayerState.allocate(dq, dev)
+        lq.lq_gdn_state_quantize(st, h0[:Bs].clone())
+        o = torch.empty((T, Bs, H, dv), dtype=torch.float32, device=dev)
+        for t in range(T):
+            n = t % W
+            lq.lq_gdn_decode_step(st, n, tok["q"][t], tok["k"][t], tok["v"][t], tok["alpha"][t],
+                                  tok["beta"][t], o[t])
+            if n == W - 1:
+                lq.lq_gdn_window_flush(st, W)
+        err = (o - o_ref).abs().amax(-1) / o_ref.abs().amax(-1).clamp_min(1e-30)
+        return {"max_rel_err": float(err.max()), "mean_rel_err": float(err.mean())}
+
+    return {"sample": f"B={Bs} H={H} T={T} tokens from the prefilled state",
+            f"windowed_W{wl.W}_C{wl.C}_smooth{wl.smooth}": run(wl.W, wl.C, wl.smooth),
+            "per_token_W1_C0_nosmooth": run(1, 0, 0)}
+
+
 def cpu_baseline(wl, windows: int, threads: int):
     """The oracle (plain C, as it is) on the host: the windowed int8 scheme
     for all B*H heads of one layer, `windows` consecutive windows per head
@@ -227,7 +380,7 @@ def cpu_baseline(wl, windows: int, threads: int):
 
 
 def main():
-    if len(sys.argv) > 1 and sys.argv[1] in ("--trace-summary", "--pmc-summary"):
+    if len(sys.argv) > 1 and sys.argv[1] in ("--trace-summary", "--pmc-summary", "--counter-summary"):
         argv = sys.argv[2:]
         cmd = ""
         if "--" in argv:
@@ -236,6 +389,8 @@ def main():
             argv = argv[:k]
         if sys.argv[1] == "--trace-summary":
             trace_summary(argv[0], argv[1], cmd)
+        elif sys.argv[1] == "--counter-summary":
+            counter_summary(argv[0], argv[1:], cmd)
         else:
             pmc_summary(argv[0], argv[1], argv[2], argv[3], argv[4], cmd)
         return
@@ -247,6 +402,8 @@ def main():
     ap.add_argument("--workload", default="gdn_batched")
     ap.add_argument("--W", type=int, default=0, help="override the window length")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the fp32-state and per-token int8 comparisons")
     ap.add_argument("--cpu-windows", type=int, default=128)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (for PMC calibration)")
@@ -297,7 +454,7 @@ def main():
     layers = [lq.LayerState.allocate(d, dev) for _ in range(L)]
     for st in layers:
         lq.lq_gdn_state_quantize(st, h)
-    del h
+    h_prefill = h
     # input ring: W tokens per layer
     ring = [gen(wl.seed * 7 + l, W) for l in range(L)]
     o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device=dev)
@@ -382,6 +539,12 @@ def main():
         "decode_us_by_slot": [round(x, 3) for x in dec_avg_us],
         "kernel_hash": hsh,
     }
+    if not args.no_compare:
+        del layers
+        torch.cuda.empty_cache()
+        res["comparisons"] = comparisons(wl, L, d, h_prefill, ring, value, dec_total_s * 1e6 / W,
+                                         max(4, min(16, args.steps)))
+    del h_prefill
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_windows, threads)
