@@ -308,6 +308,30 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
                              "speedup_windowed_vs_per_token": round(lq_value / tps1, 3)}
     del lay1
     torch.cuda.empty_cache()
+    # (3) ragged windows: batch row b sits at window position (b + t) mod W at
+    # token t, so 1/W of the rows flush after every token (device-side
+    # positions, lq_gdn_decode_step_ragged + lq_gdn_window_flush_ragged)
+    layr = [lq.LayerState.allocate(d, h0.device) for _ in range(L)]
+    for st in layr:
+        lq.lq_gdn_state_quantize(st, h0)
+    rows = torch.arange(B, dtype=torch.int32, device=h0.device)
+    pos_t = [((rows + n) % W).to(torch.int32).contiguous() for n in range(W)]
+    nb_t = [torch.where(p == W - 1, W, 0).to(torch.int32).contiguous() for p in pos_t]
+
+    def ragged_step():
+        for n in range(W):
+            for l in range(L):
+                tk = ring[l]
+                lq.lq_gdn_decode_step_ragged(layr[l], pos_t[n], tk["q"][n], tk["k"][n], tk["v"][n],
+                                             tk["alpha"][n], tk["beta"][n], o)
+                lq.lq_gdn_window_flush_ragged(layr[l], nb_t[n])
+    tpsr, msr = timed(ragged_step, B * W * L)
+    out["ragged_windows"] = {"tokens_per_s": round(tpsr, 1), "ms_per_step": round(msr, 4),
+                             "vs_lockstep": round(tpsr / lq_value, 3),
+                             "schedule": "row b at window position (b + t) mod W; rows whose window "
+                                         "fills are flushed after every token"}
+    del layr
+    torch.cuda.empty_cache()
     out["fidelity"] = fidelity(wl, d, h0)
     return out
 

@@ -151,6 +151,30 @@ int lq_gdn_window_flush(const lq_dims *d, const lq_state *st, int32_t n_buffered
                         float *h_out, void *stream);
 
 /*
+ * Ragged windows (sequences of a batch at different window positions, as in
+ * serving).  Same as lq_gdn_decode_step, with the position of batch row b
+ * read from the DEVICE array pos[b] (int32 [B], 4-byte aligned): every head
+ * of row b appends slot pos[b].  A row with pos[b] outside [0, W) is skipped
+ * (its o rows and buffer are left untouched).  The caller keeps pos.
+ * Errors: as lq_gdn_decode_step (LQ_ERR_NULL / LQ_ERR_ALIGN also for pos).
+ */
+int lq_gdn_decode_step_ragged(const lq_dims *d, const lq_state *st, const int32_t *pos,
+                              const float *q, const float *k, const float *v,
+                              const float *alpha, const float *beta, float *o, void *stream);
+
+/*
+ * Ragged windows: lq_gdn_window_flush with the number of buffered slots of
+ * batch row b read from the DEVICE array n_buffered[b] (int32 [B]).  Rows
+ * with n_buffered[b] = 0 (or outside [0, W]) are left untouched, as are their
+ * h_out rows.  A row whose window is full (or whose sequence ends) is passed
+ * its slot count and restarts at position 0.
+ * Errors: as lq_gdn_window_flush (LQ_ERR_NULL / LQ_ERR_ALIGN also for
+ * n_buffered).
+ */
+int lq_gdn_window_flush_ragged(const lq_dims *d, const lq_state *st, const int32_t *n_buffered,
+                               float *h_out, void *stream);
+
+/*
  * Quantizes an fp32 state h [B,H,dk,dv] into the codec of st (steps 1-3 of
  * lq_gdn_window_flush; buffers untouched).  Used to start decoding from a
  * prefilled state.

@@ -57,8 +57,10 @@ struct DecodeArgs {
     const float* alpha;
     const float* beta;
     float* o;
+    const int32_t* pos_dev;   // per batch row (ragged positions), or null: pos for every row
     int W;
     int C;
+    int H;
     int pos;
 };
 
@@ -118,8 +120,12 @@ void decode_kernel(DecodeArgs a) {
     const int lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const size_t head = blockIdx.x;
-    const int n = NB >= 0 ? NB : a.pos;
     const int W = a.W, C = a.C;
+    int n = NB;
+    if constexpr (NB < 0) {
+        n = a.pos_dev ? a.pos_dev[head / (unsigned)a.H] : a.pos;
+        if (n < 0 || n >= W) return;              // a row outside its window: untouched
+    }
 
     const float* __restrict__ bkr = a.bk + head * (size_t)W * DK;
     const float* __restrict__ bmr = a.bm + head * (size_t)W * DV;
@@ -391,22 +397,22 @@ hipError_t launch_dk(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
         case 8: return kda ? launch_nb<DK, 8, true, -1>(d, args, s) : launch_nb<DK, 8, false, -1>(d, args, s);
         case 16:
             if constexpr (DK == 128)
-                return kda ? launch_fixed<true>(d, args, s, std::make_integer_sequence<int, 16>{})
-                           : launch_fixed<false>(d, args, s, std::make_integer_sequence<int, 16>{});
-            else
-                return kda ? launch_nb<DK, 16, true, -1>(d, args, s) : launch_nb<DK, 16, false, -1>(d, args, s);
+                if (!args.pos_dev)
+                    return kda ? launch_fixed<true>(d, args, s, std::make_integer_sequence<int, 16>{})
+                               : launch_fixed<false>(d, args, s, std::make_integer_sequence<int, 16>{});
+            return kda ? launch_nb<DK, 16, true, -1>(d, args, s) : launch_nb<DK, 16, false, -1>(d, args, s);
         default: return kda ? launch_nb<DK, 32, true, -1>(d, args, s) : launch_nb<DK, 32, false, -1>(d, args, s);
     }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const float* q,
-                         const float* k, const float* v, const float* alpha, const float* beta,
-                         float* o, hipStream_t s) {
+hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
+                         const float* q, const float* k, const float* v, const float* alpha,
+                         const float* beta, float* o, hipStream_t s) {
     DecodeArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
                     st.buf_k, st.buf_m, st.buf_g,
-                    q, k, v, alpha, beta, o, d.W, d.C, pos};
+                    q, k, v, alpha, beta, o, pos_dev, d.W, d.C, d.H, pos};
     switch (d.dk) {
         case 16: return launch_dk<16>(d, args, s);
         case 64: return launch_dk<64>(d, args, s);

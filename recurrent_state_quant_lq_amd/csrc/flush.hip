@@ -301,10 +301,12 @@ struct FlushArgs {
     const float* bm;
     const float* bg;
     float* h_out;
+    const int32_t* n_dev;     // per batch row (ragged windows), or null: N for every row
     int W;
     int C;
     int N;
     int smooth;
+    int H;
 };
 
 // Rows 0..NPAD-1 of a [rows][D] fp32 block (row index clamped to rmax) into
@@ -363,7 +365,9 @@ void flush_kernel(FlushArgs a) {
     const int lane = t & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const size_t head = blockIdx.x;
-    const int W = a.W, C = a.C, N = a.N;
+    const int W = a.W, C = a.C;
+    const int N = a.n_dev ? a.n_dev[head / (unsigned)a.H] : a.N;
+    if (N <= 0 || N > W) return;                  // nothing buffered (or out of range): untouched
 
     const int8_t* sq = a.sq + head * (DK * DV);
 
@@ -580,10 +584,10 @@ hipError_t flush_dk(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, float* h_out,
-                        hipStream_t s) {
+hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, const int32_t* n_dev,
+                        float* h_out, hipStream_t s) {
     FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
-                   st.buf_k, st.buf_m, st.buf_g, h_out, d.W, d.C, n_buffered, d.smooth};
+                   st.buf_k, st.buf_m, st.buf_g, h_out, n_dev, d.W, d.C, n_buffered, d.smooth, d.H};
     switch (d.dk) {
         case 16: return flush_dk<16>(d, args, s);
         case 64: return flush_dk<64>(d, args, s);

@@ -151,7 +151,19 @@ int lq_gdn_decode_step(const lq_dims* d, const lq_state* st, int32_t pos, const 
     if ((rc = check_tokens(d, q, k, v, alpha, beta, o, true))) return rc;
     if (pos < 0) return LQ_ERR_POS;
     if (pos >= d->W) return LQ_ERR_WINDOW_FULL;
-    return finish(lq::launch_decode(*d, *st, pos, q, k, v, alpha, beta, o, (hipStream_t)stream));
+    return finish(lq::launch_decode(*d, *st, pos, nullptr, q, k, v, alpha, beta, o, (hipStream_t)stream));
+}
+
+int lq_gdn_decode_step_ragged(const lq_dims* d, const lq_state* st, const int32_t* pos,
+                              const float* q, const float* k, const float* v, const float* alpha,
+                              const float* beta, float* o, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, true))) return rc;
+    if ((rc = check_tokens(d, q, k, v, alpha, beta, o, true))) return rc;
+    if (!pos) return LQ_ERR_NULL;
+    if (!aligned4(pos)) return LQ_ERR_ALIGN;
+    return finish(lq::launch_decode(*d, *st, 0, pos, q, k, v, alpha, beta, o, (hipStream_t)stream));
 }
 
 int lq_gdn_window_flush(const lq_dims* d, const lq_state* st, int32_t n_buffered, float* h_out,
@@ -162,7 +174,18 @@ int lq_gdn_window_flush(const lq_dims* d, const lq_state* st, int32_t n_buffered
     if (h_out && !aligned16(h_out)) return LQ_ERR_ALIGN;
     if (n_buffered < 0 || n_buffered > d->W) return LQ_ERR_POS;
     if (n_buffered == 0) return LQ_OK;
-    return finish(lq::launch_flush(*d, *st, n_buffered, h_out, (hipStream_t)stream));
+    return finish(lq::launch_flush(*d, *st, n_buffered, nullptr, h_out, (hipStream_t)stream));
+}
+
+int lq_gdn_window_flush_ragged(const lq_dims* d, const lq_state* st, const int32_t* n_buffered,
+                               float* h_out, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, true))) return rc;
+    if (h_out && !aligned16(h_out)) return LQ_ERR_ALIGN;
+    if (!n_buffered) return LQ_ERR_NULL;
+    if (!aligned4(n_buffered)) return LQ_ERR_ALIGN;
+    return finish(lq::launch_flush(*d, *st, 0, n_buffered, h_out, (hipStream_t)stream));
 }
 
 int lq_gdn_state_quantize(const lq_dims* d, const float* h, const lq_state* st, void* stream) {

@@ -11,11 +11,12 @@ namespace lq {
 
 // Kernel launchers.  Arguments were validated by the C ABI layer; each
 // returns the hipError_t of its launch.
-hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const float* q,
-                         const float* k, const float* v, const float* alpha, const float* beta,
-                         float* o, hipStream_t s);
-hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, float* h_out,
-                        hipStream_t s);
+// pos_dev / n_dev: per-batch-row device arrays (ragged windows) or null.
+hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
+                         const float* q, const float* k, const float* v, const float* alpha,
+                         const float* beta, float* o, hipStream_t s);
+hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, const int32_t* n_dev,
+                        float* h_out, hipStream_t s);
 hipError_t launch_quantize(const lq_dims& d, const float* h, const lq_state& st, hipStream_t s);
 hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* h_out, hipStream_t s);
 hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const float* q,

@@ -23,7 +23,8 @@ LQ_OK, LQ_ERR_NULL, LQ_ERR_DIMS, LQ_ERR_UNSUPPORTED, LQ_ERR_WINDOW_FULL, LQ_ERR_
 LQ_DECAY_SCALAR, LQ_DECAY_PER_KEY = 0, 1
 
 # every symbol include/lq.h declares
-EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_state_quantize",
+EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_ragged",
+           "lq_gdn_window_flush_ragged", "lq_gdn_state_quantize",
            "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_state_bytes",
            "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims",
            "lq_timing_enable", "lq_timing_collect")
@@ -62,10 +63,13 @@ def load() -> ct.CDLL:
         D, S, P, I = ct.POINTER(lq_dims), ct.POINTER(lq_state), ct.c_void_p, ct.c_int32
         L.lq_gdn_decode_step.argtypes = [D, S, I, P, P, P, P, P, P, P]
         L.lq_gdn_window_flush.argtypes = [D, S, I, P, P]
+        L.lq_gdn_decode_step_ragged.argtypes = [D, S, P, P, P, P, P, P, P, P]
+        L.lq_gdn_window_flush_ragged.argtypes = [D, S, P, P, P]
         L.lq_gdn_state_quantize.argtypes = [D, P, S, P]
         L.lq_gdn_state_dequantize.argtypes = [D, S, P, P]
         L.lq_gdn_fp32_recurrence.argtypes = [D, P, I, P, P, P, P, P, P, P]
-        for f in ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_state_quantize",
+        for f in ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_ragged",
+                  "lq_gdn_window_flush_ragged", "lq_gdn_state_quantize",
                   "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_check_dims",
                   "lq_last_hip_error"):
             getattr(L, f).restype = ct.c_int
@@ -211,6 +215,33 @@ def lq_gdn_window_flush(st: LayerState, n_buffered: int, h_out=None, stream=None
     rc = load().lq_gdn_window_flush(ct.byref(d), ct.byref(cs), int(n_buffered), _ptr(h_out),
                                     _stream(stream))
     _raise("lq_gdn_window_flush", rc)
+
+
+def lq_gdn_decode_step_ragged(st: LayerState, pos, q, k, v, alpha, beta, o, stream=None):
+    """pos: device int32 [B], the window position of each batch row."""
+    d = st.dims
+    st.check()
+    _check(pos, "pos", (d.B,), torch.int32)
+    sh = _token_shapes(d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
+        _check(t, name, sh[name], torch.float32)
+    cs = st.c_state()
+    rc = load().lq_gdn_decode_step_ragged(ct.byref(d), ct.byref(cs), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
+    _raise("lq_gdn_decode_step_ragged", rc)
+
+
+def lq_gdn_window_flush_ragged(st: LayerState, n_buffered, h_out=None, stream=None):
+    """n_buffered: device int32 [B], slots to flush per batch row (0 = none)."""
+    d = st.dims
+    st.check()
+    _check(n_buffered, "n_buffered", (d.B,), torch.int32)
+    if h_out is not None:
+        _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
+    cs = st.c_state()
+    rc = load().lq_gdn_window_flush_ragged(ct.byref(d), ct.byref(cs), _ptr(n_buffered), _ptr(h_out),
+                                           _stream(stream))
+    _raise("lq_gdn_window_flush_ragged", rc)
 
 
 def lq_gdn_state_quantize(st: LayerState, h, stream=None):

@@ -148,3 +148,22 @@ def test_timing_hook_host_side():
     assert L.lq_timing_collect(4, None, None, ct.byref(n)) == lq.LQ_ERR_NULL
     assert L.lq_timing_collect(0, None, None, None) == lq.LQ_ERR_NULL
     assert L.lq_timing_enable(0) == lq.LQ_OK
+
+
+def test_ragged_argument_errors():
+    L = lq.load()
+    d = _dims()
+    st = _fake_state()
+    L.lq_gdn_decode_step_ragged.argtypes = [ct.c_void_p] * 10
+    L.lq_gdn_window_flush_ragged.argtypes = [ct.c_void_p] * 5
+    args = (A, A, A, A, A, A)
+    dec = lambda dd, s, p, *a: L.lq_gdn_decode_step_ragged(dd, s, p, *a, None)
+    assert dec(ct.byref(d), ct.byref(st), None, *args) == lq.LQ_ERR_NULL
+    assert dec(ct.byref(d), ct.byref(st), ct.c_void_p(0x7000002), *args) == lq.LQ_ERR_ALIGN
+    assert dec(None, ct.byref(st), A, *args) == lq.LQ_ERR_NULL
+    assert dec(ct.byref(_dims(dk=96, dv=96)), ct.byref(st), A, *args) == lq.LQ_ERR_UNSUPPORTED
+    fl = lambda dd, s, n, h: L.lq_gdn_window_flush_ragged(dd, s, n, h, None)
+    assert fl(ct.byref(d), ct.byref(st), None, None) == lq.LQ_ERR_NULL
+    assert fl(ct.byref(d), ct.byref(st), ct.c_void_p(0x7000001), None) == lq.LQ_ERR_ALIGN
+    assert fl(ct.byref(d), ct.byref(st), A, B4) == lq.LQ_ERR_ALIGN
+    assert fl(ct.byref(d), ct.byref(_fake_state(null="buf_k")), A, None) == lq.LQ_ERR_NULL

@@ -18,7 +18,7 @@ from recurrent_state_quant_lq_amd.configs import PRESETS
 pytestmark = pytest.mark.gpu
 
 from gpu_harness import (BUF_TOL, H_TOL, O_TOL, codec_equal, dims_of, head_codec,  # noqa: E402
-                         rel_err, resync_run, say, upload_head_codec)
+                         oracle_buffer, rel_err, resync_run, say, upload_head_codec)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -300,3 +300,76 @@ def test_timing_hook_records_each_launch():
     assert fam == [lq.LQ_KERNEL_DECODE] * 3 + [lq.LQ_KERNEL_FLUSH]
     assert all(0.0 < x < 100.0 for x in ms), ms
     assert lq.lq_timing_collect() == ([], [])
+
+
+@pytest.mark.parametrize("dk,per_key", [(128, False), (64, True), (16, False)])
+def test_ragged_windows(dk, per_key):
+    """Batch rows at different window positions (the ragged entry points):
+    row b's first window ends after first[b] tokens, later ones after W, the
+    last at the end of the run; each flushed window is checked against the
+    oracle (outputs, buffer rows, fp32 state, codec bytes) and the oracle's
+    next codec is uploaded (resync).  Rows not flushed keep their codec and
+    their h_out rows; a row whose position is out of range is skipped."""
+    B, H, W, C, T = 3, 4, 8, 2, 21
+    say(f"ragged dk={dk} per_key={per_key}")
+    d = lq.make_dims(B, H, dk, dk, W, C, int(per_key), 1)
+    tok = inputs.host_tokens(321 + dk, T, B, H, dk, dk, per_key=per_key, beta_lo=0.1, beta_hi=0.9)
+    tk = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in tok.items()}
+    rng = np.random.default_rng(dk)
+    H0 = (rng.standard_normal((B, H, dk, dk)) * 0.2).astype(np.float32)
+    codec = {(b, h): O.quantize(H0[b, h], C, 1) for b in range(B) for h in range(H)}
+    st = lq.LayerState.allocate(d)
+    for (b, h), cd in codec.items():
+        upload_head_codec(st, b, h, cd)
+    first = [3, W, 5]
+    wlen = list(first)                      # length of each row's current window
+    pos, start = [0] * B, [0] * B
+    o = torch.empty((B, H, dk), device="cuda")
+    h_out = torch.empty((B, H, dk, dk), device="cuda")
+    outs = []
+    flushed = 0
+    for t in range(T):
+        lq.lq_gdn_decode_step_ragged(st, torch.tensor(pos, dtype=torch.int32, device="cuda"),
+                                     tk["q"][t], tk["k"][t], tk["v"][t], tk["alpha"][t], tk["beta"][t], o)
+        outs.append(o.clone())
+        nb = [pos[b] + 1 if (pos[b] + 1 == wlen[b] or t == T - 1) else 0 for b in range(B)]
+        if not any(nb):
+            pos = [p + 1 for p in pos]
+            continue
+        before = {b: [head_codec(st, b, h) for h in range(H)] for b in range(B) if not nb[b]}
+        h_out.fill_(7.0)
+        lq.lq_gdn_window_flush_ragged(st, torch.tensor(nb, dtype=torch.int32, device="cuda"), h_out)
+        torch.cuda.synchronize()
+        for b in range(B):
+            if not nb[b]:
+                assert (h_out[b] == 7.0).all(), ("h_out row written", t, b)
+                for h in range(H):
+                    assert codec_equal(head_codec(st, b, h), before[b][h]), ("codec changed", t, b, h)
+                pos[b] += 1
+                continue
+            N, t0 = nb[b], start[b]
+            for h in range(H):
+                ht = O.head_tokens(tok, b, h, t0, t0 + N)
+                res = O.window(codec[(b, h)], ht, per_key, W, C, 1)
+                got_o = torch.stack([outs[i][b, h] for i in range(t0, t0 + N)]).cpu().numpy()
+                assert rel_err(got_o, res["o"]) <= O_TOL, (t, b, h)
+                ob = oracle_buffer(codec[(b, h)], res["buf"], N)
+                for key in ("k", "m", "g"):
+                    g = getattr(st, "buf_" + key)[b, h, :N].cpu().numpy()
+                    assert rel_err(g, ob[key]) <= BUF_TOL, (key, t, b, h)
+                hg = h_out[b, h].cpu().numpy()
+                assert np.abs(hg - res["H"]).max() <= H_TOL * max(np.abs(res["H"]).max(), 1e-30)
+                assert codec_equal(head_codec(st, b, h), O.quantize(hg, C, 1)), ("codec bytes", t, b, h)
+                codec[(b, h)] = res["codec"]
+                upload_head_codec(st, b, h, res["codec"])
+            flushed += 1
+            pos[b], start[b], wlen[b] = 0, t + 1, W
+    assert flushed >= 2 * B
+    # a row with an out-of-range position is skipped
+    o.fill_(5.0)
+    bk = st.buf_k.clone()
+    bad = torch.tensor([0, W, -1], dtype=torch.int32, device="cuda")
+    lq.lq_gdn_decode_step_ragged(st, bad, tk["q"][0], tk["k"][0], tk["v"][0], tk["alpha"][0], tk["beta"][0], o)
+    torch.cuda.synchronize()
+    assert (o[1:] == 5.0).all() and torch.equal(st.buf_k[1:], bk[1:])
+    assert not (o[0] == 5.0).all()
