@@ -332,6 +332,19 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
                                          "fills are flushed after every token"}
     del layr
     torch.cuda.empty_cache()
+    # (4) checkpoints: pack the quantized state of one layer into a blob and back
+    stc = lq.LayerState.allocate(d, h0.device)
+    lq.lq_gdn_state_quantize(stc, h0)
+    blob = torch.empty((lq.lq_checkpoint_bytes(d),), dtype=torch.uint8, device=h0.device)
+    pk = kernel_us(lambda: [lq.lq_gdn_state_pack(stc, blob) for _ in range(4)], lq.LQ_KERNEL_CHECKPOINT)
+    uk = kernel_us(lambda: [lq.lq_gdn_state_unpack(stc, blob) for _ in range(4)], lq.LQ_KERNEL_CHECKPOINT)
+    nb = blob.numel()
+    out["checkpoint"] = {"bytes": nb, "bytes_per_value": round(nb / (B * H * dk * dv), 4),
+                         "fp32_state_bytes": B * H * dk * dv * 4,
+                         "pack_us": round(pk, 3), "unpack_us": round(uk, 3),
+                         "pack_hbm_GBps": round(2 * nb / (pk * 1e-6) / 1e9, 1),
+                         "unpack_hbm_GBps": round(2 * nb / (uk * 1e-6) / 1e9, 1)}
+    del stc, blob
     out["fidelity"] = fidelity(wl, d, h0)
     return out
 

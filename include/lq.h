@@ -182,6 +182,22 @@ int lq_gdn_window_flush_ragged(const lq_dims *d, const lq_state *st, const int32
 int lq_gdn_state_quantize(const lq_dims *d, const float *h, const lq_state *st, void *stream);
 
 /*
+ * Checkpoints of the quantized state ([news ¶5]: about 1.19 bytes per value
+ * with scales and correction terms), e.g. for prefix caching at window
+ * boundaries.  The blob holds one record per head, in (b, h) order (the H
+ * records of a sequence are adjacent), each lq_checkpoint_bytes(d) / (B*H)
+ * bytes:  sq (dk*dv int8, value-column-major) | row_scale (4*dk) |
+ * col_scale (4*dv) | comp_val (4*C*dv) | comp_idx (4*C) | zero padding to a
+ * multiple of 16 bytes.  blob: device memory, 16-byte aligned, caller-owned.
+ * Pack reads the codec arrays of st; unpack writes them (the window buffer
+ * is not part of a checkpoint: take one right after a flush).
+ * Errors: LQ_ERR_NULL, LQ_ERR_ALIGN, LQ_ERR_DIMS, LQ_ERR_UNSUPPORTED.
+ */
+size_t lq_checkpoint_bytes(const lq_dims *d);
+int lq_gdn_state_pack(const lq_dims *d, const lq_state *st, void *blob, void *stream);
+int lq_gdn_state_unpack(const lq_dims *d, const void *blob, const lq_state *st, void *stream);
+
+/*
  * Writes the fp32 state the codec stands for into h_out [B,H,dk,dv]
  * (row-major): (sq_ij * row_scale_i) * col_scale_j, plus comp_val on the
  * compensator rows.
@@ -227,7 +243,8 @@ enum {
     LQ_KERNEL_FLUSH = 1,        /* lq_gdn_window_flush */
     LQ_KERNEL_QUANTIZE = 2,     /* lq_gdn_state_quantize */
     LQ_KERNEL_DEQUANTIZE = 3,   /* lq_gdn_state_dequantize */
-    LQ_KERNEL_FP32_RECURRENCE = 4
+    LQ_KERNEL_FP32_RECURRENCE = 4,
+    LQ_KERNEL_CHECKPOINT = 5    /* lq_gdn_state_pack / lq_gdn_state_unpack */
 };
 
 /* on = 1: drop earlier records and start recording (at most 65536 launches;

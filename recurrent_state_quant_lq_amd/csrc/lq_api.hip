@@ -216,6 +216,27 @@ int lq_gdn_fp32_recurrence(const lq_dims* d, float* h, int32_t T, const float* q
     return finish(lq::launch_fp32_recurrence(*d, h, T, q, k, v, alpha, beta, o, (hipStream_t)stream));
 }
 
+size_t lq_checkpoint_bytes(const lq_dims* d) {
+    if (check_dims(d) != LQ_OK) return 0;
+    return (size_t)d->B * d->H * lq::checkpoint_head_bytes(*d);
+}
+
+int lq_gdn_state_pack(const lq_dims* d, const lq_state* st, void* blob, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, false))) return rc;
+    if ((rc = check_ptrs({blob}))) return rc;
+    return finish(lq::launch_checkpoint(*d, *st, blob, true, (hipStream_t)stream));
+}
+
+int lq_gdn_state_unpack(const lq_dims* d, const void* blob, const lq_state* st, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, false))) return rc;
+    if ((rc = check_ptrs({blob}))) return rc;
+    return finish(lq::launch_checkpoint(*d, *st, const_cast<void*>(blob), false, (hipStream_t)stream));
+}
+
 size_t lq_state_bytes(const lq_dims* d) {
     if (check_dims(d) != LQ_OK) return 0;
     const size_t heads = (size_t)d->B * d->H;

@@ -27,9 +27,10 @@ EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_ragg
            "lq_gdn_window_flush_ragged", "lq_gdn_state_quantize",
            "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_state_bytes",
            "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims",
-           "lq_timing_enable", "lq_timing_collect")
+           "lq_timing_enable", "lq_timing_collect", "lq_checkpoint_bytes", "lq_gdn_state_pack",
+           "lq_gdn_state_unpack")
 LQ_KERNEL_DECODE, LQ_KERNEL_FLUSH, LQ_KERNEL_QUANTIZE, LQ_KERNEL_DEQUANTIZE, \
-    LQ_KERNEL_FP32_RECURRENCE = range(5)
+    LQ_KERNEL_FP32_RECURRENCE, LQ_KERNEL_CHECKPOINT = range(6)
 
 
 class lq_dims(ct.Structure):
@@ -81,6 +82,12 @@ def load() -> ct.CDLL:
         L.lq_status_str.argtypes = [ct.c_int]
         L.lq_status_str.restype = ct.c_char_p
         L.lq_last_hip_error.argtypes = []
+        L.lq_checkpoint_bytes.argtypes = [D]
+        L.lq_checkpoint_bytes.restype = ct.c_size_t
+        L.lq_gdn_state_pack.argtypes = [D, S, P, P]
+        L.lq_gdn_state_pack.restype = ct.c_int
+        L.lq_gdn_state_unpack.argtypes = [D, P, S, P]
+        L.lq_gdn_state_unpack.restype = ct.c_int
         L.lq_timing_enable.argtypes = [ct.c_int32]
         L.lq_timing_enable.restype = ct.c_int
         L.lq_timing_collect.argtypes = [ct.c_int32, ct.POINTER(ct.c_int32), ct.POINTER(ct.c_float),
@@ -272,6 +279,29 @@ def lq_gdn_fp32_recurrence(d: lq_dims, h, T: int, q, k, v, alpha, beta, o=None, 
     rc = load().lq_gdn_fp32_recurrence(ct.byref(d), _ptr(h), int(T), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
     _raise("lq_gdn_fp32_recurrence", rc)
+
+
+def lq_checkpoint_bytes(d: lq_dims) -> int:
+    return int(load().lq_checkpoint_bytes(ct.byref(d)))
+
+
+def lq_gdn_state_pack(st: LayerState, blob, stream=None):
+    """blob: device uint8 tensor of lq_checkpoint_bytes(st.dims) bytes."""
+    d = st.dims
+    st.check(with_buffer=False)
+    _check(blob, "blob", (lq_checkpoint_bytes(d),), torch.uint8)
+    cs = st.c_state()
+    _raise("lq_gdn_state_pack", load().lq_gdn_state_pack(ct.byref(d), ct.byref(cs), _ptr(blob),
+                                                          _stream(stream)))
+
+
+def lq_gdn_state_unpack(st: LayerState, blob, stream=None):
+    d = st.dims
+    st.check(with_buffer=False)
+    _check(blob, "blob", (lq_checkpoint_bytes(d),), torch.uint8)
+    cs = st.c_state()
+    _raise("lq_gdn_state_unpack", load().lq_gdn_state_unpack(ct.byref(d), _ptr(blob), ct.byref(cs),
+                                                              _stream(stream)))
 
 
 def lq_state_bytes(d: lq_dims) -> int:

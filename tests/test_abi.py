@@ -167,3 +167,17 @@ def test_ragged_argument_errors():
     assert fl(ct.byref(d), ct.byref(st), ct.c_void_p(0x7000001), None) == lq.LQ_ERR_ALIGN
     assert fl(ct.byref(d), ct.byref(st), A, B4) == lq.LQ_ERR_ALIGN
     assert fl(ct.byref(d), ct.byref(_fake_state(null="buf_k")), A, None) == lq.LQ_ERR_NULL
+
+
+def test_checkpoint_sizes_and_errors():
+    L = lq.load()
+    d = _dims()                                   # B=2 H=3 d=128 C=4
+    assert lq.lq_checkpoint_bytes(d) == 6 * 19472 == L.lq_state_bytes(ct.byref(d))
+    d1 = _dims(C=1)                               # 17,924 bytes padded to 17,936
+    assert lq.lq_checkpoint_bytes(d1) == 6 * 17936
+    assert lq.lq_checkpoint_bytes(_dims(dk=96, dv=96)) == 0
+    st = _fake_state()
+    assert L.lq_gdn_state_pack(ct.byref(d), ct.byref(st), None, None) == lq.LQ_ERR_NULL
+    assert L.lq_gdn_state_pack(ct.byref(d), ct.byref(st), ct.c_void_p(0x7000004), None) == lq.LQ_ERR_ALIGN
+    assert L.lq_gdn_state_unpack(ct.byref(d), A, ct.byref(_fake_state(null="sq")), None) == lq.LQ_ERR_NULL
+    assert L.lq_gdn_state_unpack(None, A, ct.byref(st), None) == lq.LQ_ERR_NULL

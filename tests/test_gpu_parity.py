@@ -373,3 +373,53 @@ def test_ragged_windows(dk, per_key):
     torch.cuda.synchronize()
     assert (o[1:] == 5.0).all() and torch.equal(st.buf_k[1:], bk[1:])
     assert not (o[0] == 5.0).all()
+
+
+@pytest.mark.parametrize("dk,C", [(128, 4), (64, 1), (16, 0)])
+def test_checkpoint_round_trip(dk, C):
+    """Pack writes each head's record in the documented layout; unpack
+    restores the codec bit for bit; a state restored from a checkpoint decodes
+    exactly like the original."""
+    B, H, W = 2, 3, 8
+    d = lq.make_dims(B, H, dk, dk, W, C, 0, 1)
+    rng = np.random.default_rng(dk + C)
+    st = lq.LayerState.allocate(d)
+    h = torch.from_numpy((rng.standard_normal((B, H, dk, dk)) * 0.3).astype(np.float32)).cuda()
+    lq.lq_gdn_state_quantize(st, h)
+    nbytes = lq.lq_checkpoint_bytes(d)
+    blob = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    lq.lq_gdn_state_pack(st, blob)
+    torch.cuda.synchronize()
+    rec = nbytes // (B * H)
+    raw = blob.cpu().numpy()
+    for b in range(B):
+        for hh in range(H):
+            want = b"".join([st.sq[b, hh].cpu().numpy().tobytes(), st.row_scale[b, hh].cpu().numpy().tobytes(),
+                             st.col_scale[b, hh].cpu().numpy().tobytes(),
+                             st.comp_val[b, hh, :C].cpu().numpy().tobytes(),
+                             st.comp_idx[b, hh, :C].cpu().numpy().tobytes()])
+            want += b"\0" * (rec - len(want))
+            off = (b * H + hh) * rec
+            assert raw[off:off + rec].tobytes() == want, (b, hh)
+    st2 = lq.LayerState.allocate(d)
+    lq.lq_gdn_state_unpack(st2, blob)
+    torch.cuda.synchronize()
+    for name in ("sq", "row_scale", "col_scale"):
+        assert torch.equal(getattr(st2, name), getattr(st, name)), name
+    if C:
+        assert torch.equal(st2.comp_idx[..., :C], st.comp_idx[..., :C])
+        assert torch.equal(st2.comp_val[..., :C, :], st.comp_val[..., :C, :])
+    tok = inputs.host_tokens(17, W, B, H, dk, dk, per_key=False, beta_lo=0.1, beta_hi=0.9)
+    tk = {k: torch.from_numpy(v).cuda() for k, v in tok.items()}
+    o1, o2 = torch.empty((B, H, dk), device="cuda"), torch.empty((B, H, dk), device="cuda")
+    h1, h2 = torch.empty_like(h), torch.empty_like(h)
+    for n in range(W):
+        args = (tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n])
+        lq.lq_gdn_decode_step(st, n, *args, o1)
+        lq.lq_gdn_decode_step(st2, n, *args, o2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), n
+    lq.lq_gdn_window_flush(st, W, h1)
+    lq.lq_gdn_window_flush(st2, W, h2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(st.sq, st2.sq)
