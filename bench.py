@@ -4,8 +4,9 @@
     python bench.py [--steps K] [--warmup W] [--layers L] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch: a window of W decode
-tokens (lq_gdn_decode_step at positions 0..W-1) followed by the window flush
-(lq_gdn_window_flush), for each of L independent GDN layers (default 8, the
+tokens (lq_gdn_decode_step at positions 0..W-2, then the window's last token
+and the flush in one launch, lq_gdn_decode_step_flush), for each of L
+independent GDN layers (default 8, the
 layers' states rotated so that the working set, about 720 MB at
 B=64 H=32 d=128, exceeds the 256 MB Infinity Cache and every step reads HBM).
 Inputs are synthetic, drawn on the device before timing; the starting state
@@ -32,6 +33,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -63,6 +65,29 @@ def flush_bytes(wl, N: int) -> int:
     a = dk if wl.per_key else 1
     codec = dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4)
     return wl.B * wl.H * (2 * codec + N * 4 * (dk + dv + a))
+
+
+def decode_flush_bytes(wl, N: int) -> int:
+    """Algorithmic HBM bytes of one fused last-token decode + flush of N slots:
+    read and write the codec, the token inputs and output, N-1 buffered slots
+    read and slot N-1 written."""
+    dk, dv, C = wl.dk, wl.dv, wl.C
+    a = dk if wl.per_key else 1
+    codec = dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4)
+    io = 4 * (2 * dk + dv + a + 1) + 4 * dv
+    return wl.B * wl.H * (2 * codec + io + N * 4 * (dk + dv + a))
+
+
+def family(name: str):
+    """Kernel family of a rocprofv3 kernel name: decode, flush or decode_flush
+    (the flush kernel's instantiation with the fused decode, last template
+    argument true)."""
+    if "decode_kernel" in name:
+        return "decode"
+    m = re.search(r"flush_kernel<([^>]*)>", name)
+    if m:
+        return "decode_flush" if m.group(1).replace(" ", "").endswith(",true") else "flush"
+    return None
 
 
 def flush_flops(wl, N: int) -> int:
@@ -108,7 +133,7 @@ def trace_summary(out_md: str, stats_csv: str, command: str):
              "Command (from the repository root; rocprofv3 writes `*_kernel_stats.csv`):", "",
              "```", command, "```", "",
              "| kernel | calls | average us | min us | max us |", "|---|---:|---:|---:|---:|"]
-    dec, fl = [], []
+    fams = {"decode": [], "flush": [], "decode_flush": []}
     other = 0
     for r in rows:
         if "lq::" not in r["Name"]:
@@ -118,31 +143,30 @@ def trace_summary(out_md: str, stats_csv: str, command: str):
         avg = float(r["AverageNs"]) / 1e3
         lines.append(f"| `{nm}` | {r['Calls']} | {avg:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
                      f"{float(r['MaxNs']) / 1e3:.3f} |")
-        if "decode_kernel" in nm:
-            dec.append((int(r["Calls"]), avg))
-        if "flush_kernel" in nm:
-            fl.append((int(r["Calls"]), avg))
+        f = family(nm)
+        if f:
+            fams[f].append((int(r["Calls"]), avg))
     summ = {}
-    if dec:
-        summ["decode_avg_launch_us"] = round(sum(c * a for c, a in dec) / sum(c for c, _ in dec), 3)
-        summ["decode_instantiations"] = len(dec)
-    if fl:
-        summ["flush_avg_launch_us"] = round(sum(c * a for c, a in fl) / sum(c for c, _ in fl), 3)
+    for f, v in fams.items():
+        if v:
+            summ[f"{f}_avg_launch_us"] = round(sum(c * a for c, a in v) / sum(c for c, _ in v), 3)
+            summ[f"{f}_instantiations"] = len(v)
     lines += ["", f"({other} launches of the harness's own torch kernels not listed.)", "",
-              "Average over all decode launches (every window slot equally often):", "",
+              "Averages per kernel family over all its launches (decode: every window slot "
+              "but the last equally often; decode_flush: the last token with the flush):", "",
               json.dumps(summ), ""]
     open(out_md, "w").write("\n".join(lines))
     print(json.dumps(summ))
 
 
-def _pmc_per_dispatch(d: str, counter: str, pat: str):
-    """Mean per-dispatch value of `counter` over dispatches whose kernel name
-    contains `pat` (rocprofv3 --pmc CSV)."""
+def _pmc_per_dispatch(d: str, counter: str, fam: str):
+    """Mean per-dispatch value of `counter` over dispatches of kernel family
+    `fam` (rocprofv3 --pmc CSV)."""
     import glob
     vals = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in _csv_rows(f):
-            if r["Counter_Name"] == counter and pat in r["Kernel_Name"]:
+            if r["Counter_Name"] == counter and family(r["Kernel_Name"]) == fam:
                 vals.append(float(r["Counter_Value"]))
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
@@ -165,20 +189,21 @@ def pmc_summary(out_md: str, fetch_dir: str, write_dir: str, cal_fetch: str, cal
     cf, cw = largest(cal_fetch, "FETCH_SIZE"), largest(cal_write, "WRITE_SIZE")
     f_fetch = wl_bytes / (cf * 1024.0)
     f_write = wl_bytes / (cw * 1024.0)
-    df, ndf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "decode_kernel")
-    dw, ndw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "decode_kernel")
-    ff, nff = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "flush_kernel")
-    fw, nfw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "flush_kernel")
+    df, ndf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "decode")
+    dw, ndw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "decode")
+    ff, nff = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "decode_flush")
+    fw, nfw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "decode_flush")
     dec_bytes = df * 1024.0 * f_fetch + dw * 1024.0 * f_write
     fl_bytes = (ff * 1024.0 * f_fetch + fw * 1024.0 * f_write) if ff is not None else None
     from recurrent_state_quant_lq_amd.configs import PRESETS
     wl = PRESETS["gdn_batched"]
-    alg = sum(decode_bytes(wl, n) for n in range(wl.W)) / wl.W
+    alg = sum(decode_bytes(wl, n) for n in range(wl.W - 1)) / (wl.W - 1)
+    fl_alg = decode_flush_bytes(wl, wl.W)
     rec = {"kernel_hash": kernel_hash(), "hbm_bytes_per_launch": int(dec_bytes),
            "algorithmic_bytes_per_launch": int(alg), "traffic_over_algorithmic": round(dec_bytes / alg, 4),
            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
-           "flush_hbm_bytes_per_launch": int(fl_bytes) if fl_bytes else None,
-           "flush_algorithmic_bytes": flush_bytes(wl, wl.W)}
+           "decode_flush_hbm_bytes_per_launch": int(fl_bytes) if fl_bytes else None,
+           "decode_flush_algorithmic_bytes": fl_alg}
     lines = [f"# HBM traffic: {os.path.basename(out_md)[:-3]}", "",
              "Commands (from the repository root, one counter per run):", "", "```", command, "```", "",
              "| quantity | value |", "|---|---:|",
@@ -187,11 +212,12 @@ def pmc_summary(out_md: str, fetch_dir: str, write_dir: str, cal_fetch: str, cal
              f"| decode: FETCH_SIZE KiB per dispatch (mean of {ndf}) | {df:.1f} |",
              f"| decode: WRITE_SIZE KiB per dispatch (mean of {ndw}) | {dw:.1f} |",
              f"| decode: scaled HBM bytes per launch | {dec_bytes:.0f} |",
-             f"| decode: algorithmic bytes per launch (slot mean) | {alg:.0f} |"]
+             f"| decode: algorithmic bytes per launch (mean over slots 0..W-2) | {alg:.0f} |"]
     if fl_bytes:
-        lines += [f"| flush: FETCH_SIZE / WRITE_SIZE KiB per dispatch | {ff:.1f} / {fw:.1f} |",
-                  f"| flush: scaled HBM bytes per launch | {fl_bytes:.0f} |",
-                  f"| flush: algorithmic bytes per launch | {flush_bytes(wl, wl.W)} |"]
+        lines += [f"| decode_flush: FETCH_SIZE / WRITE_SIZE KiB per dispatch (means of {nff}) | "
+                  f"{ff:.1f} / {fw:.1f} |",
+                  f"| decode_flush: scaled HBM bytes per launch | {fl_bytes:.0f} |",
+                  f"| decode_flush: algorithmic bytes per launch | {fl_alg} |"]
     lines += ["", "Record read by bench.py (valid while the decode kernel source hashes to kernel_hash):",
               "", json.dumps(rec), ""]
     open(out_md, "w").write("\n".join(lines))
@@ -207,8 +233,7 @@ def counter_summary(out_md: str, dirs, command: str):
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in _csv_rows(f):
-                nm = r["Kernel_Name"]
-                fam = "decode" if "decode_kernel" in nm else "flush" if "flush_kernel" in nm else None
+                fam = family(r["Kernel_Name"])
                 if fam:
                     acc[(fam, r["Counter_Name"])].append(float(r["Counter_Value"]))
     fams = sorted({f for f, _ in acc})
@@ -441,6 +466,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the fp32-state and per-token int8 comparisons")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="end each window with lq_gdn_decode_step + lq_gdn_window_flush "
+                         "instead of the fused lq_gdn_decode_step_flush")
     ap.add_argument("--cpu-windows", type=int, default=128)
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (for PMC calibration)")
@@ -474,6 +502,8 @@ def main():
     if args.W:
         wl = wl.with_(W=args.W)
     L, W = args.layers, wl.W
+    assert W >= 2, "the benchmark step needs a window of at least 2 tokens"
+    fuse = not args.no_fuse
     d = lq.make_dims(wl.B, wl.H, wl.dk, wl.dv, W, wl.C,
                      lq.LQ_DECAY_PER_KEY if wl.per_key else lq.LQ_DECAY_SCALAR, wl.smooth)
     out = inputs.make_outliers(wl.seed, wl.H, wl.dk, wl.dv) if wl.outliers else None
@@ -497,14 +527,19 @@ def main():
     o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def step():
-        for n in range(W):
+    def step(fused=fuse):
+        for n in range(W - 1 if fused else W):
             for l in range(L):
                 tk = ring[l]
                 lq.lq_gdn_decode_step(layers[l], n, tk["q"][n], tk["k"][n], tk["v"][n],
                                       tk["alpha"][n], tk["beta"][n], o)
         for l in range(L):
-            lq.lq_gdn_window_flush(layers[l], W)
+            if fused:
+                tk, n = ring[l], W - 1
+                lq.lq_gdn_decode_step_flush(layers[l], n, tk["q"][n], tk["k"][n], tk["v"][n],
+                                            tk["alpha"][n], tk["beta"][n], o)
+            else:
+                lq.lq_gdn_window_flush(layers[l], W)
 
     for _ in range(args.warmup):
         step()
@@ -528,34 +563,53 @@ def main():
     # to the kernel's own execution interval (hipExtLaunchKernelGGL on the launch
     # stream), the interval rocprofv3's kernel trace reports.
     reps = max(2, min(8, args.steps))
-    dec_ms = [0.0] * W
+    ND = W - 1 if fuse else W          # decode launches per layer and step
+    dec_ms = [0.0] * ND
     fl_ms = 0.0
     for _ in range(reps):
         lq.lq_timing_enable(True)
         step()
         lq.lq_timing_enable(False)
-        fam, t_ms = lq.lq_timing_collect(W * L + L)
-        want = [lq.LQ_KERNEL_DECODE] * (W * L) + [lq.LQ_KERNEL_FLUSH] * L
+        fam, t_ms = lq.lq_timing_collect(ND * L + L)
+        want = [lq.LQ_KERNEL_DECODE] * (ND * L) + \
+            [lq.LQ_KERNEL_DECODE_FLUSH if fuse else lq.LQ_KERNEL_FLUSH] * L
         assert fam == want, "unexpected launch sequence"
-        for i in range(W * L):
+        for i in range(ND * L):
             dec_ms[i // L] += t_ms[i]
-        fl_ms += sum(t_ms[W * L:])
+        fl_ms += sum(t_ms[ND * L:])
     launches = reps * L
     dec_avg_us = [1e3 * x / launches for x in dec_ms]
-    dec_bytes = [decode_bytes(wl, n) for n in range(W)]
+    dec_bytes = [decode_bytes(wl, n) for n in range(ND)]
     dec_total_s = sum(dec_avg_us) * 1e-6
     dec_gbs = sum(dec_bytes) / dec_total_s / 1e9
     fl_avg_us = 1e3 * fl_ms / launches
-    fl_gbs = flush_bytes(wl, W) / (fl_avg_us * 1e-6) / 1e9
+    fl_alg = decode_flush_bytes(wl, W) if fuse else flush_bytes(wl, W)
+    fl_gbs = fl_alg / (fl_avg_us * 1e-6) / 1e9
     fl_tfs = flush_flops(wl, W) / (fl_avg_us * 1e-6) / 1e12
+    # the same step ending each window with a decode launch and a flush launch
+    two_call = None
+    if fuse and not args.no_compare:
+        k2 = max(4, min(16, args.steps))
+        step(False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(k2):
+            step(False)
+        e1.record()
+        torch.cuda.synchronize()
+        ms2 = e0.elapsed_time(e1) / k2
+        two_call = {"ms_per_step": round(ms2, 4), "tokens_per_s": round(tokens_per_step / (ms2 * 1e-3), 1),
+                    "speedup_fused": round(ms2 / ms, 3),
+                    "step": "last token by lq_gdn_decode_step, then lq_gdn_window_flush"}
 
     hsh = kernel_hash()
     traffic = read_traffic(wl, hsh)
     roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "lq_gdn_decode_step (decode_kernel<128,128,16,GDN>)",
-            "avg_launch_us": round(dec_total_s * 1e6 / W, 3),
-            "bytes_per_launch_avg": int(sum(dec_bytes) / W)}
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic if fuse else None,
+            "kernel": f"lq_gdn_decode_step (decode_kernel<128,128,16,GDN>, slots 0..{ND - 1})",
+            "avg_launch_us": round(dec_total_s * 1e6 / ND, 3),
+            "bytes_per_launch_avg": int(sum(dec_bytes) / ND)}
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -565,22 +619,26 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "dk": wl.dk, "dv": wl.dv, "W": W,
                    "C": wl.C, "decay": "per-key" if wl.per_key else "scalar",
                    "layers_rotated": L, "tokens_per_step": tokens_per_step,
-                   "step": f"{W} decode tokens + 1 flush for each of {L} layers",
+                   "step": (f"{W - 1} decode tokens + 1 fused last-token decode and flush"
+                            if fuse else f"{W} decode tokens + 1 flush") + f" for each of {L} layers",
                    "value_per": "tokens through one GDN layer per second",
                    "prefill": wl.prefill},
         "roofline": roof,
         "state_GBps": round(dec_gbs, 1),
-        "flush": {"avg_launch_us": round(fl_avg_us, 3), "hbm_GBps": round(fl_gbs, 1),
-                  "hbm_frac": round(fl_gbs / HBM_PEAK_GBS, 4), "mfma_f32_TFLOPs": round(fl_tfs, 2),
-                  "mfma_frac": round(fl_tfs / MFMA_F32_PEAK_TFS, 4)},
+        ("decode_flush" if fuse else "flush"): {
+            "avg_launch_us": round(fl_avg_us, 3), "algorithmic_bytes": fl_alg, "hbm_GBps": round(fl_gbs, 1),
+            "hbm_frac": round(fl_gbs / HBM_PEAK_GBS, 4), "mfma_f32_TFLOPs": round(fl_tfs, 2),
+            "mfma_frac": round(fl_tfs / MFMA_F32_PEAK_TFS, 4)},
         "decode_us_by_slot": [round(x, 3) for x in dec_avg_us],
         "kernel_hash": hsh,
     }
     if not args.no_compare:
         del layers
         torch.cuda.empty_cache()
-        res["comparisons"] = comparisons(wl, L, d, h_prefill, ring, value, dec_total_s * 1e6 / W,
+        res["comparisons"] = comparisons(wl, L, d, h_prefill, ring, value, dec_total_s * 1e6 / ND,
                                          max(4, min(16, args.steps)))
+        if two_call:
+            res["comparisons"]["two_call_window_end"] = two_call
     del h_prefill
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)

@@ -151,6 +151,26 @@ int lq_gdn_window_flush(const lq_dims *d, const lq_state *st, int32_t n_buffered
                         float *h_out, void *stream);
 
 /*
+ * lq_gdn_decode_step at position pos followed by lq_gdn_window_flush of
+ * pos + 1 slots, in one launch: the usual call for a window's last token
+ * (pos = W - 1; [news ¶3]: no update is skipped, and the state is rebuilt and
+ * requantized at the boundary).  Same arguments, layouts and effects as the
+ * two calls: writes o, buffer slot pos (k, g, m) and the requantized codec,
+ * and h_out (nullable) receives the fp32 H of the flush.  The result equals
+ * the two calls up to fp32 rounding in o, m_pos and H (the decode's
+ * projections Hb^T (exp(g_n) o x) are evaluated as (Gamma Hb)^T x from the
+ * flush's fp32 Gamma Hb instead of the int8 matrix cores); the requantized
+ * bytes follow the fp32 H written to h_out exactly as in the flush.
+ * The caller then restarts the window at pos 0.
+ * Errors: LQ_ERR_WINDOW_FULL if pos >= W, LQ_ERR_POS if pos < 0, plus those
+ * of the two calls.
+ */
+int lq_gdn_decode_step_flush(const lq_dims *d, const lq_state *st, int32_t pos,
+                             const float *q, const float *k, const float *v,
+                             const float *alpha, const float *beta, float *o, float *h_out,
+                             void *stream);
+
+/*
  * Ragged windows (sequences of a batch at different window positions, as in
  * serving).  Same as lq_gdn_decode_step, with the position of batch row b
  * read from the DEVICE array pos[b] (int32 [B], 4-byte aligned): every head
@@ -244,7 +264,8 @@ enum {
     LQ_KERNEL_QUANTIZE = 2,     /* lq_gdn_state_quantize */
     LQ_KERNEL_DEQUANTIZE = 3,   /* lq_gdn_state_dequantize */
     LQ_KERNEL_FP32_RECURRENCE = 4,
-    LQ_KERNEL_CHECKPOINT = 5    /* lq_gdn_state_pack / lq_gdn_state_unpack */
+    LQ_KERNEL_CHECKPOINT = 5,   /* lq_gdn_state_pack / lq_gdn_state_unpack */
+    LQ_KERNEL_DECODE_FLUSH = 6  /* lq_gdn_decode_step_flush */
 };
 
 /* on = 1: drop earlier records and start recording (at most 65536 launches;

@@ -297,9 +297,9 @@ struct FlushArgs {
     float* s;
     int32_t* idx;
     float* cv;
-    const float* bk;
-    const float* bm;
-    const float* bg;
+    float* bk;                // written only by the fused decode (slot N-1)
+    float* bm;
+    float* bg;
     float* h_out;
     const int32_t* n_dev;     // per batch row (ragged windows), or null: N for every row
     int W;
@@ -307,13 +307,21 @@ struct FlushArgs {
     int N;
     int smooth;
     int H;
+    // the token decoded into slot N-1 first (decode fused into the flush)
+    const float* q;
+    const float* k;
+    const float* v;
+    const float* alpha;
+    const float* beta;
+    float* o;
 };
 
 // Rows 0..NPAD-1 of a [rows][D] fp32 block (row index clamped to rmax) into
 // LDS dst[NPAD][D]; 16-byte pieces, one kilobyte per wave-wide copy, copies
-// spread over the NW waves.
+// spread over the NW waves.  Row rsub (if >= 0) comes from the vector sub.
 template <int NPAD, int D, int NW>
-__device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst, int w, int lane) {
+__device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst, int w, int lane,
+                                         int rsub = -1, const float* sub = nullptr) {
     constexpr int NCOPY = NPAD * D / 256;
     static_assert((NPAD * D) % 256 == 0, "block of whole copies");
 #pragma unroll
@@ -321,33 +329,44 @@ __device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst,
         const int cp = i * NW + w;
         if (cp < NCOPY) {
             const int e = cp * 256 + 4 * lane;
-            lds_dma16(src + (size_t)min(e / D, rmax) * D + e % D, dst + cp * 256);
+            const int row = min(e / D, rmax);
+            lds_dma16(row == rsub ? sub + e % D : src + (size_t)row * D + e % D, dst + cp * 256);
         }
     }
 }
 
 // Workgroup LDS of the flush kernel (byte offsets).
-template <int DK, int DV, int NPAD, bool KDA>
+template <int DK, int DV, int NPAD, bool KDA, bool DEC>
 struct FlushLds {
     static constexpr int RS = 0;                                   // r | s | cv rows
-    static constexpr int MISC = RS + (2 + CMAX) * DK * 4;          // idx
+    static constexpr int MISC = RS + (2 + CMAX) * DK * 4;          // idx; 8: beta, 9: alpha (scalar)
     static constexpr int GS = MISC + 64;                           // scalar log-decays
     static constexpr int MB = GS + 4 * 32;                         // buffered m rows
     static constexpr int KB = MB + NPAD * DV * 4;                  // buffered keys
     static constexpr int GB = KB + NPAD * DK * 4;                  // per-key log-decays
-    static constexpr int CODEC = GB + (KDA ? NPAD * DK * 4 : 0);   // codec stage
-    static constexpr int BYTES = CODEC + (int)sizeof(CodecLds<DK, DV, (DK / 16 < 4 ? DK / 16 : 4)>);
+    static constexpr int TOK = GB + (KDA ? NPAD * DK * 4 : 0);     // token q | v | alpha (DEC)
+    static constexpr int DOT = TOK + (DEC ? (2 * DK + DV) * 4 : 0);   // rr_i | a_i (DEC)
+    static constexpr int CODEC = DOT + (DEC ? 2 * NPAD * 4 : 0);   // codec stage; GEMV partials (DEC)
+    static constexpr int NWF = DK / 16 < 4 ? DK / 16 : 4;
+    static constexpr int BYTES = CODEC + (int)sizeof(CodecLds<DK, DV, NWF>);
+    static_assert(!DEC || 2 * NWF * DV * 4 <= (int)sizeof(CodecLds<DK, DV, NWF>), "GEMV partials");
 };
 
-template <int DK, int DV, int WM, bool KDA>
+// DEC = true: first decode one token into slot n = N-1 (the window's last
+// slot when N = W), then flush N slots, in one launch.  The decode's
+// projections Hb^T (e^{g_n} o x) (x = q, k; compensator rows included) are
+// (Gamma Hb)^T x with Gamma = diag e^{g_{N-1}}, i.e. GEMVs of the dequantized
+// Gamma Hb that the flush holds in registers before its window terms.  The
+// new slot's m_n then joins the window terms like any buffered slot.
+template <int DK, int DV, int WM, bool KDA, bool DEC>
 __global__ __launch_bounds__((FS<DK, DV>::NT))
 __attribute__((amdgpu_waves_per_eu(WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2), WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2))))
 void flush_kernel(FlushArgs a) {
     using S = FS<DK, DV>;
-    constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, RPL = S::RPL;
+    constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, RPL = S::RPL, NT = S::NT;
     constexpr int NPAD = WM <= 16 ? 16 : 32;   // slots padded to the MFMA size
     using RBy = RowBytes<RPL>;
-    using LY = FlushLds<DK, DV, NPAD, KDA>;
+    using LY = FlushLds<DK, DV, NPAD, KDA, DEC>;
     constexpr int KC = CMAX / 4;
 
     __shared__ __align__(16) char smem[LY::BYTES];
@@ -359,6 +378,13 @@ void flush_kernel(FlushArgs a) {
     float* s_M = reinterpret_cast<float*>(smem + LY::MB);          // [NPAD][DV]
     float* s_K = reinterpret_cast<float*>(smem + LY::KB);          // [NPAD][DK]
     float* s_G = reinterpret_cast<float*>(smem + LY::GB);          // [NPAD][DK] (per-key decay)
+    float* s_tq = reinterpret_cast<float*>(smem + LY::TOK);        // token q [DK] (DEC)
+    float* s_tv = s_tq + DK;                                       // token v [DV] (DEC)
+    float* s_tal = s_tv + DV;                                      // token alpha [DK] (DEC, per-key)
+    float* s_rr = reinterpret_cast<float*>(smem + LY::DOT);        // [NPAD] (DEC)
+    float* s_a = s_rr + NPAD;                                      // [NPAD] (DEC)
+    float* s_pq = reinterpret_cast<float*>(smem + LY::CODEC);      // [NW][DV] GEMV partials (DEC)
+    float* s_pk = s_pq + NW * DV;
     auto& L = *reinterpret_cast<CodecLds<DK, DV, NW>*>(smem + LY::CODEC);
 
     const int t = threadIdx.x;
@@ -368,6 +394,7 @@ void flush_kernel(FlushArgs a) {
     const int W = a.W, C = a.C;
     const int N = a.n_dev ? a.n_dev[head / (unsigned)a.H] : a.N;
     if (N <= 0 || N > W) return;                  // nothing buffered (or out of range): untouched
+    const int n = N - 1;                          // DEC: the decoded token's slot
 
     const int8_t* sq = a.sq + head * (DK * DV);
 
@@ -390,10 +417,34 @@ void flush_kernel(FlushArgs a) {
             }
             if (src) lds_dma16(src + 4 * (lane % SEGL), s_r + s0 * DK);
         }
-        if (w == 0 && lane < C) lds_dma4(a.idx + head * C + lane, s_idx);
+        if constexpr (DEC) {
+            // token q, v [, alpha]
+            constexpr int NTS = KDA ? 3 : 2;
+            for (int s0 = SPI * w; s0 < NTS; s0 += SPI * NW) {
+                const float* src = nullptr;
+#pragma unroll
+                for (int q = 0; q < SPI; ++q) {
+                    const int sg = s0 + q;
+                    const float* p = sg == 0 ? a.q + head * DK
+                                   : sg == 1 ? a.v + head * DV
+                                   : sg < NTS ? a.alpha + head * DK : nullptr;
+                    if (my == q) src = p;
+                }
+                if (src) lds_dma16(src + 4 * (lane % SEGL), s_tq + s0 * DK);
+            }
+        }
+        if (w == 0) {
+            const void* src4 = nullptr;
+            if (lane < C) src4 = a.idx + head * C + lane;
+            else if (DEC && lane == 8) src4 = a.beta + head;
+            else if (DEC && !KDA && lane == 9) src4 = a.alpha + head;
+            if (src4) lds_dma4(src4, s_idx);
+        }
         if (!KDA && w == NW - 1 && lane < NPAD) lds_dma4(a.bg + head * W + min(lane, W - 1), s_gs);
         dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, W - 1, s_M, w, lane);
-        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane);
+        // DEC: the token's key lands in row n
+        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane, DEC ? n : -1,
+                               DEC ? a.k + head * DK : nullptr);
         if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, W - 1, s_G, w, lane);
     }
     // D-layout bytes of the base state: column li*CT + ct, this lane's RPL rows
@@ -404,6 +455,61 @@ void flush_kernel(FlushArgs a) {
         hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + (size_t)(li * CT + ct) * DK + row0);
     all_loads_barrier();
 
+    // log-decay of the last slot, g_{N-1}[row]: from the buffer, or (DEC) the
+    // decoded token's g_n = g_{n-1} + log alpha
+    float gn_s = 0.0f;
+    if constexpr (DEC && !KDA) gn_s = (n > 0 ? s_gs[n - 1] : 0.0f) + logf(__int_as_float(s_idx[9]));
+    auto glast = [&](int row) -> float {
+        if constexpr (DEC)
+            return KDA ? (n > 0 ? s_G[(n - 1) * DK + row] : 0.0f) + logf(s_tal[row]) : gn_s;
+        else
+            return KDA ? s_G[(N - 1) * DK + row] : s_gs[N - 1];
+    };
+
+    // ---- DEC: slot dot products rr_i = <k, E_i o k_i>, a_i = <q, E_i o k_i> (i < n),
+    //      a_n = <q, k>; TPS lanes per slot ------------------------------------------------------------
+    if constexpr (DEC) {
+        constexpr int TPS = DK < 16 ? DK : 16, CH = DK / TPS, SPR = NT / TPS;
+        const int c0 = (t % TPS) * CH;
+        float kq[CH], kk[CH];
+        load_floats<CH>(s_tq + c0, kq);
+        load_floats<CH>(s_K + n * DK + c0, kk);
+        for (int sb = 0; sb <= n; sb += SPR) {
+            const int slot = sb + t / TPS;
+            float rr = 0.0f, aa = 0.0f;
+            if (slot < n) {
+                float ks[CH];
+                load_floats<CH>(s_K + slot * DK + c0, ks);
+                if constexpr (KDA) {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        const float x = ks[c] * __expf(glast(c0 + c) - s_G[slot * DK + c0 + c]);
+                        rr += kk[c] * x;
+                        aa += kq[c] * x;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        rr += kk[c] * ks[c];
+                        aa += kq[c] * ks[c];
+                    }
+                    const float e = __expf(gn_s - s_gs[slot]);
+                    rr *= e;
+                    aa *= e;
+                }
+            } else if (slot == n) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) aa += kq[c] * kk[c];
+            }
+            rr = group_sum<TPS>(rr);
+            aa = group_sum<TPS>(aa);
+            if ((t % TPS) == 0 && slot <= n) {
+                s_rr[slot] = rr;
+                s_a[slot] = aa;
+            }
+        }
+    }
+
     // ---- H = Gamma Hb + Kt^T M (fp32 MFMA, accumulating in place) -------------------------------
     // A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg (0 past N)
     float ka[RBW][NPAD / 4];
@@ -411,19 +517,20 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
             const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
-            const float gl = s_G[(N - 1) * DK + rowa];
+            const float gl = glast(rowa);
 #pragma unroll
             for (int ks = 0; ks < NPAD / 4; ++ks) {
                 const int slot = 4 * ks + lg;
-                ka[rb][ks] = slot < N ? __expf(gl - s_G[slot * DK + rowa]) * s_K[slot * DK + rowa] : 0.0f;
+                const float gsl = DEC && slot == n ? gl : s_G[slot * DK + rowa];
+                ka[rb][ks] = slot < N ? __expf(gl - gsl) * s_K[slot * DK + rowa] : 0.0f;
             }
         }
     } else {
-        const float gl = s_gs[N - 1];
+        const float gl = glast(0);
 #pragma unroll
         for (int ks = 0; ks < NPAD / 4; ++ks) {
             const int slot = 4 * ks + lg;
-            const float e = __expf(gl - s_gs[slot]);
+            const float e = __expf(gl - (DEC && slot == n ? gl : s_gs[slot]));
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
@@ -437,11 +544,10 @@ void flush_kernel(FlushArgs a) {
         load_floats<CT>(s_s + li * CT, sc);
         load_floats<RPL>(s_r + row0, rr);
         if constexpr (KDA) {
-            load_floats<RPL>(s_G + (N - 1) * DK + row0, gm);
 #pragma unroll
-            for (int k = 0; k < RPL; ++k) gm[k] = __expf(gm[k]);
+            for (int k = 0; k < RPL; ++k) gm[k] = __expf(glast(row0 + k));
         } else {
-            const float g = __expf(s_gs[N - 1]);
+            const float g = __expf(glast(0));
 #pragma unroll
             for (int k = 0; k < RPL; ++k) gm[k] = g;
         }
@@ -469,13 +575,76 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
-                const float g = KDA ? __expf(s_G[(N - 1) * DK + rowa]) : __expf(s_gs[N - 1]);
+                const float g = __expf(glast(rowa));
                 const float av = ic == rowa ? g : 0.0f;
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
                     H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bcv[ct], H[rb][ct], 0, 0, 0);
             }
         }
+
+    // ---- DEC: (Gamma Hb)^T q and (Gamma Hb)^T k, then m_n and the output --------------------------
+    if constexpr (DEC) {
+        float pq[CT], pk[CT];
+        {
+            float xq[RPL], xk[RPL];
+            load_floats<RPL>(s_tq + row0, xq);
+            load_floats<RPL>(s_K + n * DK + row0, xk);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                pq[ct] = 0.0f;
+                pk[ct] = 0.0f;
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        pq[ct] += H[rb][ct][v] * xq[rb * 4 + v];
+                        pk[ct] += H[rb][ct][v] * xk[rb * 4 + v];
+                    }
+            }
+        }
+        // sum over the four lane groups (the wave's row blocks), then over waves in LDS
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            pq[ct] += swz_xor16(pq[ct]);
+            pk[ct] += swz_xor16(pk[ct]);
+            pq[ct] += __shfl_xor(pq[ct], 32, 64);
+            pk[ct] += __shfl_xor(pk[ct], 32, 64);
+        }
+        if (lg == 0) {
+            store_floats<CT>(s_pq + w * DV + li * CT, pq);
+            store_floats<CT>(s_pk + w * DV + li * CT, pk);
+        }
+        lds_barrier();
+        if (t < DV) {
+            const int j = t;
+            float hq = 0.0f, hk = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                hq += s_pq[ww * DV + j];
+                hk += s_pk[ww * DV + j];
+            }
+            float sr = 0.0f, sa = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NPAD; ++i)
+                if (i < n) {
+                    const float mi = s_M[i * DV + j];
+                    sr += s_rr[i] * mi;
+                    sa += s_a[i] * mi;
+                }
+            const float mn = __int_as_float(s_idx[8]) * (s_tv[j] - hk - sr);
+            s_M[n * DV + j] = mn;
+            a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
+            a.o[head * DV + j] = hq + sa + s_a[n] * mn;
+        }
+        if (t < DK) {
+            a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = s_K[n * DK + t];
+            if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = glast(t);
+            else if (t == 0) a.bg[head * (size_t)W + n] = gn_s;
+        }
+        lds_barrier();
+    }
+
     // window terms: B = M rows (rows past N are zero; the buffer may hold
     // anything there)
 #pragma unroll
@@ -569,17 +738,26 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
     }
 }
 
-template <int DK, int WM, bool KDA>
+template <int DK, int WM, bool KDA, bool DEC>
 hipError_t flush_t(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
-    return launch_kernel(LQ_KERNEL_FLUSH, flush_kernel<DK, DK, WM, KDA>, dim3((unsigned)d.B * (unsigned)d.H),
-                         dim3(FS<DK, DK>::NT), s, args);
+    return launch_kernel(DEC ? LQ_KERNEL_DECODE_FLUSH : LQ_KERNEL_FLUSH, flush_kernel<DK, DK, WM, KDA, DEC>,
+                         dim3((unsigned)d.B * (unsigned)d.H), dim3(FS<DK, DK>::NT), s, args);
 }
 
-template <int DK>
+template <int DK, bool DEC>
 hipError_t flush_dk(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
     const bool kda = d.decay_mode == LQ_DECAY_PER_KEY;
-    if (d.W <= 16) return kda ? flush_t<DK, 16, true>(d, args, s) : flush_t<DK, 16, false>(d, args, s);
-    return kda ? flush_t<DK, 32, true>(d, args, s) : flush_t<DK, 32, false>(d, args, s);
+    if (d.W <= 16) return kda ? flush_t<DK, 16, true, DEC>(d, args, s) : flush_t<DK, 16, false, DEC>(d, args, s);
+    return kda ? flush_t<DK, 32, true, DEC>(d, args, s) : flush_t<DK, 32, false, DEC>(d, args, s);
+}
+
+template <bool DEC>
+hipError_t flush_any(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
+    switch (d.dk) {
+        case 16: return flush_dk<16, DEC>(d, args, s);
+        case 64: return flush_dk<64, DEC>(d, args, s);
+        default: return flush_dk<128, DEC>(d, args, s);
+    }
 }
 
 }  // namespace
@@ -587,12 +765,18 @@ hipError_t flush_dk(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
 hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, const int32_t* n_dev,
                         float* h_out, hipStream_t s) {
     FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
-                   st.buf_k, st.buf_m, st.buf_g, h_out, n_dev, d.W, d.C, n_buffered, d.smooth, d.H};
-    switch (d.dk) {
-        case 16: return flush_dk<16>(d, args, s);
-        case 64: return flush_dk<64>(d, args, s);
-        default: return flush_dk<128>(d, args, s);
-    }
+                   st.buf_k, st.buf_m, st.buf_g, h_out, n_dev, d.W, d.C, n_buffered, d.smooth, d.H,
+                   nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    return flush_any<false>(d, args, s);
+}
+
+hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, const float* q, const float* k,
+                               const float* v, const float* alpha, const float* beta, float* o, float* h_out,
+                               hipStream_t s) {
+    FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
+                   st.buf_k, st.buf_m, st.buf_g, h_out, nullptr, d.W, d.C, pos + 1, d.smooth, d.H,
+                   q, k, v, alpha, beta, o};
+    return flush_any<true>(d, args, s);
 }
 
 hipError_t launch_quantize(const lq_dims& d, const float* h, const lq_state& st, hipStream_t s) {

@@ -160,7 +160,9 @@ def prefill_state(wl: Workload, src: TokenSource, st: lq.LayerState, sample, chu
 
 
 def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smooth=None,
-               T=None, check_buffers=True, log_every=0) -> Report:
+               T=None, check_buffers=True, log_every=0, fused=False) -> Report:
+    """fused: each window's last token goes through lq_gdn_decode_step_flush
+    (decode + flush in one launch) instead of a decode step and a flush."""
     d = dims_of(wl, W, C, smooth)
     W, T = d.W, (T if T is not None else wl.T)
     src = TokenSource(wl, host_tokens)
@@ -175,12 +177,17 @@ def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smoot
         tk = src.tokens(wl.prefill + t, wl.prefill + t + N)
         outs = torch.empty((N, wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
         for n in range(N):
-            lq.lq_gdn_decode_step(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
-                                  tk["beta"][n], o)
+            args = (tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o)
+            if fused and n == N - 1:
+                lq.lq_gdn_decode_step_flush(st, n, *args, h_out=h_out)
+            else:
+                lq.lq_gdn_decode_step(st, n, *args)
             outs[n].copy_(o)
+        if not fused:
+            lq.lq_gdn_window_flush(st, N, h_out)
+        # the flush leaves the buffer as the decode steps wrote it
         bufs = ({k: getattr(st, "buf_" + k).clone() for k in ("k", "m", "g")}
                 if check_buffers else None)
-        lq.lq_gdn_window_flush(st, N, h_out)
         torch.cuda.synchronize()
         for (b, h) in sample:
             ht = {k: v[:, b, h].cpu().numpy() for k, v in tk.items()}

@@ -169,6 +169,21 @@ def test_ragged_argument_errors():
     assert fl(ct.byref(d), ct.byref(_fake_state(null="buf_k")), A, None) == lq.LQ_ERR_NULL
 
 
+def test_decode_flush_argument_errors():
+    L = lq.load()
+    d = _dims()
+    st = _fake_state()
+    call = lambda dd, s, pos, *p: L.lq_gdn_decode_step_flush(dd, s, pos, *p, None)
+    args = (A, A, A, A, A, A)
+    assert call(None, ct.byref(st), 0, *args, None) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), ct.byref(st), 16, *args, None) == lq.LQ_ERR_WINDOW_FULL
+    assert call(ct.byref(d), ct.byref(st), -1, *args, None) == lq.LQ_ERR_POS
+    assert call(ct.byref(d), ct.byref(st), 15, A, A, A, A, A, None, None) == lq.LQ_ERR_NULL   # o
+    assert call(ct.byref(d), ct.byref(st), 15, *args, B4) == lq.LQ_ERR_ALIGN                  # h_out
+    assert call(ct.byref(d), ct.byref(_fake_state(null="buf_m")), 15, *args, None) == lq.LQ_ERR_NULL
+    assert call(ct.byref(_dims(dk=96, dv=96)), ct.byref(st), 0, *args, None) == lq.LQ_ERR_UNSUPPORTED
+
+
 def test_checkpoint_sizes_and_errors():
     L = lq.load()
     d = _dims()                                   # B=2 H=3 d=128 C=4

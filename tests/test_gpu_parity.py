@@ -375,6 +375,78 @@ def test_ragged_windows(dk, per_key):
     assert not (o[0] == 5.0).all()
 
 
+# ---------------------------------------------------------------------------
+# fused last token: decode step + flush in one launch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,sample,T", [
+    ("tiny_gdn", [(0, 0)], None),
+    ("gdn_layer", [(0, h) for h in range(16)], 128),
+    ("gdn_batched", [(0, 0), (17, 5), (63, 31)], 64),
+    ("kda", [(0, 0), (31, 31)], 64),
+])
+def test_fused_decode_flush_presets(name, sample, T):
+    """Each window's last token through lq_gdn_decode_step_flush; same checks
+    as the two-call path (o_t, buffer rows incl. the fused slot, fp32 state,
+    codec bytes of that state), resynchronised to the oracle per window."""
+    wl = PRESETS[name]
+    _check(resync_run(wl, sample, host_tokens=wl.B * wl.H <= 16, T=T, fused=True), f"fused {name}")
+
+
+@pytest.mark.parametrize("dk,W,C,kda,smooth,T", [
+    (16, 4, 1, False, 1, 23),     # ragged last window: fused at pos 2 < W - 1
+    (16, 16, 0, True, 0, 40),
+    (64, 8, 8, True, 1, 21),
+    (64, 32, 3, False, 1, 70),
+    (128, 1, 0, False, 0, 7),     # W = 1: the fused call is the whole window
+    (128, 32, 8, True, 0, 33),
+    (128, 5, 2, False, 1, 12),
+])
+def test_fused_decode_flush_shapes(dk, W, C, kda, smooth, T):
+    wl = PRESETS["gdn_layer"].with_(B=2, H=3, dk=dk, dv=dk, W=W, C=C, T=T, prefill=40,
+                                    decay=1 if kda else 0, smooth=smooth, seed=91 + dk + W)
+    sample = [(b, h) for b in range(2) for h in range(3)]
+    _check(resync_run(wl, sample, host_tokens=True, fused=True),
+           f"fused shape dk={dk} W={W} C={C} kda={kda}")
+
+
+def test_fused_matches_two_calls():
+    """The fused call against lq_gdn_decode_step + lq_gdn_window_flush on the
+    same state and token (full gdn_batched size): o, the new buffer slot and
+    h_out agree to fp32 rounding; the earlier slots are left untouched."""
+    wl = PRESETS["gdn_batched"]
+    d = dims_of(wl)
+    say(f"fused vs two calls B={wl.B} H={wl.H}")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    st = lq.LayerState.allocate(d)
+    h0 = torch.randn((wl.B, wl.H, wl.dk, wl.dv), device="cuda", generator=g) * 0.3
+    lq.lq_gdn_state_quantize(st, h0)
+    tk = inputs.device_tokens(17, wl.W, wl.B, wl.H, wl.dk, wl.dv, per_key=False, beta_lo=0.1,
+                              beta_hi=0.9, device="cuda")
+    o = torch.empty((wl.B, wl.H, wl.dv), device="cuda")
+    for n in range(wl.W - 1):
+        lq.lq_gdn_decode_step(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o)
+    n = wl.W - 1
+    last = (tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n])
+    snap = {f: getattr(st, f).clone() for f in ("sq", "row_scale", "col_scale", "comp_idx", "comp_val",
+                                                 "buf_k", "buf_m", "buf_g")}
+    o2, h2 = torch.empty_like(o), torch.empty_like(h0)
+    lq.lq_gdn_decode_step(st, n, *last, o2)
+    lq.lq_gdn_window_flush(st, wl.W, h2)
+    bufs2 = {f: getattr(st, f).clone() for f in ("buf_k", "buf_m", "buf_g")}
+    for f, v in snap.items():
+        getattr(st, f).copy_(v)
+    o1, h1 = torch.empty_like(o), torch.empty_like(h0)
+    lq.lq_gdn_decode_step_flush(st, n, *last, o1, h_out=h1)
+    torch.cuda.synchronize()
+    assert rel_err(o1.cpu().numpy(), o2.cpu().numpy()) <= 1e-5
+    assert rel_err(h1.flatten(2).cpu().numpy(), h2.flatten(2).cpu().numpy()) <= 1e-5
+    for f in ("buf_k", "buf_g"):
+        assert torch.equal(getattr(st, f), bufs2[f]), f
+    assert torch.equal(st.buf_m[:, :, :n], bufs2["buf_m"][:, :, :n])
+    assert rel_err(st.buf_m[:, :, n].cpu().numpy(), bufs2["buf_m"][:, :, n].cpu().numpy()) <= 1e-5
+
+
 @pytest.mark.parametrize("dk,C", [(128, 4), (64, 1), (16, 0)])
 def test_checkpoint_round_trip(dk, C):
     """Pack writes each head's record in the documented layout; unpack
