@@ -345,19 +345,22 @@ struct FlushLds {
     static constexpr int KB = MB + NPAD * DV * 4;                  // buffered keys
     static constexpr int GB = KB + NPAD * DK * 4;                  // per-key log-decays
     static constexpr int TOK = GB + (KDA ? NPAD * DK * 4 : 0);     // token q | v | alpha (DEC)
-    static constexpr int DOT = TOK + (DEC ? (2 * DK + DV) * 4 : 0);   // rr_i | a_i (DEC)
-    static constexpr int CODEC = DOT + (DEC ? 2 * NPAD * 4 : 0);   // codec stage; GEMV partials (DEC)
+    static constexpr int CODEC = TOK + (DEC ? (2 * DK + DV) * 4 : 0);   // codec stage; GEMV partials (DEC)
     static constexpr int NWF = DK / 16 < 4 ? DK / 16 : 4;
     static constexpr int BYTES = CODEC + (int)sizeof(CodecLds<DK, DV, NWF>);
-    static_assert(!DEC || 2 * NWF * DV * 4 <= (int)sizeof(CodecLds<DK, DV, NWF>), "GEMV partials");
+    static_assert(!DEC || (2 * DV + 1) * NWF * 4 <= (int)sizeof(CodecLds<DK, DV, NWF>), "GEMV partials");
 };
 
 // DEC = true: first decode one token into slot n = N-1 (the window's last
-// slot when N = W), then flush N slots, in one launch.  The decode's
-// projections Hb^T (e^{g_n} o x) (x = q, k; compensator rows included) are
-// (Gamma Hb)^T x with Gamma = diag e^{g_{N-1}}, i.e. GEMVs of the dequantized
-// Gamma Hb that the flush holds in registers before its window terms.  The
-// new slot's m_n then joins the window terms like any buffered slot.
+// slot when N = W), then flush N slots, in one launch.  With Gamma =
+// diag e^{g_n}, the flush's registers after the window terms of slots i < n
+// hold H' = Gamma Hb + sum_{i<n} Kt_i m_i^T, and
+//     H'^T q = Hb^T (e^{g_n} o q) + sum_{i<n} a_i m_i,
+//     H'^T k = Hb^T (e^{g_n} o k) + sum_{i<n} rr_i m_i
+// (compensator rows included), the two sums of the decode step; so
+// m_n = beta (v - H'^T k), o = H'^T q + <q, k> m_n, and H = H' + k m_n^T.
+// The GEMVs run on the fp32 registers (fma, lane-group rows summed with the
+// row swaps, waves through LDS).
 template <int DK, int DV, int WM, bool KDA, bool DEC>
 __global__ __launch_bounds__((FS<DK, DV>::NT))
 __attribute__((amdgpu_waves_per_eu(WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2), WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2))))
@@ -381,9 +384,7 @@ void flush_kernel(FlushArgs a) {
     float* s_tq = reinterpret_cast<float*>(smem + LY::TOK);        // token q [DK] (DEC)
     float* s_tv = s_tq + DK;                                       // token v [DV] (DEC)
     float* s_tal = s_tv + DV;                                      // token alpha [DK] (DEC, per-key)
-    float* s_rr = reinterpret_cast<float*>(smem + LY::DOT);        // [NPAD] (DEC)
-    float* s_a = s_rr + NPAD;                                      // [NPAD] (DEC)
-    float* s_pq = reinterpret_cast<float*>(smem + LY::CODEC);      // [NW][DV] GEMV partials (DEC)
+    float* s_pq = reinterpret_cast<float*>(smem + LY::CODEC);      // [2][NW][DV] GEMV partials (DEC)
     float* s_pk = s_pq + NW * DV;
     auto& L = *reinterpret_cast<CodecLds<DK, DV, NW>*>(smem + LY::CODEC);
 
@@ -465,53 +466,20 @@ void flush_kernel(FlushArgs a) {
         else
             return KDA ? s_G[(N - 1) * DK + row] : s_gs[N - 1];
     };
-
-    // ---- DEC: slot dot products rr_i = <k, E_i o k_i>, a_i = <q, E_i o k_i> (i < n),
-    //      a_n = <q, k>; TPS lanes per slot ------------------------------------------------------------
     if constexpr (DEC) {
-        constexpr int TPS = DK < 16 ? DK : 16, CH = DK / TPS, SPR = NT / TPS;
-        const int c0 = (t % TPS) * CH;
-        float kq[CH], kk[CH];
-        load_floats<CH>(s_tq + c0, kq);
-        load_floats<CH>(s_K + n * DK + c0, kk);
-        for (int sb = 0; sb <= n; sb += SPR) {
-            const int slot = sb + t / TPS;
-            float rr = 0.0f, aa = 0.0f;
-            if (slot < n) {
-                float ks[CH];
-                load_floats<CH>(s_K + slot * DK + c0, ks);
-                if constexpr (KDA) {
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) {
-                        const float x = ks[c] * __expf(glast(c0 + c) - s_G[slot * DK + c0 + c]);
-                        rr += kk[c] * x;
-                        aa += kq[c] * x;
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) {
-                        rr += kk[c] * ks[c];
-                        aa += kq[c] * ks[c];
-                    }
-                    const float e = __expf(gn_s - s_gs[slot]);
-                    rr *= e;
-                    aa *= e;
-                }
-            } else if (slot == n) {
-#pragma unroll
-                for (int c = 0; c < CH; ++c) aa += kq[c] * kk[c];
-            }
-            rr = group_sum<TPS>(rr);
-            aa = group_sum<TPS>(aa);
-            if ((t % TPS) == 0 && slot <= n) {
-                s_rr[slot] = rr;
-                s_a[slot] = aa;
-            }
+        // slot n's key and log-decay
+        if (t < DK) {
+            a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = s_K[n * DK + t];
+            if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = glast(t);
+            else if (t == 0) a.bg[head * (size_t)W + n] = gn_s;
         }
     }
 
     // ---- H = Gamma Hb + Kt^T M (fp32 MFMA, accumulating in place) -------------------------------
-    // A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg (0 past N)
+    // A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg (0 from NM on).
+    // DEC: the MFMA terms cover slots < n; slot n (Kt row = k, its m from the decode) is a
+    // rank-1 update afterwards.
+    const int NM = DEC ? n : N;
     float ka[RBW][NPAD / 4];
     if constexpr (KDA) {
 #pragma unroll
@@ -521,8 +489,7 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
             for (int ks = 0; ks < NPAD / 4; ++ks) {
                 const int slot = 4 * ks + lg;
-                const float gsl = DEC && slot == n ? gl : s_G[slot * DK + rowa];
-                ka[rb][ks] = slot < N ? __expf(gl - gsl) * s_K[slot * DK + rowa] : 0.0f;
+                ka[rb][ks] = slot < NM ? __expf(gl - s_G[slot * DK + rowa]) * s_K[slot * DK + rowa] : 0.0f;
             }
         }
     } else {
@@ -530,11 +497,11 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NPAD / 4; ++ks) {
             const int slot = 4 * ks + lg;
-            const float e = __expf(gl - (DEC && slot == n ? gl : s_gs[slot]));
+            const float e = __expf(gl - s_gs[slot]);
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
-                ka[rb][ks] = slot < N ? e * s_K[slot * DK + rowa] : 0.0f;
+                ka[rb][ks] = slot < NM ? e * s_K[slot * DK + rowa] : 0.0f;
             }
         }
     }
@@ -583,74 +550,12 @@ void flush_kernel(FlushArgs a) {
             }
         }
 
-    // ---- DEC: (Gamma Hb)^T q and (Gamma Hb)^T k, then m_n and the output --------------------------
-    if constexpr (DEC) {
-        float pq[CT], pk[CT];
-        {
-            float xq[RPL], xk[RPL];
-            load_floats<RPL>(s_tq + row0, xq);
-            load_floats<RPL>(s_K + n * DK + row0, xk);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                pq[ct] = 0.0f;
-                pk[ct] = 0.0f;
-#pragma unroll
-                for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        pq[ct] += H[rb][ct][v] * xq[rb * 4 + v];
-                        pk[ct] += H[rb][ct][v] * xk[rb * 4 + v];
-                    }
-            }
-        }
-        // sum over the four lane groups (the wave's row blocks), then over waves in LDS
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            pq[ct] += swz_xor16(pq[ct]);
-            pk[ct] += swz_xor16(pk[ct]);
-            pq[ct] += __shfl_xor(pq[ct], 32, 64);
-            pk[ct] += __shfl_xor(pk[ct], 32, 64);
-        }
-        if (lg == 0) {
-            store_floats<CT>(s_pq + w * DV + li * CT, pq);
-            store_floats<CT>(s_pk + w * DV + li * CT, pk);
-        }
-        lds_barrier();
-        if (t < DV) {
-            const int j = t;
-            float hq = 0.0f, hk = 0.0f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                hq += s_pq[ww * DV + j];
-                hk += s_pk[ww * DV + j];
-            }
-            float sr = 0.0f, sa = 0.0f;
-#pragma unroll
-            for (int i = 0; i < NPAD; ++i)
-                if (i < n) {
-                    const float mi = s_M[i * DV + j];
-                    sr += s_rr[i] * mi;
-                    sa += s_a[i] * mi;
-                }
-            const float mn = __int_as_float(s_idx[8]) * (s_tv[j] - hk - sr);
-            s_M[n * DV + j] = mn;
-            a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
-            a.o[head * DV + j] = hq + sa + s_a[n] * mn;
-        }
-        if (t < DK) {
-            a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = s_K[n * DK + t];
-            if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = glast(t);
-            else if (t == 0) a.bg[head * (size_t)W + n] = gn_s;
-        }
-        lds_barrier();
-    }
-
-    // window terms: B = M rows (rows past N are zero; the buffer may hold
+    // window terms: B = M rows (rows from NM on are zero; the buffer may hold
     // anything there)
 #pragma unroll
     for (int ks = 0; ks < NPAD / 4; ++ks) {
-        if (4 * ks < N) {
-            const bool live = 4 * ks + lg < N;
+        if (4 * ks < NM) {
+            const bool live = 4 * ks + lg < NM;
             float bm[CT];
             load_floats<CT>(&s_M[(4 * ks + lg) * DV + li * CT], bm);
 #pragma unroll
@@ -660,6 +565,75 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
                     H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[rb][ks], bm[ct], H[rb][ct], 0, 0, 0);
+        }
+    }
+
+    // ---- DEC: the token of slot n.  H now holds Gamma Hb + sum_{i<n} Kt_i m_i^T, so
+    //      H^T q = Hb^T (e^{g_n} o q) + sum_{i<n} a_i m_i and H^T k likewise with rr_i:
+    //      m_n = beta (v - H^T k), o = H^T q + <q, k> m_n, then H += k m_n^T ------------------
+    if constexpr (DEC) {
+        float* s_an = s_pk + NW * DV;                              // [NW] partial <q, k>
+        {
+            float an = t < DK ? s_tq[t] * s_K[n * DK + t] : 0.0f;
+            an = group_sum<64>(an);
+            if (lane == 0) s_an[w] = an;
+        }
+        // x = q, then k: column partials over this lane's rows, totals over the
+        // wave's four lane-group rows, then over the waves in LDS
+#pragma unroll
+        for (int vec = 0; vec < 2; ++vec) {
+            float x[RPL], p[CT];
+            load_floats<RPL>((vec ? s_K + n * DK : s_tq) + row0, x);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                p[ct] = 0.0f;
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) p[ct] = __builtin_fmaf(H[rb][ct][v], x[rb * 4 + v], p[ct]);
+            }
+            float* dst = s_pq + vec * NW * DV + w * DV + li * CT;
+            if constexpr (CT % 4 == 0) {
+                // row r of rows_sum4's result: the total of column 4m + r
+#pragma unroll
+                for (int m = 0; m < CT / 4; ++m)
+                    dst[4 * m + lg] = rows_sum4(p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]);
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    p[ct] += swz_xor16(p[ct]);
+                    p[ct] += __shfl_xor(p[ct], 32, 64);
+                }
+                if (lg == 0) store_floats<CT>(dst, p);
+            }
+        }
+        lds_barrier();
+        if (t < DV) {
+            const int j = t;
+            float hq = 0.0f, hk = 0.0f, aq = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                hq += s_pq[ww * DV + j];
+                hk += s_pk[ww * DV + j];
+                aq += s_an[ww];
+            }
+            const float mn = __int_as_float(s_idx[8]) * (s_tv[j] - hk);
+            s_M[n * DV + j] = mn;
+            a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
+            a.o[head * DV + j] = hq + aq * mn;
+        }
+        lds_barrier();
+        {
+            float xk[RPL], mv[CT];
+            load_floats<RPL>(s_K + n * DK + row0, xk);
+            load_floats<CT>(s_M + n * DV + li * CT, mv);
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        H[rb][ct][v] = __builtin_fmaf(xk[rb * 4 + v], mv[ct], H[rb][ct][v]);
         }
     }
 

@@ -109,6 +109,21 @@ __device__ __forceinline__ float swz_xor16(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
 }
 
+// Totals over the four 16-lane rows of a wave for four values at once, with
+// the gfx950 row swaps (v_permlane32_swap: upper half of the first operand
+// <-> lower half of the second; v_permlane16_swap: odd rows of the first <->
+// even rows of the second).  Row r of the result holds the sum over all 64
+// lanes' rows of (a, b, c, d)[r], at the lane's position within the row.
+__device__ __forceinline__ float rows_sum4(float a, float b, float c, float d) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(c), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(b), __float_as_uint(d), false, false);
+    // rows of x: a0+a2, a1+a3, c0+c2, c1+c3; of y: the same for b and d
+    const float x = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
+    const float y = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+}
+
 // Sum / max over aligned groups of G lanes (G a power of two <= 64); every
 // lane of a group receives the result.  After the two quad steps all lanes
 // of a quad agree, so the mirror steps pair whole quads, then whole halves.
