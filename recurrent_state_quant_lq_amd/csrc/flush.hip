@@ -114,7 +114,10 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                             float* __restrict__ h_out, int C, int smooth) {
     constexpr int RPL = FS<DK, DV>::RPL;
     constexpr int NT = 64 * NW;
-    const int t = threadIdx.x;
+    // the lane indices are recomputed here (an opaque copy of the thread id), so
+    // the compiler keeps no codec address live through the caller's registers
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
     const int lane = t & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int row0 = row_of<DK, DV>(w, lg, 0, 0);
@@ -582,15 +585,17 @@ void flush_kernel(FlushArgs a) {
         // wave's four lane-group rows, then over the waves in LDS
 #pragma unroll
         for (int vec = 0; vec < 2; ++vec) {
-            float x[RPL], p[CT];
-            load_floats<RPL>((vec ? s_K + n * DK : s_tq) + row0, x);
+            float p[CT];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                p[ct] = 0.0f;
+            for (int ct = 0; ct < CT; ++ct) p[ct] = 0.0f;
 #pragma unroll
-                for (int rb = 0; rb < RBW; ++rb)
+            for (int rb = 0; rb < RBW; ++rb) {
+                float x[4];
+                load_floats<4>((vec ? s_K + n * DK : s_tq) + row0 + 4 * rb, x);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) p[ct] = __builtin_fmaf(H[rb][ct][v], x[rb * 4 + v], p[ct]);
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) p[ct] = __builtin_fmaf(H[rb][ct][v], x[v], p[ct]);
             }
             float* dst = s_pq + vec * NW * DV + w * DV + li * CT;
             if constexpr (CT % 4 == 0) {
@@ -624,16 +629,17 @@ void flush_kernel(FlushArgs a) {
         }
         lds_barrier();
         {
-            float xk[RPL], mv[CT];
-            load_floats<RPL>(s_K + n * DK + row0, xk);
+            float mv[CT];
             load_floats<CT>(s_M + n * DV + li * CT, mv);
 #pragma unroll
-            for (int rb = 0; rb < RBW; ++rb)
+            for (int rb = 0; rb < RBW; ++rb) {
+                float xk[4];
+                load_floats<4>(s_K + n * DK + row0 + 4 * rb, xk);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        H[rb][ct][v] = __builtin_fmaf(xk[rb * 4 + v], mv[ct], H[rb][ct][v]);
+                    for (int v = 0; v < 4; ++v) H[rb][ct][v] = __builtin_fmaf(xk[v], mv[ct], H[rb][ct][v]);
+            }
         }
     }
 
