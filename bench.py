@@ -10,8 +10,8 @@ independent GDN layers (default 8, the
 layers' states rotated so that the working set, about 720 MB at
 B=64 H=32 d=128, exceeds the 256 MB Infinity Cache and every step reads HBM).
 Inputs are synthetic, drawn on the device before timing; the starting state
-comes from a 512-token fp32 prefill run by the library's fp32 recurrence and
-quantized by its quantizer.
+comes from a 512-token prefill run by the library's chunked fp32 prefill
+(lq_gdn_prefill), quantized once.
 
 Printed (one JSON line): tokens/s through one layer (B * W * L tokens per
 step), the decode kernel's roofline (algorithmic bytes over its per-launch
@@ -270,7 +270,7 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
     (W = 1, no compensators, no smoothing), plus the output error of both int8
     schemes against the fp32 recurrence on a sample of heads."""
     import torch
-    from recurrent_state_quant_lq_amd import lq
+    from recurrent_state_quant_lq_amd import inputs, lq
     W = wl.W
     B, H, dk, dv = wl.B, wl.H, wl.dk, wl.dv
     o = torch.empty((B, H, dv), dtype=torch.float32, device=h0.device)
@@ -370,6 +370,24 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
                          "pack_hbm_GBps": round(2 * nb / (pk * 1e-6) / 1e9, 1),
                          "unpack_hbm_GBps": round(2 * nb / (uk * 1e-6) / 1e9, 1)}
     del stc, blob
+    # (f2) prefill of a 128-token prompt chunk: chunked fp32 form (lq_gdn_prefill,
+    # without its final quantization) against the token-by-token fp32 recurrence
+    Tp = 128
+    tp = inputs.device_tokens(wl.seed * 31, Tp, B, H, dk, dv, per_key=wl.per_key, beta_lo=wl.beta_lo,
+                              beta_hi=wl.beta_hi, device=h0.device)
+    hp = h0.clone()
+    op = torch.empty((Tp, B, H, dv), dtype=torch.float32, device=h0.device)
+    args = (tp["q"], tp["k"], tp["v"], tp["alpha"], tp["beta"], op)
+    chunked = kernel_us(lambda: [lq.lq_gdn_prefill(d, None, hp, Tp, *args) for _ in range(3)],
+                        lq.LQ_KERNEL_PREFILL)
+    rec = kernel_us(lambda: [lq.lq_gdn_fp32_recurrence(d, hp, Tp, *args) for _ in range(3)],
+                    lq.LQ_KERNEL_FP32_RECURRENCE)
+    out["prefill"] = {"tokens": Tp, "chunked_us": round(chunked, 2), "fp32_recurrence_us": round(rec, 2),
+                      "chunked_tokens_per_s": round(B * Tp / (chunked * 1e-6), 1),
+                      "speedup_chunked": round(rec / chunked, 3),
+                      "note": "with outputs; the state stays fp32 (the prompt's final quantization "
+                              "is one lq_gdn_state_quantize launch)"}
+    del hp, op, tp
     out["fidelity"] = fidelity(wl, d, h0)
     return out
 
@@ -511,16 +529,20 @@ def main():
                                                beta_lo=wl.beta_lo, beta_hi=wl.beta_hi, device=dev,
                                                outliers=out)
 
-    # starting state: fp32 prefill on the device, quantized, copied into L layers
+    # starting state: chunked fp32 prefill on the device, quantized once, copied into L layers
     h = torch.zeros((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    layers = [lq.LayerState.allocate(d, dev) for _ in range(L)]
     for c0 in range(0, wl.prefill, 128):
         T = min(128, wl.prefill - c0)
         tk = gen(wl.seed * 100 + c0, T)
-        lq.lq_gdn_fp32_recurrence(d, h, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"])
+        lq.lq_gdn_prefill(d, layers[0] if c0 + T == wl.prefill else None, h, T, tk["q"], tk["k"], tk["v"],
+                          tk["alpha"], tk["beta"])
         del tk
-    layers = [lq.LayerState.allocate(d, dev) for _ in range(L)]
-    for st in layers:
-        lq.lq_gdn_state_quantize(st, h)
+    if wl.prefill == 0:
+        lq.lq_gdn_prefill(d, layers[0], h, 0, None, None, None, None, None)
+    for st in layers[1:]:
+        for f in ("sq", "row_scale", "col_scale", "comp_idx", "comp_val"):
+            getattr(st, f).copy_(getattr(layers[0], f))
     h_prefill = h
     # input ring: W tokens per layer
     ring = [gen(wl.seed * 7 + l, W) for l in range(L)]

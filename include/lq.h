@@ -235,6 +235,30 @@ int lq_gdn_fp32_recurrence(const lq_dims *d, float *h, int32_t T,
                            const float *q, const float *k, const float *v,
                            const float *alpha, const float *beta, float *o, void *stream);
 
+/*
+ * Prefill of a prompt: the state after T tokens, computed in fp32 in chunks
+ * of 16 tokens (the chunk form of the same recurrence: within a chunk the
+ * updates are combined in WY form and applied with fp32 matrix-core
+ * products), then quantized once into st's codec (steps 1-3 of
+ * lq_gdn_window_flush).  [abstract]: decoding reads the low-bit state;
+ * [news ¶3]: it is quantized once per window, not per token, so the prompt
+ * runs in fp32 and only its final state is quantized.
+ *   h      fp32 [B,H,dk,dv] (row-major), in: the state before the prompt
+ *          (zeros for a new sequence), out: the state after it;
+ *   q..beta as lq_gdn_fp32_recurrence, [T,B,H,...];
+ *   o      nullable fp32 [T,B,H,dv]: every prompt token's output;
+ *   st     nullable: codec arrays written (buffers untouched); NULL leaves
+ *          the state in fp32 only.
+ * T = 0 only quantizes h.  The results equal lq_gdn_fp32_recurrence followed
+ * by lq_gdn_state_quantize up to fp32 rounding in h and o; the codec bytes
+ * are those of the fp32 h written.
+ * Errors: LQ_ERR_POS if T < 0; LQ_ERR_NULL / LQ_ERR_ALIGN for h and the
+ * token arrays.
+ */
+int lq_gdn_prefill(const lq_dims *d, const lq_state *st, float *h, int32_t T,
+                   const float *q, const float *k, const float *v,
+                   const float *alpha, const float *beta, float *o, void *stream);
+
 /* Bytes of one layer's codec arrays (sq, scales, compensators), i.e.
  * B*H*(dk*dv + 4dk + 4dv + C*(4dv + 4)); 0 if d is NULL or invalid. */
 size_t lq_state_bytes(const lq_dims *d);
@@ -265,7 +289,8 @@ enum {
     LQ_KERNEL_DEQUANTIZE = 3,   /* lq_gdn_state_dequantize */
     LQ_KERNEL_FP32_RECURRENCE = 4,
     LQ_KERNEL_CHECKPOINT = 5,   /* lq_gdn_state_pack / lq_gdn_state_unpack */
-    LQ_KERNEL_DECODE_FLUSH = 6  /* lq_gdn_decode_step_flush */
+    LQ_KERNEL_DECODE_FLUSH = 6, /* lq_gdn_decode_step_flush */
+    LQ_KERNEL_PREFILL = 7       /* lq_gdn_prefill (its quantization: LQ_KERNEL_QUANTIZE) */
 };
 
 /* on = 1: drop earlier records and start recording (at most 65536 launches;

@@ -229,6 +229,20 @@ int lq_gdn_fp32_recurrence(const lq_dims* d, float* h, int32_t T, const float* q
     return finish(lq::launch_fp32_recurrence(*d, h, T, q, k, v, alpha, beta, o, (hipStream_t)stream));
 }
 
+int lq_gdn_prefill(const lq_dims* d, const lq_state* st, float* h, int32_t T, const float* q,
+                   const float* k, const float* v, const float* alpha, const float* beta, float* o,
+                   void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if (st && (rc = check_state(d, st, false))) return rc;
+    if ((rc = check_ptrs({h}))) return rc;
+    if (T < 0) return LQ_ERR_POS;
+    if (T > 0 && (rc = check_tokens(d, q, k, v, alpha, beta, o, false))) return rc;
+    const hipStream_t s = (hipStream_t)stream;
+    if (T > 0 && (rc = finish(lq::launch_prefill(*d, h, T, q, k, v, alpha, beta, o, s)))) return rc;
+    return st ? finish(lq::launch_quantize(*d, h, *st, s)) : LQ_OK;
+}
+
 size_t lq_checkpoint_bytes(const lq_dims* d) {
     if (check_dims(d) != LQ_OK) return 0;
     return (size_t)d->B * d->H * lq::checkpoint_head_bytes(*d);

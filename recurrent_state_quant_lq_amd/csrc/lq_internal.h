@@ -26,6 +26,9 @@ hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* h_out,
 // Quantized-state records (lq_gdn_state_pack / unpack).
 size_t checkpoint_head_bytes(const lq_dims& d);
 hipError_t launch_checkpoint(const lq_dims& d, const lq_state& st, void* blob, bool pack, hipStream_t s);
+// Chunked fp32 prefill of T tokens, state h updated in place (lq_gdn_prefill).
+hipError_t launch_prefill(const lq_dims& d, float* h, int T, const float* q, const float* k, const float* v,
+                          const float* alpha, const float* beta, float* o, hipStream_t s);
 hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const float* q,
                                   const float* k, const float* v, const float* alpha,
                                   const float* beta, float* o, hipStream_t s);

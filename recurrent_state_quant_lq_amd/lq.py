@@ -28,9 +28,10 @@ EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_ragg
            "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_state_bytes",
            "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims",
            "lq_timing_enable", "lq_timing_collect", "lq_checkpoint_bytes", "lq_gdn_state_pack",
-           "lq_gdn_state_unpack", "lq_gdn_decode_step_flush")
+           "lq_gdn_state_unpack", "lq_gdn_decode_step_flush", "lq_gdn_prefill")
 LQ_KERNEL_DECODE, LQ_KERNEL_FLUSH, LQ_KERNEL_QUANTIZE, LQ_KERNEL_DEQUANTIZE, \
-    LQ_KERNEL_FP32_RECURRENCE, LQ_KERNEL_CHECKPOINT, LQ_KERNEL_DECODE_FLUSH = range(7)
+    LQ_KERNEL_FP32_RECURRENCE, LQ_KERNEL_CHECKPOINT, LQ_KERNEL_DECODE_FLUSH, \
+    LQ_KERNEL_PREFILL = range(8)
 
 
 class lq_dims(ct.Structure):
@@ -65,12 +66,13 @@ def load() -> ct.CDLL:
         L.lq_gdn_decode_step.argtypes = [D, S, I, P, P, P, P, P, P, P]
         L.lq_gdn_window_flush.argtypes = [D, S, I, P, P]
         L.lq_gdn_decode_step_flush.argtypes = [D, S, I, P, P, P, P, P, P, P, P]
+        L.lq_gdn_prefill.argtypes = [D, S, P, I, P, P, P, P, P, P, P]
         L.lq_gdn_decode_step_ragged.argtypes = [D, S, P, P, P, P, P, P, P, P]
         L.lq_gdn_window_flush_ragged.argtypes = [D, S, P, P, P]
         L.lq_gdn_state_quantize.argtypes = [D, P, S, P]
         L.lq_gdn_state_dequantize.argtypes = [D, S, P, P]
         L.lq_gdn_fp32_recurrence.argtypes = [D, P, I, P, P, P, P, P, P, P]
-        for f in ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_flush",
+        for f in ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_flush", "lq_gdn_prefill",
                   "lq_gdn_decode_step_ragged",
                   "lq_gdn_window_flush_ragged", "lq_gdn_state_quantize",
                   "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_check_dims",
@@ -298,6 +300,26 @@ def lq_gdn_fp32_recurrence(d: lq_dims, h, T: int, q, k, v, alpha, beta, o=None, 
     rc = load().lq_gdn_fp32_recurrence(ct.byref(d), _ptr(h), int(T), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
     _raise("lq_gdn_fp32_recurrence", rc)
+
+
+def lq_gdn_prefill(d: lq_dims, st, h, T: int, q, k, v, alpha, beta, o=None, stream=None):
+    """Chunked fp32 prefill of T tokens (h in/out), then the codec of the final
+    state into st (a LayerState, or None for the fp32 state only)."""
+    _check(h, "h", (d.B, d.H, d.dk, d.dv), torch.float32)
+    sh = _token_shapes(d, T)
+    if T > 0:
+        for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+            _check(t, name, sh[name], torch.float32)
+    if o is not None:
+        _check(o, "o", sh["o"], torch.float32)
+    cs = None
+    if st is not None:
+        st.check(with_buffer=False)
+        cs = st.c_state()
+    rc = load().lq_gdn_prefill(ct.byref(d), ct.byref(cs) if cs is not None else None, _ptr(h), int(T),
+                               _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
+                               _stream(stream))
+    _raise("lq_gdn_prefill", rc)
 
 
 def lq_checkpoint_bytes(d: lq_dims) -> int:

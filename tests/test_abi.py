@@ -184,6 +184,23 @@ def test_decode_flush_argument_errors():
     assert call(ct.byref(_dims(dk=96, dv=96)), ct.byref(st), 0, *args, None) == lq.LQ_ERR_UNSUPPORTED
 
 
+def test_prefill_argument_errors():
+    L = lq.load()
+    d = _dims()
+    st = _fake_state()
+    call = lambda dd, s, h, T, *p: L.lq_gdn_prefill(dd, s, h, T, *p, None)
+    args = (A, A, A, A, A, None)
+    assert call(None, ct.byref(st), A, 4, *args) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), ct.byref(st), None, 4, *args) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), ct.byref(st), B4, 4, *args) == lq.LQ_ERR_ALIGN
+    assert call(ct.byref(d), ct.byref(st), A, -1, *args) == lq.LQ_ERR_POS
+    assert call(ct.byref(d), ct.byref(st), A, 4, A, None, A, A, A, None) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), ct.byref(st), A, 4, A, A, A, A, A, B4) == lq.LQ_ERR_ALIGN          # o
+    assert call(ct.byref(d), ct.byref(_fake_state(null="sq")), A, 4, *args) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), None, A, 0, *args) == lq.LQ_OK             # nothing to do
+    assert call(ct.byref(_dims(dk=96, dv=96)), ct.byref(st), A, 4, *args) == lq.LQ_ERR_UNSUPPORTED
+
+
 def test_checkpoint_sizes_and_errors():
     L = lq.load()
     d = _dims()                                   # B=2 H=3 d=128 C=4

@@ -185,6 +185,85 @@ def test_fp32_recurrence_kernel(dk, kda):
 
 
 # ---------------------------------------------------------------------------
+# chunked prefill
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,kda,T,zero", [
+    (16, False, 1, True),       # one token, a chunk of one
+    (16, True, 23, False),      # a full chunk and a ragged tail
+    (64, False, 40, False),
+    (64, True, 16, True),       # exactly one chunk
+    (128, False, 77, False),
+    (128, True, 50, False),
+])
+def test_prefill_kernel(dk, kda, T, zero):
+    """lq_gdn_prefill against the oracle's fp64 recurrence from the same
+    starting state: every output, the final fp32 state, and the codec bytes
+    against the oracle's codec of that fp32 state (bit-exact)."""
+    B, H, C = 2, 3, 4
+    say(f"prefill dk={dk} kda={kda} T={T}")
+    tok = inputs.host_tokens(57 + dk + T, T, B, H, dk, dk, per_key=kda, beta_lo=0.0, beta_hi=1.0)
+    d = lq.make_dims(B, H, dk, dk, 16, C, int(kda), 1)
+    rng = np.random.default_rng(dk + T)
+    H0 = np.zeros((B, H, dk, dk), np.float32) if zero else \
+        (rng.standard_normal((B, H, dk, dk)) * 0.3).astype(np.float32)
+    h = torch.from_numpy(H0).cuda()
+    o = torch.empty((T, B, H, dk), dtype=torch.float32, device="cuda")
+    tk = {k: torch.from_numpy(v).cuda() for k, v in tok.items()}
+    st = lq.LayerState.allocate(d)
+    lq.lq_gdn_prefill(d, st, h, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], o)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for hh in range(H):
+            ht = O.head_tokens(tok, b, hh)
+            o_ref, _, H_ref, _ = O.run_head(dk, dk, kda, T, 0, 1, route=0, use_codec=False, tok=ht,
+                                            H0=H0[b, hh].astype(np.float64))
+            assert rel_err(o[:, b, hh].cpu().numpy(), o_ref) < 2e-5, (b, hh)
+            hg = h[b, hh].cpu().numpy()
+            assert np.abs(hg - H_ref).max() / max(np.abs(H_ref).max(), 1e-30) < 2e-5, (b, hh)
+            assert codec_equal(head_codec(st, b, hh), O.quantize(hg, C, 1)), ("codec", b, hh)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_prefill_matches_fp32_recurrence_full_size(kda):
+    """At the benchmark's shape (B=64 H=32 d=128, or B=32 per-key) and a
+    512-token prompt in 128-token calls: the chunked prefill against the
+    token-by-token fp32 recurrence kernel, outputs and final state to fp32
+    rounding, and against the oracle on sampled heads."""
+    wl = PRESETS["kda" if kda else "gdn_batched"]
+    B, H, dk = wl.B, wl.H, wl.dk
+    d = dims_of(wl)
+    say(f"prefill full size kda={kda} B={B} H={H}")
+    h1 = torch.zeros((B, H, dk, dk), device="cuda")
+    h2 = torch.zeros_like(h1)
+    st = lq.LayerState.allocate(d)
+    T, chunk = 512, 128
+    worst_o = 0.0
+    for c0 in range(0, T, chunk):
+        tk = inputs.device_tokens(wl.seed * 100 + c0, chunk, B, H, dk, dk, per_key=kda, beta_lo=0.1,
+                                  beta_hi=0.9, device="cuda")
+        o1 = torch.empty((chunk, B, H, dk), device="cuda")
+        o2 = torch.empty_like(o1)
+        lq.lq_gdn_prefill(d, st if c0 + chunk == T else None, h1, chunk, tk["q"], tk["k"], tk["v"],
+                          tk["alpha"], tk["beta"], o1)
+        lq.lq_gdn_fp32_recurrence(d, h2, chunk, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], o2)
+        torch.cuda.synchronize()
+        # per head over the whole call (a single token's o can be tiny when
+        # q and k are nearly orthogonal, and then both fp32 kernels carry
+        # ulp-level absolute error in <q, k> that is large relative to it)
+        per_head = lambda x: x.permute(1, 2, 0, 3).reshape(B * H, -1).cpu().numpy()
+        worst_o = max(worst_o, rel_err(per_head(o1), per_head(o2)))
+    say(f"  o rel err vs fp32 recurrence {worst_o:.2e}")
+    assert worst_o < 2e-5
+    a, b = h1.cpu().numpy(), h2.cpu().numpy()
+    err = (np.abs(a - b).max(axis=(2, 3)) / np.abs(b).max(axis=(2, 3))).max()
+    say(f"  state rel err vs fp32 recurrence {err:.2e}")
+    assert err < 2e-5
+    for (bb, hh) in [(0, 0), (B - 1, H - 1)]:
+        assert codec_equal(head_codec(st, bb, hh), O.quantize(a[bb, hh], d.C, d.smooth)), (bb, hh)
+
+
+# ---------------------------------------------------------------------------
 # memory safety and determinism
 # ---------------------------------------------------------------------------
 
