@@ -351,10 +351,37 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
                                              tk["alpha"][n], tk["beta"][n], o)
                 lq.lq_gdn_window_flush_ragged(layr[l], nb_t[n])
     tpsr, msr = timed(ragged_step, B * W * L)
+    # the rows whose window fills decode and flush in one launch
+    # (lq_gdn_decode_step_flush_ragged), the others decode; on one stream, or
+    # with the fused calls on a second stream running beside the decodes
+    dec_t = [torch.where(p == W - 1, -1, p).to(torch.int32).contiguous() for p in pos_t]
+    end_t = [torch.where(p == W - 1, W - 1, -1).to(torch.int32).contiguous() for p in pos_t]
+    o_side = torch.empty_like(o)
+    side = torch.cuda.Stream(device=h0.device)
+
+    def ragged_fused_step(two_streams):
+        main = torch.cuda.current_stream()
+        for n in range(W):
+            if two_streams:
+                side.wait_stream(main)
+            for l in range(L):
+                tk = ring[l]
+                args = (tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n])
+                lq.lq_gdn_decode_step_flush_ragged(layr[l], end_t[n], *args, o_side,
+                                                   stream=side if two_streams else main)
+                lq.lq_gdn_decode_step_ragged(layr[l], dec_t[n], *args, o, stream=main)
+            if two_streams:
+                main.wait_stream(side)
+    tpsf, msf = timed(lambda: ragged_fused_step(False), B * W * L)
+    tps2, ms2 = timed(lambda: ragged_fused_step(True), B * W * L)
     out["ragged_windows"] = {"tokens_per_s": round(tpsr, 1), "ms_per_step": round(msr, 4),
                              "vs_lockstep": round(tpsr / lq_value, 3),
                              "schedule": "row b at window position (b + t) mod W; rows whose window "
-                                         "fills are flushed after every token"}
+                                         "fills are flushed after every token",
+                             "fused": {"tokens_per_s": round(tpsf, 1), "ms_per_step": round(msf, 4),
+                                       "vs_lockstep": round(tpsf / lq_value, 3)},
+                             "fused_two_streams": {"tokens_per_s": round(tps2, 1), "ms_per_step": round(ms2, 4),
+                                                   "vs_lockstep": round(tps2 / lq_value, 3)}}
     del layr
     torch.cuda.empty_cache()
     # (4) checkpoints: pack the quantized state of one layer into a blob and back

@@ -195,6 +195,21 @@ int lq_gdn_window_flush_ragged(const lq_dims *d, const lq_state *st, const int32
                                float *h_out, void *stream);
 
 /*
+ * Ragged windows: lq_gdn_decode_step_flush with the position of batch row b
+ * read from the DEVICE array pos[b] (int32 [B], 4-byte aligned): every head
+ * of row b decodes its token into slot pos[b] and flushes pos[b] + 1 slots.
+ * Rows with pos[b] outside [0, W) are left untouched (codec, buffer, o and
+ * h_out rows), so one call serves the rows whose window fills (or whose
+ * sequence ends) while lq_gdn_decode_step_ragged serves the others, e.g. on
+ * a second stream at the same time: the two calls touch disjoint rows.
+ * Errors: as lq_gdn_decode_step_flush (LQ_ERR_NULL / LQ_ERR_ALIGN also for pos).
+ */
+int lq_gdn_decode_step_flush_ragged(const lq_dims *d, const lq_state *st, const int32_t *pos,
+                                    const float *q, const float *k, const float *v,
+                                    const float *alpha, const float *beta, float *o, float *h_out,
+                                    void *stream);
+
+/*
  * Quantizes an fp32 state h [B,H,dk,dv] into the codec of st (steps 1-3 of
  * lq_gdn_window_flush; buffers untouched).  Used to start decoding from a
  * prefilled state.

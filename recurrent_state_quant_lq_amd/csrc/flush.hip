@@ -304,7 +304,7 @@ struct FlushArgs {
     float* bm;
     float* bg;
     float* h_out;
-    const int32_t* n_dev;     // per batch row (ragged windows), or null: N for every row
+    const int32_t* n_dev;     // per batch row (ragged windows; DEC: positions), or null: N for every row
     int W;
     int C;
     int N;
@@ -396,7 +396,8 @@ void flush_kernel(FlushArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const size_t head = blockIdx.x;
     const int W = a.W, C = a.C;
-    const int N = a.n_dev ? a.n_dev[head / (unsigned)a.H] : a.N;
+    // n_dev: the slot count per batch row, or (DEC) the decoded token's position
+    const int N = a.n_dev ? a.n_dev[head / (unsigned)a.H] + (DEC ? 1 : 0) : a.N;
     if (N <= 0 || N > W) return;                  // nothing buffered (or out of range): untouched
     const int n = N - 1;                          // DEC: the decoded token's slot
 
@@ -750,11 +751,11 @@ hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, co
     return flush_any<false>(d, args, s);
 }
 
-hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, const float* q, const float* k,
-                               const float* v, const float* alpha, const float* beta, float* o, float* h_out,
-                               hipStream_t s) {
+hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
+                               const float* q, const float* k, const float* v, const float* alpha,
+                               const float* beta, float* o, float* h_out, hipStream_t s) {
     FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
-                   st.buf_k, st.buf_m, st.buf_g, h_out, nullptr, d.W, d.C, pos + 1, d.smooth, d.H,
+                   st.buf_k, st.buf_m, st.buf_g, h_out, pos_dev, d.W, d.C, pos + 1, d.smooth, d.H,
                    q, k, v, alpha, beta, o};
     return flush_any<true>(d, args, s);
 }

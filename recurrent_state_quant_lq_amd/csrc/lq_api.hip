@@ -187,7 +187,21 @@ int lq_gdn_decode_step_flush(const lq_dims* d, const lq_state* st, int32_t pos, 
     if (h_out && !aligned16(h_out)) return LQ_ERR_ALIGN;
     if (pos < 0) return LQ_ERR_POS;
     if (pos >= d->W) return LQ_ERR_WINDOW_FULL;
-    return finish(lq::launch_decode_flush(*d, *st, pos, q, k, v, alpha, beta, o, h_out, (hipStream_t)stream));
+    return finish(lq::launch_decode_flush(*d, *st, pos, nullptr, q, k, v, alpha, beta, o, h_out,
+                                          (hipStream_t)stream));
+}
+
+int lq_gdn_decode_step_flush_ragged(const lq_dims* d, const lq_state* st, const int32_t* pos,
+                                    const float* q, const float* k, const float* v, const float* alpha,
+                                    const float* beta, float* o, float* h_out, void* stream) {
+    int rc = check_dims(d);
+    if (rc) return rc;
+    if ((rc = check_state(d, st, true))) return rc;
+    if ((rc = check_tokens(d, q, k, v, alpha, beta, o, true))) return rc;
+    if (h_out && !aligned16(h_out)) return LQ_ERR_ALIGN;
+    if (!pos) return LQ_ERR_NULL;
+    if (!aligned4(pos)) return LQ_ERR_ALIGN;
+    return finish(lq::launch_decode_flush(*d, *st, 0, pos, q, k, v, alpha, beta, o, h_out, (hipStream_t)stream));
 }
 
 int lq_gdn_window_flush_ragged(const lq_dims* d, const lq_state* st, const int32_t* n_buffered,

@@ -17,10 +17,11 @@ hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const in
                          const float* beta, float* o, hipStream_t s);
 hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, const int32_t* n_dev,
                         float* h_out, hipStream_t s);
-// Decode of one token into slot pos, then the flush of pos + 1 slots, in one launch.
-hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, const float* q, const float* k,
-                               const float* v, const float* alpha, const float* beta, float* o, float* h_out,
-                               hipStream_t s);
+// Decode of one token into slot pos, then the flush of pos + 1 slots, in one launch
+// (pos_dev: per-batch-row positions, rows outside [0, W) skipped; or null).
+hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
+                               const float* q, const float* k, const float* v, const float* alpha,
+                               const float* beta, float* o, float* h_out, hipStream_t s);
 hipError_t launch_quantize(const lq_dims& d, const float* h, const lq_state& st, hipStream_t s);
 hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* h_out, hipStream_t s);
 // Quantized-state records (lq_gdn_state_pack / unpack).

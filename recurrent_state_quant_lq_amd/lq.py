@@ -28,7 +28,8 @@ EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_ragg
            "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_state_bytes",
            "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims",
            "lq_timing_enable", "lq_timing_collect", "lq_checkpoint_bytes", "lq_gdn_state_pack",
-           "lq_gdn_state_unpack", "lq_gdn_decode_step_flush", "lq_gdn_prefill")
+           "lq_gdn_state_unpack", "lq_gdn_decode_step_flush", "lq_gdn_prefill",
+           "lq_gdn_decode_step_flush_ragged")
 LQ_KERNEL_DECODE, LQ_KERNEL_FLUSH, LQ_KERNEL_QUANTIZE, LQ_KERNEL_DEQUANTIZE, \
     LQ_KERNEL_FP32_RECURRENCE, LQ_KERNEL_CHECKPOINT, LQ_KERNEL_DECODE_FLUSH, \
     LQ_KERNEL_PREFILL = range(8)
@@ -67,13 +68,14 @@ def load() -> ct.CDLL:
         L.lq_gdn_window_flush.argtypes = [D, S, I, P, P]
         L.lq_gdn_decode_step_flush.argtypes = [D, S, I, P, P, P, P, P, P, P, P]
         L.lq_gdn_prefill.argtypes = [D, S, P, I, P, P, P, P, P, P, P]
+        L.lq_gdn_decode_step_flush_ragged.argtypes = [D, S, P, P, P, P, P, P, P, P, P]
         L.lq_gdn_decode_step_ragged.argtypes = [D, S, P, P, P, P, P, P, P, P]
         L.lq_gdn_window_flush_ragged.argtypes = [D, S, P, P, P]
         L.lq_gdn_state_quantize.argtypes = [D, P, S, P]
         L.lq_gdn_state_dequantize.argtypes = [D, S, P, P]
         L.lq_gdn_fp32_recurrence.argtypes = [D, P, I, P, P, P, P, P, P, P]
         for f in ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_flush", "lq_gdn_prefill",
-                  "lq_gdn_decode_step_ragged",
+                  "lq_gdn_decode_step_flush_ragged", "lq_gdn_decode_step_ragged",
                   "lq_gdn_window_flush_ragged", "lq_gdn_state_quantize",
                   "lq_gdn_state_dequantize", "lq_gdn_fp32_recurrence", "lq_check_dims",
                   "lq_last_hip_error"):
@@ -243,6 +245,24 @@ def lq_gdn_decode_step_flush(st: LayerState, pos: int, q, k, v, alpha, beta, o, 
                                          _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(h_out),
                                          _stream(stream))
     _raise("lq_gdn_decode_step_flush", rc)
+
+
+def lq_gdn_decode_step_flush_ragged(st: LayerState, pos, q, k, v, alpha, beta, o, h_out=None,
+                                    stream=None):
+    """pos: device int32 [B]; rows with pos in [0, W) decode slot pos and flush pos + 1 slots."""
+    d = st.dims
+    st.check()
+    _check(pos, "pos", (d.B,), torch.int32)
+    sh = _token_shapes(d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
+        _check(t, name, sh[name], torch.float32)
+    if h_out is not None:
+        _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
+    cs = st.c_state()
+    rc = load().lq_gdn_decode_step_flush_ragged(ct.byref(d), ct.byref(cs), _ptr(pos), _ptr(q), _ptr(k),
+                                                _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(h_out),
+                                                _stream(stream))
+    _raise("lq_gdn_decode_step_flush_ragged", rc)
 
 
 def lq_gdn_decode_step_ragged(st: LayerState, pos, q, k, v, alpha, beta, o, stream=None):

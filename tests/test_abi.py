@@ -184,6 +184,20 @@ def test_decode_flush_argument_errors():
     assert call(ct.byref(_dims(dk=96, dv=96)), ct.byref(st), 0, *args, None) == lq.LQ_ERR_UNSUPPORTED
 
 
+def test_decode_flush_ragged_argument_errors():
+    L = lq.load()
+    d = _dims()
+    st = _fake_state()
+    L.lq_gdn_decode_step_flush_ragged.argtypes = [ct.c_void_p] * 11
+    call = lambda dd, s, p, *a: L.lq_gdn_decode_step_flush_ragged(dd, s, p, *a, None)
+    args = (A, A, A, A, A, A, None)
+    assert call(ct.byref(d), ct.byref(st), None, *args) == lq.LQ_ERR_NULL
+    assert call(ct.byref(d), ct.byref(st), ct.c_void_p(0x7000002), *args) == lq.LQ_ERR_ALIGN
+    assert call(ct.byref(d), ct.byref(st), A, A, A, A, A, A, A, B4) == lq.LQ_ERR_ALIGN       # h_out
+    assert call(ct.byref(d), ct.byref(_fake_state(null="buf_g")), A, *args) == lq.LQ_ERR_NULL
+    assert call(ct.byref(_dims(dk=96, dv=96)), ct.byref(st), A, *args) == lq.LQ_ERR_UNSUPPORTED
+
+
 def test_prefill_argument_errors():
     L = lq.load()
     d = _dims()

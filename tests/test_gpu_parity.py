@@ -381,16 +381,22 @@ def test_timing_hook_records_each_launch():
     assert lq.lq_timing_collect() == ([], [])
 
 
-@pytest.mark.parametrize("dk,per_key", [(128, False), (64, True), (16, False)])
-def test_ragged_windows(dk, per_key):
+@pytest.mark.parametrize("dk,per_key,mode", [(128, False, "two_call"), (64, True, "two_call"),
+                                              (16, False, "two_call"), (128, False, "fused"),
+                                              (64, True, "fused_2streams"), (16, False, "fused")])
+def test_ragged_windows(dk, per_key, mode):
     """Batch rows at different window positions (the ragged entry points):
     row b's first window ends after first[b] tokens, later ones after W, the
     last at the end of the run; each flushed window is checked against the
     oracle (outputs, buffer rows, fp32 state, codec bytes) and the oracle's
     next codec is uploaded (resync).  Rows not flushed keep their codec and
-    their h_out rows; a row whose position is out of range is skipped."""
+    their h_out rows; a row whose position is out of range is skipped.
+    mode two_call: every row decodes, then the ending rows flush; fused: the
+    ending rows go through lq_gdn_decode_step_flush_ragged and the others
+    through lq_gdn_decode_step_ragged (fused_2streams: the two calls on two
+    streams at once, joined by events)."""
     B, H, W, C, T = 3, 4, 8, 2, 21
-    say(f"ragged dk={dk} per_key={per_key}")
+    say(f"ragged dk={dk} per_key={per_key} mode={mode}")
     d = lq.make_dims(B, H, dk, dk, W, C, int(per_key), 1)
     tok = inputs.host_tokens(321 + dk, T, B, H, dk, dk, per_key=per_key, beta_lo=0.1, beta_hi=0.9)
     tk = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in tok.items()}
@@ -407,17 +413,35 @@ def test_ragged_windows(dk, per_key):
     h_out = torch.empty((B, H, dk, dk), device="cuda")
     outs = []
     flushed = 0
+    side = torch.cuda.Stream() if mode == "fused_2streams" else None
     for t in range(T):
-        lq.lq_gdn_decode_step_ragged(st, torch.tensor(pos, dtype=torch.int32, device="cuda"),
-                                     tk["q"][t], tk["k"][t], tk["v"][t], tk["alpha"][t], tk["beta"][t], o)
-        outs.append(o.clone())
         nb = [pos[b] + 1 if (pos[b] + 1 == wlen[b] or t == T - 1) else 0 for b in range(B)]
-        if not any(nb):
-            pos = [p + 1 for p in pos]
-            continue
-        before = {b: [head_codec(st, b, h) for h in range(H)] for b in range(B) if not nb[b]}
-        h_out.fill_(7.0)
-        lq.lq_gdn_window_flush_ragged(st, torch.tensor(nb, dtype=torch.int32, device="cuda"), h_out)
+        tok_t = (tk["q"][t], tk["k"][t], tk["v"][t], tk["alpha"][t], tk["beta"][t], o)
+        if mode == "two_call" or not any(nb):
+            before = {b: [head_codec(st, b, h) for h in range(H)] for b in range(B) if not nb[b]}
+            lq.lq_gdn_decode_step_ragged(st, torch.tensor(pos, dtype=torch.int32, device="cuda"), *tok_t)
+            outs.append(o.clone())
+            if not any(nb):
+                pos = [p + 1 for p in pos]
+                continue
+            h_out.fill_(7.0)
+            lq.lq_gdn_window_flush_ragged(st, torch.tensor(nb, dtype=torch.int32, device="cuda"), h_out)
+        else:
+            before = {b: [head_codec(st, b, h) for h in range(H)] for b in range(B) if not nb[b]}
+            h_out.fill_(7.0)
+            dec_pos = torch.tensor([-1 if nb[b] else pos[b] for b in range(B)], dtype=torch.int32, device="cuda")
+            end_pos = torch.tensor([pos[b] if nb[b] else -1 for b in range(B)], dtype=torch.int32, device="cuda")
+            if side is None:
+                lq.lq_gdn_decode_step_flush_ragged(st, end_pos, *tok_t, h_out=h_out)
+                lq.lq_gdn_decode_step_ragged(st, dec_pos, *tok_t)
+            else:
+                main = torch.cuda.current_stream()
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    lq.lq_gdn_decode_step_flush_ragged(st, end_pos, *tok_t, h_out=h_out, stream=side)
+                lq.lq_gdn_decode_step_ragged(st, dec_pos, *tok_t, stream=main)
+                main.wait_stream(side)
+            outs.append(o.clone())
         torch.cuda.synchronize()
         for b in range(B):
             if not nb[b]:
@@ -452,6 +476,17 @@ def test_ragged_windows(dk, per_key):
     torch.cuda.synchronize()
     assert (o[1:] == 5.0).all() and torch.equal(st.buf_k[1:], bk[1:])
     assert not (o[0] == 5.0).all()
+    if mode != "two_call":
+        o.fill_(5.0)
+        h_out.fill_(7.0)
+        bk = st.buf_k.clone()
+        keep = {b: [head_codec(st, b, h) for h in range(H)] for b in (1, 2)}
+        lq.lq_gdn_decode_step_flush_ragged(st, bad, tk["q"][0], tk["k"][0], tk["v"][0], tk["alpha"][0],
+                                           tk["beta"][0], o, h_out=h_out)
+        torch.cuda.synchronize()
+        assert (o[1:] == 5.0).all() and (h_out[1:] == 7.0).all() and torch.equal(st.buf_k[1:], bk[1:])
+        assert all(codec_equal(head_codec(st, b, h), keep[b][h]) for b in (1, 2) for h in range(H))
+        assert not (o[0] == 5.0).all() and not (h_out[0] == 7.0).all()
 
 
 # ---------------------------------------------------------------------------
