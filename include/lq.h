@@ -58,7 +58,7 @@ extern "C" {
 enum lq_status {
     LQ_OK = 0,
     LQ_ERR_NULL = 1,          /* a required pointer is NULL */
-    LQ_ERR_DIMS = 2,          /* B, H, dk, dv, W <= 0; C < 0 or C > dk; bad mode flag */
+    LQ_ERR_DIMS = 2,          /* B, H, dk, dv, W <= 0; C < 0 or C > dk; bad mode or dtype flag */
     LQ_ERR_UNSUPPORTED = 3,   /* valid but not built: dk/dv, W > 32 or C > 8 */
     LQ_ERR_WINDOW_FULL = 4,   /* decode_step with pos >= W: flush first */
     LQ_ERR_POS = 5,           /* pos < 0, n_buffered outside [0, W], T < 0 */
@@ -68,12 +68,19 @@ enum lq_status {
 
 enum lq_decay_mode { LQ_DECAY_SCALAR = 0, LQ_DECAY_PER_KEY = 1 };
 
+/* Element type of the token vectors q, k, v and of the outputs o (the gates
+ * alpha, beta and everything in lq_state stay fp32).  bf16 values are widened
+ * exactly; outputs are rounded to nearest, ties to even. */
+enum lq_io_dtype { LQ_IO_F32 = 0, LQ_IO_BF16 = 1 };
+
 /* Problem shape.  smooth: 1 = residual smoothing on (per-column scaling,
- * [forum] technique 3), 0 = off (col_scale written as 1). */
+ * [forum] technique 3), 0 = off (col_scale written as 1).  io_dtype: an
+ * lq_io_dtype. */
 typedef struct lq_dims {
     int32_t B, H, dk, dv, W, C;
     int32_t decay_mode;
     int32_t smooth;
+    int32_t io_dtype;
 } lq_dims;
 
 /* Device arrays of one layer's quantized state and window buffer.
@@ -118,14 +125,14 @@ typedef struct lq_state {
  * H_n = A_n Hb + sum_i (E_i o k_i) u_i^T with A_n = Gamma_n - sum_i
  * (E_i o k_i) y_i^T; the buffer keeps m_i = u_i - Hb^T y_i, i.e. the WY
  * factors projected once through the fixed Hb.)
- *   q, k  fp32 [B,H,dk];  v, o fp32 [B,H,dv];  beta fp32 [B,H];
+ *   q, k  [B,H,dk];  v, o [B,H,dv]  (fp32 or bf16 per d->io_dtype);  beta fp32 [B,H];
  *   alpha fp32 [B,H] (scalar mode) or [B,H,dk] (per-key mode), in (0, 1].
  * Reads the codec and buffer slots 0..n-1; writes buffer slot n and o.
  * Errors: LQ_ERR_WINDOW_FULL if pos >= W, LQ_ERR_POS if pos < 0.
  */
 int lq_gdn_decode_step(const lq_dims *d, const lq_state *st, int32_t pos,
-                       const float *q, const float *k, const float *v,
-                       const float *alpha, const float *beta, float *o, void *stream);
+                       const void *q, const void *k, const void *v,
+                       const float *alpha, const float *beta, void *o, void *stream);
 
 /*
  * Window boundary for every (b, h) ([news ¶3]: the state is rebuilt and
@@ -166,8 +173,8 @@ int lq_gdn_window_flush(const lq_dims *d, const lq_state *st, int32_t n_buffered
  * of the two calls.
  */
 int lq_gdn_decode_step_flush(const lq_dims *d, const lq_state *st, int32_t pos,
-                             const float *q, const float *k, const float *v,
-                             const float *alpha, const float *beta, float *o, float *h_out,
+                             const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta, void *o, float *h_out,
                              void *stream);
 
 /*
@@ -179,8 +186,8 @@ int lq_gdn_decode_step_flush(const lq_dims *d, const lq_state *st, int32_t pos,
  * Errors: as lq_gdn_decode_step (LQ_ERR_NULL / LQ_ERR_ALIGN also for pos).
  */
 int lq_gdn_decode_step_ragged(const lq_dims *d, const lq_state *st, const int32_t *pos,
-                              const float *q, const float *k, const float *v,
-                              const float *alpha, const float *beta, float *o, void *stream);
+                              const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, void *o, void *stream);
 
 /*
  * Ragged windows: lq_gdn_window_flush with the number of buffered slots of
@@ -205,8 +212,8 @@ int lq_gdn_window_flush_ragged(const lq_dims *d, const lq_state *st, const int32
  * Errors: as lq_gdn_decode_step_flush (LQ_ERR_NULL / LQ_ERR_ALIGN also for pos).
  */
 int lq_gdn_decode_step_flush_ragged(const lq_dims *d, const lq_state *st, const int32_t *pos,
-                                    const float *q, const float *k, const float *v,
-                                    const float *alpha, const float *beta, float *o, float *h_out,
+                                    const void *q, const void *k, const void *v,
+                                    const float *alpha, const float *beta, void *o, float *h_out,
                                     void *stream);
 
 /*
@@ -247,8 +254,8 @@ int lq_gdn_state_dequantize(const lq_dims *d, const lq_state *st, float *h_out, 
  * d->W, d->C and d->smooth are ignored.  Errors: LQ_ERR_POS if T < 0.
  */
 int lq_gdn_fp32_recurrence(const lq_dims *d, float *h, int32_t T,
-                           const float *q, const float *k, const float *v,
-                           const float *alpha, const float *beta, float *o, void *stream);
+                           const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, void *o, void *stream);
 
 /*
  * Prefill of a prompt: the state after T tokens, computed in fp32 in chunks
@@ -271,8 +278,8 @@ int lq_gdn_fp32_recurrence(const lq_dims *d, float *h, int32_t T,
  * token arrays.
  */
 int lq_gdn_prefill(const lq_dims *d, const lq_state *st, float *h, int32_t T,
-                   const float *q, const float *k, const float *v,
-                   const float *alpha, const float *beta, float *o, void *stream);
+                   const void *q, const void *k, const void *v,
+                   const float *alpha, const float *beta, void *o, void *stream);
 
 /* Bytes of one layer's codec arrays (sq, scales, compensators), i.e.
  * B*H*(dk*dv + 4dk + 4dv + C*(4dv + 4)); 0 if d is NULL or invalid. */

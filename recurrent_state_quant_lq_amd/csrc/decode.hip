@@ -51,12 +51,12 @@ struct DecodeArgs {
     float* bk;
     float* bm;
     float* bg;
-    const float* q;
-    const float* k;
-    const float* v;
+    const void* q;            // q, k, v, o: fp32 or bf16 (the kernel's TI)
+    const void* k;
+    const void* v;
     const float* alpha;
     const float* beta;
-    float* o;
+    void* o;
     const int32_t* pos_dev;   // per batch row (ragged positions), or null: pos for every row
     int W;
     int C;
@@ -97,7 +97,7 @@ struct Dec {
     static constexpr int WPE = WM <= 16 ? (KDA ? 6 : 8) : 4;
 };
 
-template <int DK, int DV, int WM, bool KDA, int NB>
+template <int DK, int DV, int WM, bool KDA, int NB, typename TI>
 __global__ __launch_bounds__((Dec<DK, DV, WM, KDA>::NT))
 __attribute__((amdgpu_waves_per_eu(Dec<DK, DV, WM, KDA>::WPE, Dec<DK, DV, WM, KDA>::WPE)))
 void decode_kernel(DecodeArgs a) {
@@ -135,14 +135,16 @@ void decode_kernel(DecodeArgs a) {
     // Three contiguous copies, 16-byte chunk c of a region landing at region + 4c floats
     // (lane l of a wave writes its wave's base + 16*l bytes).
     {
-        // q k v r s [alpha gprev]: segment sg = t / SEGL, one chunk per lane
+        // q k v r s [alpha gprev]: segment sg = t / SEGL, one chunk per lane (bf16 q, k,
+        // v fill the first half of their segments)
         constexpr int NVS = D::SCV;
         const int sg = t / SEGL, off = 4 * (t % SEGL);
+        const bool tin = sizeof(TI) == 4 || 2 * off < DK;   // this lane's chunk lies in the token row
         const float* src = nullptr;
         switch (sg) {
-            case D::SQ: src = a.q + head * DK; break;
-            case D::SK: src = a.k + head * DK; break;
-            case D::SV: src = a.v + head * DV; break;
+            case D::SQ: if (tin) src = reinterpret_cast<const float*>(static_cast<const TI*>(a.q) + head * DK); break;
+            case D::SK: if (tin) src = reinterpret_cast<const float*>(static_cast<const TI*>(a.k) + head * DK); break;
+            case D::SV: if (tin) src = reinterpret_cast<const float*>(static_cast<const TI*>(a.v) + head * DV); break;
             case D::SR: src = a.r + head * DK; break;
             case D::SS: src = a.s + head * DV; break;
             default:
@@ -226,7 +228,8 @@ void decode_kernel(DecodeArgs a) {
     // ---- A. digits of r o e^g o q and r o e^g o k; slot n's key and decay; dot products ----
     float xq = 0.0f, xk = 0.0f;                   // r o e^g o q, r o e^g o k (channel lanes)
     if (is_ch) {
-        const float qc = s_vec[D::SQ * DK + t], kc = s_vec[D::SK * DK + t], rc = s_vec[D::SR * DK + t];
+        const float qc = seg_ld<TI>(s_vec + D::SQ * DK, t), kc = seg_ld<TI>(s_vec + D::SK * DK, t);
+        const float rc = s_vec[D::SR * DK + t];
         float gn;
         if constexpr (KDA) gn = (n > 0 ? s_vec[D::SG * DK + t] : 0.0f) + logf(s_vec[D::SA * DK + t]);
         else gn = gn_s;
@@ -262,8 +265,8 @@ void decode_kernel(DecodeArgs a) {
     }
     {
         float kq[CH], kk[CH];
-        load_floats<CH>(s_vec + D::SQ * DK + c0, kq);
-        load_floats<CH>(s_vec + D::SK * DK + c0, kk);
+        seg_ld_n<CH, TI>(s_vec + D::SQ * DK, c0, kq);
+        seg_ld_n<CH, TI>(s_vec + D::SK * DK, c0, kk);
 #pragma unroll
         for (int rd = 0; rd < ROUNDS; ++rd) {
             const int slot = slot0 + rd * SPR;
@@ -364,12 +367,12 @@ void decode_kernel(DecodeArgs a) {
                 const int ic = s_misc[c] & (DK - 1);
                 const float e = KDA ? s_en[ic] : eg;
                 const float cvj = s_vec[(D::SCV + c) * DK + j];
-                hq += (e * s_vec[D::SQ * DK + ic]) * cvj;
-                hk += (e * s_vec[D::SK * DK + ic]) * cvj;
+                hq += (e * seg_ld<TI>(s_vec + D::SQ * DK, ic)) * cvj;
+                hk += (e * seg_ld<TI>(s_vec + D::SK * DK, ic)) * cvj;
             }
-        const float mn = beta * (s_vec[D::SV * DK + j] - hk - sr);
+        const float mn = beta * (seg_ld<TI>(s_vec + D::SV * DK, j) - hk - sr);
         a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
-        a.o[head * DV + j] = hq + sa + s_a[n] * mn;
+        tok_st<TI>(a.o, head * DV + j, hq + sa + s_a[n] * mn);
     }
 }
 
@@ -377,7 +380,11 @@ template <int DK, int WM, bool KDA, int NB>
 hipError_t launch_nb(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
     constexpr int NT = Dec<DK, DK, WM, KDA>::NT;
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
-    return launch_kernel(LQ_KERNEL_DECODE, decode_kernel<DK, DK, WM, KDA, NB>, dim3(grid), dim3(NT), s, args);
+    if (d.io_dtype == LQ_IO_BF16)
+        return launch_kernel(LQ_KERNEL_DECODE, decode_kernel<DK, DK, WM, KDA, NB, uint16_t>, dim3(grid), dim3(NT),
+                             s, args);
+    return launch_kernel(LQ_KERNEL_DECODE, decode_kernel<DK, DK, WM, KDA, NB, float>, dim3(grid), dim3(NT), s,
+                         args);
 }
 
 // dk = 128, W <= 16: one kernel per window position (no runtime guards).
@@ -408,8 +415,8 @@ hipError_t launch_dk(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
-                         const float* q, const float* k, const float* v, const float* alpha,
-                         const float* beta, float* o, hipStream_t s) {
+                         const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, void* o, hipStream_t s) {
     DecodeArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
                     st.buf_k, st.buf_m, st.buf_g,
                     q, k, v, alpha, beta, o, pos_dev, d.W, d.C, d.H, pos};

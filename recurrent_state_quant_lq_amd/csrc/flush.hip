@@ -311,20 +311,22 @@ struct FlushArgs {
     int smooth;
     int H;
     // the token decoded into slot N-1 first (decode fused into the flush)
-    const float* q;
-    const float* k;
-    const float* v;
+    const void* q;            // q, k, v, o: fp32 or bf16 (the kernel's TI)
+    const void* k;
+    const void* v;
     const float* alpha;
     const float* beta;
-    float* o;
+    void* o;
 };
 
 // Rows 0..NPAD-1 of a [rows][D] fp32 block (row index clamped to rmax) into
 // LDS dst[NPAD][D]; 16-byte pieces, one kilobyte per wave-wide copy, copies
-// spread over the NW waves.  Row rsub (if >= 0) comes from the vector sub.
+// spread over the NW waves.  Row rsub (if >= 0) comes from the vector sub,
+// whose first sub_len floats' worth of bytes are copied (D, or D/2 for a
+// bf16 vector, which lands in the first half of the row).
 template <int NPAD, int D, int NW>
 __device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst, int w, int lane,
-                                         int rsub = -1, const float* sub = nullptr) {
+                                         int rsub = -1, const float* sub = nullptr, int sub_len = D) {
     constexpr int NCOPY = NPAD * D / 256;
     static_assert((NPAD * D) % 256 == 0, "block of whole copies");
 #pragma unroll
@@ -333,7 +335,8 @@ __device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst,
         if (cp < NCOPY) {
             const int e = cp * 256 + 4 * lane;
             const int row = min(e / D, rmax);
-            lds_dma16(row == rsub ? sub + e % D : src + (size_t)row * D + e % D, dst + cp * 256);
+            if (row != rsub) lds_dma16(src + (size_t)row * D + e % D, dst + cp * 256);
+            else if (e % D < sub_len) lds_dma16(sub + e % D, dst + cp * 256);
         }
     }
 }
@@ -364,7 +367,7 @@ struct FlushLds {
 // m_n = beta (v - H'^T k), o = H'^T q + <q, k> m_n, and H = H' + k m_n^T.
 // The GEMVs run on the fp32 registers (fma, lane-group rows summed with the
 // row swaps, waves through LDS).
-template <int DK, int DV, int WM, bool KDA, bool DEC>
+template <int DK, int DV, int WM, bool KDA, bool DEC, typename TI>
 __global__ __launch_bounds__((FS<DK, DV>::NT))
 __attribute__((amdgpu_waves_per_eu(WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2), WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2))))
 void flush_kernel(FlushArgs a) {
@@ -430,12 +433,14 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
                 for (int q = 0; q < SPI; ++q) {
                     const int sg = s0 + q;
-                    const float* p = sg == 0 ? a.q + head * DK
-                                   : sg == 1 ? a.v + head * DV
+                    const float* p = sg == 0 ? reinterpret_cast<const float*>(static_cast<const TI*>(a.q) + head * DK)
+                                   : sg == 1 ? reinterpret_cast<const float*>(static_cast<const TI*>(a.v) + head * DV)
                                    : sg < NTS ? a.alpha + head * DK : nullptr;
                     if (my == q) src = p;
                 }
-                if (src) lds_dma16(src + 4 * (lane % SEGL), s_tq + s0 * DK);
+                // bf16 q and v fill the first half of their segments
+                const bool in_row = sizeof(TI) == 4 || s0 + my >= 2 || 8 * (lane % SEGL) < DK;
+                if (src && in_row) lds_dma16(src + 4 * (lane % SEGL), s_tq + s0 * DK);
             }
         }
         if (w == 0) {
@@ -449,7 +454,9 @@ void flush_kernel(FlushArgs a) {
         dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, W - 1, s_M, w, lane);
         // DEC: the token's key lands in row n
         dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane, DEC ? n : -1,
-                               DEC ? a.k + head * DK : nullptr);
+                               DEC ? reinterpret_cast<const float*>(static_cast<const TI*>(a.k) + head * DK)
+                                   : nullptr,
+                               DK * (int)sizeof(TI) / 4);
         if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, W - 1, s_G, w, lane);
     }
     // D-layout bytes of the base state: column li*CT + ct, this lane's RPL rows
@@ -473,7 +480,7 @@ void flush_kernel(FlushArgs a) {
     if constexpr (DEC) {
         // slot n's key and log-decay
         if (t < DK) {
-            a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = s_K[n * DK + t];
+            a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = seg_ld<TI>(s_K + n * DK, t);
             if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = glast(t);
             else if (t == 0) a.bg[head * (size_t)W + n] = gn_s;
         }
@@ -578,7 +585,7 @@ void flush_kernel(FlushArgs a) {
     if constexpr (DEC) {
         float* s_an = s_pk + NW * DV;                              // [NW] partial <q, k>
         {
-            float an = t < DK ? s_tq[t] * s_K[n * DK + t] : 0.0f;
+            float an = t < DK ? seg_ld<TI>(s_tq, t) * seg_ld<TI>(s_K + n * DK, t) : 0.0f;
             an = group_sum<64>(an);
             if (lane == 0) s_an[w] = an;
         }
@@ -592,7 +599,7 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 float x[4];
-                load_floats<4>((vec ? s_K + n * DK : s_tq) + row0 + 4 * rb, x);
+                seg_ld_n<4, TI>(vec ? s_K + n * DK : s_tq, row0 + 4 * rb, x);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -623,10 +630,10 @@ void flush_kernel(FlushArgs a) {
                 hk += s_pk[ww * DV + j];
                 aq += s_an[ww];
             }
-            const float mn = __int_as_float(s_idx[8]) * (s_tv[j] - hk);
+            const float mn = __int_as_float(s_idx[8]) * (seg_ld<TI>(s_tv, j) - hk);
             s_M[n * DV + j] = mn;
             a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
-            a.o[head * DV + j] = hq + aq * mn;
+            tok_st<TI>(a.o, head * DV + j, hq + aq * mn);
         }
         lds_barrier();
         {
@@ -635,7 +642,7 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 float xk[4];
-                load_floats<4>(s_K + n * DK + row0 + 4 * rb, xk);
+                seg_ld_n<4, TI>(s_K + n * DK, row0 + 4 * rb, xk);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -721,8 +728,12 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
 
 template <int DK, int WM, bool KDA, bool DEC>
 hipError_t flush_t(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
-    return launch_kernel(DEC ? LQ_KERNEL_DECODE_FLUSH : LQ_KERNEL_FLUSH, flush_kernel<DK, DK, WM, KDA, DEC>,
-                         dim3((unsigned)d.B * (unsigned)d.H), dim3(FS<DK, DK>::NT), s, args);
+    const dim3 grid((unsigned)d.B * (unsigned)d.H), block(FS<DK, DK>::NT);
+    if (DEC && d.io_dtype == LQ_IO_BF16)
+        return launch_kernel(LQ_KERNEL_DECODE_FLUSH, flush_kernel<DK, DK, WM, KDA, DEC, uint16_t>, grid, block, s,
+                             args);
+    return launch_kernel(DEC ? LQ_KERNEL_DECODE_FLUSH : LQ_KERNEL_FLUSH, flush_kernel<DK, DK, WM, KDA, DEC, float>,
+                         grid, block, s, args);
 }
 
 template <int DK, bool DEC>
@@ -752,8 +763,8 @@ hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, co
 }
 
 hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
-                               const float* q, const float* k, const float* v, const float* alpha,
-                               const float* beta, float* o, float* h_out, hipStream_t s) {
+                               const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, void* o, float* h_out, hipStream_t s) {
     FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
                    st.buf_k, st.buf_m, st.buf_g, h_out, pos_dev, d.W, d.C, pos + 1, d.smooth, d.H,
                    q, k, v, alpha, beta, o};

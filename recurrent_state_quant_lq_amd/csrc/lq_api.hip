@@ -16,8 +16,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Token inputs: q, k, v, o vectors 16-byte aligned; alpha 16-byte aligned in
 // per-key mode and 4-byte aligned (one float per head) in scalar mode; beta
 // 4-byte aligned.
-int check_tokens(const lq_dims* d, const float* q, const float* k, const float* v,
-                 const float* alpha, const float* beta, const float* o, bool o_required) {
+int check_tokens(const lq_dims* d, const void* q, const void* k, const void* v,
+                 const float* alpha, const float* beta, const void* o, bool o_required) {
     if (!q || !k || !v || !alpha || !beta || (o_required && !o)) return LQ_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o))) return LQ_ERR_ALIGN;
     if (d->decay_mode == LQ_DECAY_PER_KEY ? !aligned16(alpha) : !aligned4(alpha)) return LQ_ERR_ALIGN;
@@ -31,6 +31,7 @@ int check_dims(const lq_dims* d) {
     if (d->C < 0 || d->C > d->dk) return LQ_ERR_DIMS;
     if (d->decay_mode != LQ_DECAY_SCALAR && d->decay_mode != LQ_DECAY_PER_KEY) return LQ_ERR_DIMS;
     if (d->smooth != 0 && d->smooth != 1) return LQ_ERR_DIMS;
+    if (d->io_dtype != LQ_IO_F32 && d->io_dtype != LQ_IO_BF16) return LQ_ERR_DIMS;
     if ((int64_t)d->B * (int64_t)d->H > 0x7fffffffLL) return LQ_ERR_DIMS;
     if (d->dk != d->dv || (d->dk != 16 && d->dk != 64 && d->dk != 128)) return LQ_ERR_UNSUPPORTED;
     if (d->W > 32 || d->C > 8) return LQ_ERR_UNSUPPORTED;
@@ -142,9 +143,9 @@ extern "C" {
 
 int lq_check_dims(const lq_dims* d) { return check_dims(d); }
 
-int lq_gdn_decode_step(const lq_dims* d, const lq_state* st, int32_t pos, const float* q,
-                       const float* k, const float* v, const float* alpha, const float* beta,
-                       float* o, void* stream) {
+int lq_gdn_decode_step(const lq_dims* d, const lq_state* st, int32_t pos, const void* q,
+                       const void* k, const void* v, const float* alpha, const float* beta,
+                       void* o, void* stream) {
     int rc = check_dims(d);
     if (rc) return rc;
     if ((rc = check_state(d, st, true))) return rc;
@@ -155,8 +156,8 @@ int lq_gdn_decode_step(const lq_dims* d, const lq_state* st, int32_t pos, const 
 }
 
 int lq_gdn_decode_step_ragged(const lq_dims* d, const lq_state* st, const int32_t* pos,
-                              const float* q, const float* k, const float* v, const float* alpha,
-                              const float* beta, float* o, void* stream) {
+                              const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, void* o, void* stream) {
     int rc = check_dims(d);
     if (rc) return rc;
     if ((rc = check_state(d, st, true))) return rc;
@@ -177,9 +178,9 @@ int lq_gdn_window_flush(const lq_dims* d, const lq_state* st, int32_t n_buffered
     return finish(lq::launch_flush(*d, *st, n_buffered, nullptr, h_out, (hipStream_t)stream));
 }
 
-int lq_gdn_decode_step_flush(const lq_dims* d, const lq_state* st, int32_t pos, const float* q,
-                             const float* k, const float* v, const float* alpha, const float* beta,
-                             float* o, float* h_out, void* stream) {
+int lq_gdn_decode_step_flush(const lq_dims* d, const lq_state* st, int32_t pos, const void* q,
+                             const void* k, const void* v, const float* alpha, const float* beta,
+                             void* o, float* h_out, void* stream) {
     int rc = check_dims(d);
     if (rc) return rc;
     if ((rc = check_state(d, st, true))) return rc;
@@ -192,8 +193,8 @@ int lq_gdn_decode_step_flush(const lq_dims* d, const lq_state* st, int32_t pos, 
 }
 
 int lq_gdn_decode_step_flush_ragged(const lq_dims* d, const lq_state* st, const int32_t* pos,
-                                    const float* q, const float* k, const float* v, const float* alpha,
-                                    const float* beta, float* o, float* h_out, void* stream) {
+                                    const void* q, const void* k, const void* v, const float* alpha,
+                                    const float* beta, void* o, float* h_out, void* stream) {
     int rc = check_dims(d);
     if (rc) return rc;
     if ((rc = check_state(d, st, true))) return rc;
@@ -231,8 +232,8 @@ int lq_gdn_state_dequantize(const lq_dims* d, const lq_state* st, float* h_out, 
     return finish(lq::launch_dequantize(*d, *st, h_out, (hipStream_t)stream));
 }
 
-int lq_gdn_fp32_recurrence(const lq_dims* d, float* h, int32_t T, const float* q, const float* k,
-                           const float* v, const float* alpha, const float* beta, float* o,
+int lq_gdn_fp32_recurrence(const lq_dims* d, float* h, int32_t T, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta, void* o,
                            void* stream) {
     int rc = check_dims(d);
     if (rc) return rc;
@@ -243,8 +244,8 @@ int lq_gdn_fp32_recurrence(const lq_dims* d, float* h, int32_t T, const float* q
     return finish(lq::launch_fp32_recurrence(*d, h, T, q, k, v, alpha, beta, o, (hipStream_t)stream));
 }
 
-int lq_gdn_prefill(const lq_dims* d, const lq_state* st, float* h, int32_t T, const float* q,
-                   const float* k, const float* v, const float* alpha, const float* beta, float* o,
+int lq_gdn_prefill(const lq_dims* d, const lq_state* st, float* h, int32_t T, const void* q,
+                   const void* k, const void* v, const float* alpha, const float* beta, void* o,
                    void* stream) {
     int rc = check_dims(d);
     if (rc) return rc;

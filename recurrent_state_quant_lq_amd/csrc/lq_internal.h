@@ -13,26 +13,26 @@ namespace lq {
 // returns the hipError_t of its launch.
 // pos_dev / n_dev: per-batch-row device arrays (ragged windows) or null.
 hipError_t launch_decode(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
-                         const float* q, const float* k, const float* v, const float* alpha,
-                         const float* beta, float* o, hipStream_t s);
+                         const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, void* o, hipStream_t s);
 hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, const int32_t* n_dev,
                         float* h_out, hipStream_t s);
 // Decode of one token into slot pos, then the flush of pos + 1 slots, in one launch
 // (pos_dev: per-batch-row positions, rows outside [0, W) skipped; or null).
 hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, const int32_t* pos_dev,
-                               const float* q, const float* k, const float* v, const float* alpha,
-                               const float* beta, float* o, float* h_out, hipStream_t s);
+                               const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, void* o, float* h_out, hipStream_t s);
 hipError_t launch_quantize(const lq_dims& d, const float* h, const lq_state& st, hipStream_t s);
 hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* h_out, hipStream_t s);
 // Quantized-state records (lq_gdn_state_pack / unpack).
 size_t checkpoint_head_bytes(const lq_dims& d);
 hipError_t launch_checkpoint(const lq_dims& d, const lq_state& st, void* blob, bool pack, hipStream_t s);
 // Chunked fp32 prefill of T tokens, state h updated in place (lq_gdn_prefill).
-hipError_t launch_prefill(const lq_dims& d, float* h, int T, const float* q, const float* k, const float* v,
-                          const float* alpha, const float* beta, float* o, hipStream_t s);
-hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const float* q,
-                                  const float* k, const float* v, const float* alpha,
-                                  const float* beta, float* o, hipStream_t s);
+hipError_t launch_prefill(const lq_dims& d, float* h, int T, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, void* o, hipStream_t s);
+hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const void* q,
+                                  const void* k, const void* v, const float* alpha,
+                                  const float* beta, void* o, hipStream_t s);
 
 // Kernel timing (lq_timing_*): when recording is on, hands out the event
 // pair of the next launch of `family` and returns true.
@@ -239,6 +239,55 @@ __device__ __forceinline__ void store_floats(float* __restrict__ p, const float 
 #pragma unroll
         for (int i = 0; i < N; ++i) p[i] = x[i];
     }
+}
+
+// bf16 token I/O.  A bf16 value is the upper half of an fp32 bit pattern:
+// widening is exact; narrowing rounds to nearest, ties to even (adding
+// 0x7fff plus the lowest kept bit carries into the kept half exactly when
+// the dropped half is above one half, or equal with an odd kept half), and
+// keeps NaNs quiet.
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Token vectors staged in LDS: fp32 (TI = float), or bf16 (TI = uint16_t)
+// packed into the first half of an fp32-sized segment.
+template <typename TI>
+__device__ __forceinline__ float seg_ld(const float* seg, int i) {
+    if constexpr (sizeof(TI) == 4) return seg[i];
+    else return bf16_to_f32(reinterpret_cast<const uint16_t*>(seg)[i]);
+}
+template <int N, typename TI>
+__device__ __forceinline__ void seg_ld_n(const float* seg, int i0, float (&x)[N]) {
+    if constexpr (sizeof(TI) == 4) {
+        load_floats<N>(seg + i0, x);
+    } else if constexpr (N % 2 != 0) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) x[e] = seg_ld<TI>(seg, i0 + e);
+    } else {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(seg) + i0 / 2;
+#pragma unroll
+        for (int e = 0; e < N / 2; ++e) {
+            const uint32_t w = p[e];
+            x[2 * e] = __uint_as_float(w << 16);
+            x[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+    }
+}
+// One output element (fp32 or bf16, round to nearest even).
+template <typename TI>
+__device__ __forceinline__ void tok_st(void* base, size_t i, float x) {
+    if constexpr (sizeof(TI) == 4) reinterpret_cast<float*>(base)[i] = x;
+    else reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16(x);
+}
+// One input element from global memory.
+template <typename TI>
+__device__ __forceinline__ float tok_ld(const void* base, size_t i) {
+    if constexpr (sizeof(TI) == 4) return reinterpret_cast<const float*>(base)[i];
+    else return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
 }
 
 // Global -> LDS without registers.  Lane l of the wave writes

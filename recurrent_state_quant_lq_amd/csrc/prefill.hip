@@ -36,19 +36,19 @@ namespace {
 
 struct PrefillArgs {
     float* h;
-    const float* q;
-    const float* k;
-    const float* v;
+    const void* q;            // q, k, v, o: fp32 or bf16 (the kernel's TI)
+    const void* k;
+    const void* v;
     const float* alpha;
     const float* beta;
-    float* o;
+    void* o;
     int T;
     int heads;     // B*H: stride between tokens, in heads
 };
 
 constexpr int CL = 16;   // chunk length (the MFMA tile)
 
-template <int DK, int DV, bool KDA>
+template <int DK, int DV, bool KDA, typename TI>
 struct PF {
     static_assert(DK == DV && DK % 16 == 0, "square heads, 16-multiples");
     static constexpr int NW = DV / 16 < 4 ? DV / 16 : 4;   // waves
@@ -67,17 +67,18 @@ struct PF {
     static constexpr int SA = G + 2 * CL;                  // A = beta rr (strictly lower) [CL][CL]
     static constexpr int SP = SA + CL * CL;                // P = a masked [CL][CL]
     static constexpr int ST = SP + CL * CL;                // T = (I + A)^{-1} [CL][CL]
-    static constexpr int FLOATS = ST + CL * CL;
+    static constexpr int STG = ST + CL * CL;               // bf16 q | k | v rows as loaded [3][CL][DK]
+    static constexpr int FLOATS = STG + (sizeof(TI) == 2 ? 3 * CL * DK / 2 : 0);
     // waves per SIMD the registers are sized for (4: 128 registers, the state
     // tiles take 64 of them at d = 128)
     static constexpr int WPE = 4;
 };
 
-template <int DK, int DV, bool KDA>
-__global__ __launch_bounds__((PF<DK, DV, KDA>::NT))
-__attribute__((amdgpu_waves_per_eu(PF<DK, DV, KDA>::WPE, PF<DK, DV, KDA>::WPE)))
+template <int DK, int DV, bool KDA, typename TI>
+__global__ __launch_bounds__((PF<DK, DV, KDA, TI>::NT))
+__attribute__((amdgpu_waves_per_eu(PF<DK, DV, KDA, TI>::WPE, PF<DK, DV, KDA, TI>::WPE)))
 void prefill_kernel(PrefillArgs a) {
-    using P = PF<DK, DV, KDA>;
+    using P = PF<DK, DV, KDA, TI>;
     constexpr int NW = P::NW, NT = P::NT, RT = P::RT, CTW = P::CTW;
     __shared__ __align__(16) float sm[P::FLOATS];
     float* sQ = sm + P::TOK;
@@ -118,18 +119,28 @@ void prefill_kernel(PrefillArgs a) {
         const int L = min(CL, T - c0);        // tokens of this chunk; the rest are identity steps
         // ---- chunk tokens -> LDS (rows past T repeat the last token; they are masked) ----
         {
-            constexpr int RPC = 256 / DK;                // rows per wave-wide 16-byte copy
-            constexpr int NCOPY = P::NMAT * CL / RPC;
-            const int rin = lane / (DK / 4), off = 4 * (lane % (DK / 4));
+            // q, k, v rows (TI; bf16 into the staging rows), then per-key alpha rows (fp32)
+            constexpr int RB = DK * (int)sizeof(TI);     // bytes per token row
+            constexpr int RPC = 1024 / RB;               // rows per wave-wide 16-byte copy
+            constexpr int NCOPY = (3 * CL + RPC - 1) / RPC;
+            char* tdst = reinterpret_cast<char*>(sizeof(TI) == 4 ? sQ : sm + P::STG);
+            const int rin = lane / (RB / 16), off = 16 * (lane % (RB / 16));
             for (int cp = w; cp < NCOPY; cp += NW) {
-                const int row = cp * RPC + rin;          // row of the [NMAT][CL] stack
+                const int row = cp * RPC + rin;          // row of the [3][CL] stack
+                if (row >= 3 * CL) continue;
                 const int mat = row / CL, n = row % CL;
                 const size_t th = (size_t)min(c0 + n, T - 1) * heads + head;
-                const float* src = mat == 0 ? a.q + th * DK
-                                 : mat == 1 ? a.k + th * DK
-                                 : mat == 2 ? a.v + th * DV
-                                            : a.alpha + th * DK;
-                lds_dma16(src + off, sQ + cp * 256);
+                const void* src = mat == 0 ? a.q : mat == 1 ? a.k : a.v;
+                lds_dma16(reinterpret_cast<const char*>(src) + th * RB + off, tdst + cp * 1024);
+            }
+            if constexpr (KDA) {
+                constexpr int RPCA = 256 / DK;
+                const int rina = lane / (DK / 4), offa = 4 * (lane % (DK / 4));
+                for (int cp = w; cp < CL / RPCA; cp += NW) {
+                    const int n = cp * RPCA + rina;
+                    const size_t th = (size_t)min(c0 + n, T - 1) * heads + head;
+                    lds_dma16(a.alpha + th * DK + offa, sAl + cp * 256);
+                }
             }
             if (w == 0 && lane < 2 * CL) {
                 const int n = lane % CL;
@@ -139,6 +150,17 @@ void prefill_kernel(PrefillArgs a) {
             }
         }
         all_loads_barrier();
+        if constexpr (sizeof(TI) == 2) {
+            // bf16 rows -> the fp32 q | k | v rows (exact)
+            const uint32_t* stg = reinterpret_cast<const uint32_t*>(sm + P::STG);
+#pragma unroll 1
+            for (int e = t; e < 3 * CL * DK / 2; e += NT) {
+                const uint32_t x = stg[e];
+                *reinterpret_cast<float2*>(sQ + 2 * e) = make_float2(__uint_as_float(x << 16),
+                                                                     __uint_as_float(x & 0xffff0000u));
+            }
+            lds_barrier();
+        }
 
         // ---- gates: chunk-local log-decay prefix g, masked beta ------------------------------------
         if constexpr (KDA) {
@@ -280,7 +302,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int n = 4 * lg + v;
-                    if (n < L) a.o[((size_t)(c0 + n) * heads + head) * DV + col] = hq[v];
+                    if (n < L) tok_st<TI>(a.o, ((size_t)(c0 + n) * heads + head) * DV + col, hq[v]);
                 }
             }
             // H = diag(e^{g_L}) H + Kt^T M, Kt[n][row] = e^{g_L - g_n} k_n[row]
@@ -307,8 +329,9 @@ void prefill_kernel(PrefillArgs a) {
 
     // the store addresses are recomputed from an opaque copy of the lane's base, so
     // the load addresses are not kept live through the chunk loop
-    int base = 4 * lg * DV + w * CTW * 16 + li;
-    asm volatile("" : "+v"(base));
+    int tt = threadIdx.x;
+    asm volatile("" : "+v"(tt));
+    const int base = 4 * ((tt & 63) >> 4) * DV + (tt >> 6) * CTW * 16 + (tt & 15);
     float* hb = hp + base;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -320,14 +343,18 @@ void prefill_kernel(PrefillArgs a) {
 
 template <int DK, bool KDA>
 hipError_t prefill_t(const lq_dims& d, const PrefillArgs& args, hipStream_t s) {
-    return launch_kernel(LQ_KERNEL_PREFILL, prefill_kernel<DK, DK, KDA>, dim3((unsigned)d.B * (unsigned)d.H),
-                         dim3(PF<DK, DK, KDA>::NT), s, args);
+    const dim3 grid((unsigned)d.B * (unsigned)d.H);
+    if (d.io_dtype == LQ_IO_BF16)
+        return launch_kernel(LQ_KERNEL_PREFILL, prefill_kernel<DK, DK, KDA, uint16_t>, grid,
+                             dim3(PF<DK, DK, KDA, uint16_t>::NT), s, args);
+    return launch_kernel(LQ_KERNEL_PREFILL, prefill_kernel<DK, DK, KDA, float>, grid,
+                         dim3(PF<DK, DK, KDA, float>::NT), s, args);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const lq_dims& d, float* h, int T, const float* q, const float* k, const float* v,
-                          const float* alpha, const float* beta, float* o, hipStream_t s) {
+hipError_t launch_prefill(const lq_dims& d, float* h, int T, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, void* o, hipStream_t s) {
     PrefillArgs args{h, q, k, v, alpha, beta, o, T, d.B * d.H};
     const bool kda = d.decay_mode == LQ_DECAY_PER_KEY;
     switch (d.dk) {

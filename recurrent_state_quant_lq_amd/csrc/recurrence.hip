@@ -16,17 +16,17 @@ namespace {
 
 struct RecArgs {
     float* h;
-    const float* q;
-    const float* k;
-    const float* v;
+    const void* q;            // q, k, v, o: fp32 or bf16 (the kernel's TI)
+    const void* k;
+    const void* v;
     const float* alpha;
     const float* beta;
-    float* o;
+    void* o;
     int T;
     size_t heads;   // B*H: stride between tokens, in heads
 };
 
-template <int DK, int DV, bool KDA, int NT>
+template <int DK, int DV, bool KDA, int NT, typename TI>
 __global__ __launch_bounds__(NT) void fp32_rec_kernel(RecArgs a) {
     constexpr int CPR4 = DV / 4;
     constexpr int RPP = NT / CPR4;
@@ -54,21 +54,24 @@ __global__ __launch_bounds__(NT) void fp32_rec_kernel(RecArgs a) {
 
     for (int tok = 0; tok < a.T; ++tok) {
         const size_t th = (size_t)tok * a.heads + head;
-        const float* q = a.q + th * DK;
-        const float* k = a.k + th * DK;
         const float* al = a.alpha + th * GD;
         const float beta = a.beta[th];
-        const float4 vv = *reinterpret_cast<const float4*>(a.v + th * DV + c0);
+        float4 vv;
+        if constexpr (sizeof(TI) == 4)
+            vv = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + th * DV + c0);
+        else
+            vv = make_float4(tok_ld<TI>(a.v, th * DV + c0), tok_ld<TI>(a.v, th * DV + c0 + 1),
+                             tok_ld<TI>(a.v, th * DV + c0 + 2), tok_ld<TI>(a.v, th * DV + c0 + 3));
         float kr[PASSES], qr[PASSES], dr[PASSES];
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
             const int row = p * RPP + rg;
-            kr[p] = k[row];
-            qr[p] = q[row];
+            kr[p] = tok_ld<TI>(a.k, th * DK + row);
+            qr[p] = tok_ld<TI>(a.q, th * DK + row);
             dr[p] = KDA ? al[row] : al[0];
         }
         float kq = 0.0f;
-        if (t < DK) kq = k[t] * q[t];
+        if (t < DK) kq = tok_ld<TI>(a.k, th * DK + t) * tok_ld<TI>(a.q, th * DK + t);
         // decay, then the two column reductions
         float4 pp = make_float4(0.f, 0.f, 0.f, 0.f), zz = pp;
 #pragma unroll
@@ -112,7 +115,14 @@ __global__ __launch_bounds__(NT) void fp32_rec_kernel(RecArgs a) {
         if (a.o && rg == 0) {
             float4 ov;
             ov.x = Z.x + u.x * KQ; ov.y = Z.y + u.y * KQ; ov.z = Z.z + u.z * KQ; ov.w = Z.w + u.w * KQ;
-            *reinterpret_cast<float4*>(a.o + th * DV + c0) = ov;
+            if constexpr (sizeof(TI) == 4) {
+                *reinterpret_cast<float4*>(static_cast<float*>(a.o) + th * DV + c0) = ov;
+            } else {
+                tok_st<TI>(a.o, th * DV + c0, ov.x);
+                tok_st<TI>(a.o, th * DV + c0 + 1, ov.y);
+                tok_st<TI>(a.o, th * DV + c0 + 2, ov.z);
+                tok_st<TI>(a.o, th * DV + c0 + 3, ov.w);
+            }
         }
     }
 #pragma unroll
@@ -124,15 +134,18 @@ __global__ __launch_bounds__(NT) void fp32_rec_kernel(RecArgs a) {
 template <int DK, bool KDA>
 hipError_t rec_t(const lq_dims& d, const RecArgs& args, hipStream_t s) {
     constexpr int NT = DK >= 64 ? 256 : 64;
-    return launch_kernel(LQ_KERNEL_FP32_RECURRENCE, fp32_rec_kernel<DK, DK, KDA, NT>,
+    if (d.io_dtype == LQ_IO_BF16)
+        return launch_kernel(LQ_KERNEL_FP32_RECURRENCE, fp32_rec_kernel<DK, DK, KDA, NT, uint16_t>,
+                             dim3((unsigned)d.B * (unsigned)d.H), dim3(NT), s, args);
+    return launch_kernel(LQ_KERNEL_FP32_RECURRENCE, fp32_rec_kernel<DK, DK, KDA, NT, float>,
                          dim3((unsigned)d.B * (unsigned)d.H), dim3(NT), s, args);
 }
 
 }  // namespace
 
-hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const float* q,
-                                  const float* k, const float* v, const float* alpha,
-                                  const float* beta, float* o, hipStream_t s) {
+hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const void* q,
+                                  const void* k, const void* v, const float* alpha,
+                                  const float* beta, void* o, hipStream_t s) {
     RecArgs args{h, q, k, v, alpha, beta, o, T, (size_t)d.B * (size_t)d.H};
     const bool kda = d.decay_mode == LQ_DECAY_PER_KEY;
     switch (d.dk) {

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "liblq.so")
 LQ_OK, LQ_ERR_NULL, LQ_ERR_DIMS, LQ_ERR_UNSUPPORTED, LQ_ERR_WINDOW_FULL, LQ_ERR_POS, \
     LQ_ERR_ALIGN, LQ_ERR_HIP = range(8)
 LQ_DECAY_SCALAR, LQ_DECAY_PER_KEY = 0, 1
+LQ_IO_F32, LQ_IO_BF16 = 0, 1
 
 # every symbol include/lq.h declares
 EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_ragged",
@@ -36,7 +37,8 @@ LQ_KERNEL_DECODE, LQ_KERNEL_FLUSH, LQ_KERNEL_QUANTIZE, LQ_KERNEL_DEQUANTIZE, \
 
 
 class lq_dims(ct.Structure):
-    _fields_ = [(n, ct.c_int32) for n in ("B", "H", "dk", "dv", "W", "C", "decay_mode", "smooth")]
+    _fields_ = [(n, ct.c_int32) for n in ("B", "H", "dk", "dv", "W", "C", "decay_mode", "smooth",
+                                          "io_dtype")]
 
 
 class lq_state(ct.Structure):
@@ -103,8 +105,17 @@ def load() -> ct.CDLL:
     return _lib
 
 
-def make_dims(B, H, dk, dv, W, C, decay_mode=LQ_DECAY_SCALAR, smooth=1) -> lq_dims:
-    return lq_dims(B, H, dk, dv, W, C, decay_mode, smooth)
+def make_dims(B, H, dk, dv, W, C, decay_mode=LQ_DECAY_SCALAR, smooth=1, io_dtype=LQ_IO_F32) -> lq_dims:
+    return lq_dims(B, H, dk, dv, W, C, decay_mode, smooth, io_dtype)
+
+
+def io_torch_dtype(d: lq_dims):
+    """torch dtype of the token vectors q, k, v and outputs o for these dims."""
+    return torch.bfloat16 if d.io_dtype == LQ_IO_BF16 else torch.float32
+
+
+def _dtype_of(d: lq_dims, name: str):
+    return io_torch_dtype(d) if name in ("q", "k", "v", "o") else torch.float32
 
 
 def _ptr(t):
@@ -212,7 +223,7 @@ def lq_gdn_decode_step(st: LayerState, pos: int, q, k, v, alpha, beta, o, stream
     st.check()
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
-        _check(t, name, sh[name], torch.float32)
+        _check(t, name, sh[name], _dtype_of(d, name))
     cs = st.c_state()
     rc = load().lq_gdn_decode_step(ct.byref(d), ct.byref(cs), int(pos), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
@@ -237,7 +248,7 @@ def lq_gdn_decode_step_flush(st: LayerState, pos: int, q, k, v, alpha, beta, o, 
     st.check()
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
-        _check(t, name, sh[name], torch.float32)
+        _check(t, name, sh[name], _dtype_of(d, name))
     if h_out is not None:
         _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
     cs = st.c_state()
@@ -255,7 +266,7 @@ def lq_gdn_decode_step_flush_ragged(st: LayerState, pos, q, k, v, alpha, beta, o
     _check(pos, "pos", (d.B,), torch.int32)
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
-        _check(t, name, sh[name], torch.float32)
+        _check(t, name, sh[name], _dtype_of(d, name))
     if h_out is not None:
         _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
     cs = st.c_state()
@@ -272,7 +283,7 @@ def lq_gdn_decode_step_ragged(st: LayerState, pos, q, k, v, alpha, beta, o, stre
     _check(pos, "pos", (d.B,), torch.int32)
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
-        _check(t, name, sh[name], torch.float32)
+        _check(t, name, sh[name], _dtype_of(d, name))
     cs = st.c_state()
     rc = load().lq_gdn_decode_step_ragged(ct.byref(d), ct.byref(cs), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
@@ -314,9 +325,9 @@ def lq_gdn_fp32_recurrence(d: lq_dims, h, T: int, q, k, v, alpha, beta, o=None, 
     _check(h, "h", (d.B, d.H, d.dk, d.dv), torch.float32)
     sh = _token_shapes(d, T)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
-        _check(t, name, sh[name], torch.float32)
+        _check(t, name, sh[name], _dtype_of(d, name))
     if o is not None:
-        _check(o, "o", sh["o"], torch.float32)
+        _check(o, "o", sh["o"], _dtype_of(d, "o"))
     rc = load().lq_gdn_fp32_recurrence(ct.byref(d), _ptr(h), int(T), _ptr(q), _ptr(k), _ptr(v),
                                        _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
     _raise("lq_gdn_fp32_recurrence", rc)
@@ -329,9 +340,9 @@ def lq_gdn_prefill(d: lq_dims, st, h, T: int, q, k, v, alpha, beta, o=None, stre
     sh = _token_shapes(d, T)
     if T > 0:
         for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
-            _check(t, name, sh[name], torch.float32)
+            _check(t, name, sh[name], _dtype_of(d, name))
     if o is not None:
-        _check(o, "o", sh["o"], torch.float32)
+        _check(o, "o", sh["o"], _dtype_of(d, "o"))
     cs = None
     if st is not None:
         st.check(with_buffer=False)

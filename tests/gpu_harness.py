@@ -26,6 +26,10 @@ from recurrent_state_quant_lq_amd import inputs, lq
 from recurrent_state_quant_lq_amd.configs import Workload
 
 O_TOL = 2e-3      # max relative error on o_t (norm-wise per token and head)
+# bf16 outputs: bf16 keeps 8 significant bits, so rounding to nearest moves
+# each element by at most half an ulp, 2^-8 of itself (so of the row's max),
+# on top of the fp32 path's error (well under 1e-4)
+O_TOL_BF16 = 2.0 ** -8 + 1e-4
 H_TOL = 1e-5      # rebuilt fp32 state vs oracle fp64 state (max-abs relative)
 BUF_TOL = 1e-5    # WY buffer rows (max-abs relative per slot)
 
@@ -35,10 +39,23 @@ def say(*a):
     sys.stdout.flush()
 
 
-def dims_of(wl: Workload, W=None, C=None, smooth=None) -> lq.lq_dims:
+def dims_of(wl: Workload, W=None, C=None, smooth=None, io_bf16=False) -> lq.lq_dims:
     return lq.make_dims(wl.B, wl.H, wl.dk, wl.dv, W or wl.W, wl.C if C is None else C,
                         lq.LQ_DECAY_PER_KEY if wl.per_key else lq.LQ_DECAY_SCALAR,
-                        wl.smooth if smooth is None else smooth)
+                        wl.smooth if smooth is None else smooth,
+                        lq.LQ_IO_BF16 if io_bf16 else lq.LQ_IO_F32)
+
+
+def io_tokens(tk: dict, bf16: bool) -> dict:
+    """q, k, v as the library's token dtype (bf16: rounded once, here)."""
+    if not bf16:
+        return tk
+    return {k: (v.to(torch.bfloat16) if k in ("q", "k", "v") else v) for k, v in tk.items()}
+
+
+def host(x) -> np.ndarray:
+    """Device tensor (fp32 or bf16) -> fp32 numpy (bf16 widens exactly)."""
+    return x.float().cpu().numpy()
 
 
 def rel_err(a, b, axis=-1):
@@ -144,10 +161,10 @@ def prefill_state(wl: Workload, src: TokenSource, st: lq.LayerState, sample, chu
         Hs = {bh: np.zeros((dk, dv)) for bh in sample}
         for t0 in range(0, wl.prefill, chunk):
             t1 = min(wl.prefill, t0 + chunk)
-            tk = src.tokens(t0, t1)
+            tk = io_tokens(src.tokens(t0, t1), d.io_dtype == lq.LQ_IO_BF16)
             lq.lq_gdn_fp32_recurrence(d, h, t1 - t0, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"])
             for (b, hh) in sample:
-                ht = {k: v[:, b, hh].cpu().numpy() for k, v in tk.items()}
+                ht = {k: host(v[:, b, hh]) for k, v in tk.items()}
                 _, _, Hs[(b, hh)], _ = O.run_head(dk, dv, wl.per_key, t1 - t0, 0, 1, route=0,
                                                   use_codec=False, tok=ht, H0=Hs[(b, hh)])
         lq.lq_gdn_state_quantize(st, h)
@@ -160,22 +177,24 @@ def prefill_state(wl: Workload, src: TokenSource, st: lq.LayerState, sample, chu
 
 
 def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smooth=None,
-               T=None, check_buffers=True, log_every=0, fused=False) -> Report:
+               T=None, check_buffers=True, log_every=0, fused=False, io_bf16=False) -> Report:
     """fused: each window's last token goes through lq_gdn_decode_step_flush
-    (decode + flush in one launch) instead of a decode step and a flush."""
-    d = dims_of(wl, W, C, smooth)
+    (decode + flush in one launch) instead of a decode step and a flush.
+    io_bf16: q, k, v and o in bf16 (the oracle gets the bf16 values widened)."""
+    d = dims_of(wl, W, C, smooth, io_bf16)
     W, T = d.W, (T if T is not None else wl.T)
     src = TokenSource(wl, host_tokens)
     st = lq.LayerState.allocate(d)
     codec = prefill_state(wl, src, st, sample)
     rep = Report(heads=len(sample))
-    o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+    iot = lq.io_torch_dtype(d)
+    o = torch.empty((wl.B, wl.H, wl.dv), dtype=iot, device="cuda")
     h_out = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
     t = 0
     while t < T:
         N = min(W, T - t)
-        tk = src.tokens(wl.prefill + t, wl.prefill + t + N)
-        outs = torch.empty((N, wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+        tk = io_tokens(src.tokens(wl.prefill + t, wl.prefill + t + N), io_bf16)
+        outs = torch.empty((N, wl.B, wl.H, wl.dv), dtype=iot, device="cuda")
         for n in range(N):
             args = (tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o)
             if fused and n == N - 1:
@@ -190,9 +209,9 @@ def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smoot
                 if check_buffers else None)
         torch.cuda.synchronize()
         for (b, h) in sample:
-            ht = {k: v[:, b, h].cpu().numpy() for k, v in tk.items()}
+            ht = {k: host(v[:, b, h]) for k, v in tk.items()}
             res = O.window(codec[(b, h)], ht, wl.per_key, W, d.C, d.smooth, route="wy")
-            rep.o_err = max(rep.o_err, rel_err(outs[:, b, h].cpu().numpy(), res["o"]))
+            rep.o_err = max(rep.o_err, rel_err(host(outs[:, b, h]), res["o"]))
             hg = h_out[b, h].cpu().numpy()
             rep.h_err = max(rep.h_err, float(np.abs(hg - res["H"]).max() / max(np.abs(res["H"]).max(), 1e-30)))
             if check_buffers:

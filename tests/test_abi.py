@@ -34,9 +34,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def _dims(**kw):
-    base = dict(B=2, H=3, dk=128, dv=128, W=16, C=4, decay_mode=0, smooth=1)
+    base = dict(B=2, H=3, dk=128, dv=128, W=16, C=4, decay_mode=0, smooth=1, io_dtype=0)
     base.update(kw)
-    return lq.lq_dims(*[base[n] for n in ("B", "H", "dk", "dv", "W", "C", "decay_mode", "smooth")])
+    return lq.lq_dims(*[base[n] for n in ("B", "H", "dk", "dv", "W", "C", "decay_mode", "smooth",
+                                          "io_dtype")])
 
 
 def test_sizes():
@@ -56,6 +57,7 @@ def test_sizes():
     (dict(B=0), lq.LQ_ERR_DIMS), (dict(H=-1), lq.LQ_ERR_DIMS), (dict(W=0), lq.LQ_ERR_DIMS),
     (dict(C=-1), lq.LQ_ERR_DIMS), (dict(dk=16, dv=16, C=17), lq.LQ_ERR_DIMS),
     (dict(decay_mode=2), lq.LQ_ERR_DIMS), (dict(smooth=3), lq.LQ_ERR_DIMS),
+    (dict(io_dtype=2), lq.LQ_ERR_DIMS), (dict(io_dtype=-1), lq.LQ_ERR_DIMS), (dict(io_dtype=1), lq.LQ_OK),
     (dict(dk=96, dv=96), lq.LQ_ERR_UNSUPPORTED), (dict(dk=128, dv=64), lq.LQ_ERR_UNSUPPORTED),
     (dict(W=33), lq.LQ_ERR_UNSUPPORTED), (dict(C=9), lq.LQ_ERR_UNSUPPORTED),
     (dict(dk=16, dv=16, W=4, C=1), lq.LQ_OK), (dict(dk=64, dv=64, W=32, C=8), lq.LQ_OK),

@@ -17,8 +17,8 @@ from recurrent_state_quant_lq_amd.configs import PRESETS
 
 pytestmark = pytest.mark.gpu
 
-from gpu_harness import (BUF_TOL, H_TOL, O_TOL, codec_equal, dims_of, head_codec,  # noqa: E402
-                         oracle_buffer, rel_err, resync_run, say, upload_head_codec)
+from gpu_harness import (BUF_TOL, H_TOL, O_TOL, O_TOL_BF16, codec_equal, dims_of, head_codec,  # noqa: E402
+                         host, io_tokens, oracle_buffer, rel_err, resync_run, say, upload_head_codec)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,11 +28,11 @@ def _gpu():
     lq.load()
 
 
-def _check(rep, name):
+def _check(rep, name, o_tol=O_TOL):
     say(f"{name}: windows {rep.windows} heads {rep.heads} o_err {rep.o_err:.3e} "
         f"h_err {rep.h_err:.3e} buf_err {rep.buf_err:.3e} bytes_exact {rep.bytes_exact}")
     assert rep.bytes_exact, rep.mismatches[:5]
-    assert rep.o_err <= O_TOL
+    assert rep.o_err <= o_tol
     assert rep.h_err <= H_TOL
     assert rep.buf_err <= BUF_TOL
 
@@ -182,6 +182,95 @@ def test_fp32_recurrence_kernel(dk, kda):
                                             H0=H0[b, hh].astype(np.float64))
             assert rel_err(o[:, b, hh].cpu().numpy(), o_ref) < 1e-5
             assert np.abs(h[b, hh].cpu().numpy() - H_ref).max() / np.abs(H_ref).max() < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# bf16 token I/O
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,sample,T,fused", [
+    ("tiny_gdn", [(0, 0)], None, False),
+    ("tiny_gdn", [(0, 0)], None, True),
+    ("gdn_layer", [(0, h) for h in range(0, 16, 3)], 64, True),
+    ("kda", [(0, 0), (31, 31)], 48, False),
+])
+def test_bf16_io_presets(name, sample, T, fused):
+    """q, k, v and o in bf16: the resync harness with the oracle fed the bf16
+    values (widened exactly); o to the bf16 bound, buffers, state and codec
+    bytes as for fp32 I/O."""
+    wl = PRESETS[name]
+    _check(resync_run(wl, sample, host_tokens=wl.B * wl.H <= 16, T=T, fused=fused, io_bf16=True),
+           f"bf16 {name} fused={fused}", o_tol=O_TOL_BF16)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_bf16_io_equals_fp32_path_rounded(kda):
+    """At full size, the bf16-I/O path on bf16-valued tokens against the fp32
+    path on the same values: every output is the fp32 output rounded to bf16
+    (bit for bit), and the buffers, codec and fp32 state are identical."""
+    wl = PRESETS["kda" if kda else "gdn_batched"]
+    B, H, dk = wl.B, wl.H, wl.dk
+    say(f"bf16 vs fp32 full size kda={kda}")
+    d32, d16 = dims_of(wl), dims_of(wl, io_bf16=True)
+    tk = io_tokens(inputs.device_tokens(23, wl.W, B, H, dk, dk, per_key=kda, beta_lo=0.1, beta_hi=0.9,
+                                        device="cuda"), True)
+    t32 = {k: (v.float() if k in ("q", "k", "v") else v) for k, v in tk.items()}
+    g = torch.Generator(device="cuda").manual_seed(9)
+    h0 = torch.randn((B, H, dk, dk), device="cuda", generator=g) * 0.3
+    sts = []
+    for d in (d32, d16):
+        st = lq.LayerState.allocate(d)
+        lq.lq_gdn_state_quantize(st, h0)
+        sts.append(st)
+    outs = []
+    for st, d, tkk in ((sts[0], d32, t32), (sts[1], d16, tk)):
+        o = torch.empty((wl.W, B, H, dk), dtype=lq.io_torch_dtype(d), device="cuda")
+        h_out = torch.empty((B, H, dk, dk), device="cuda")
+        for n in range(wl.W):
+            args = (tkk["q"][n], tkk["k"][n], tkk["v"][n], tkk["alpha"][n], tkk["beta"][n], o[n])
+            if n < wl.W - 1:
+                lq.lq_gdn_decode_step(st, n, *args)
+            else:
+                lq.lq_gdn_decode_step_flush(st, n, *args, h_out=h_out)
+        outs.append((o, h_out))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].to(torch.bfloat16), outs[1][0]), "o: bf16 path != fp32 path rounded"
+    assert torch.equal(outs[0][1], outs[1][1]), "h_out"
+    for f in ("sq", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_k", "buf_m", "buf_g"):
+        assert torch.equal(getattr(sts[0], f), getattr(sts[1], f)), f
+
+
+@pytest.mark.parametrize("dk,kda", [(16, False), (64, True), (128, False)])
+def test_bf16_io_prefill_and_recurrence(dk, kda):
+    """lq_gdn_prefill and lq_gdn_fp32_recurrence with bf16 I/O against the
+    oracle on the bf16 token values (outputs to the bf16 bound, state to
+    2e-5, codec bytes of the fp32 state bit-exact)."""
+    B, H, C, T = 2, 3, 4, 37
+    say(f"bf16 prefill/recurrence dk={dk} kda={kda}")
+    tok = inputs.host_tokens(71 + dk, T, B, H, dk, dk, per_key=kda, beta_lo=0.1, beta_hi=0.9)
+    d = lq.make_dims(B, H, dk, dk, 16, C, int(kda), 1, lq.LQ_IO_BF16)
+    tk = io_tokens({k: torch.from_numpy(v).cuda() for k, v in tok.items()}, True)
+    rng = np.random.default_rng(dk)
+    H0 = (rng.standard_normal((B, H, dk, dk)) * 0.3).astype(np.float32)
+    for which in ("prefill", "recurrence"):
+        h = torch.from_numpy(H0).cuda()
+        o = torch.empty((T, B, H, dk), dtype=torch.bfloat16, device="cuda")
+        st = lq.LayerState.allocate(d)
+        if which == "prefill":
+            lq.lq_gdn_prefill(d, st, h, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], o)
+        else:
+            lq.lq_gdn_fp32_recurrence(d, h, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], o)
+        torch.cuda.synchronize()
+        for b in range(B):
+            for hh in range(H):
+                ht = {k: host(v[:, b, hh]) for k, v in tk.items()}
+                o_ref, _, H_ref, _ = O.run_head(dk, dk, kda, T, 0, 1, route=0, use_codec=False, tok=ht,
+                                                H0=H0[b, hh].astype(np.float64))
+                assert rel_err(host(o[:, b, hh]), o_ref) <= O_TOL_BF16, (which, b, hh)
+                hg = h[b, hh].cpu().numpy()
+                assert np.abs(hg - H_ref).max() / np.abs(H_ref).max() < 2e-5, (which, b, hh)
+                if which == "prefill":
+                    assert codec_equal(head_codec(st, b, hh), O.quantize(hg, C, 1)), (b, hh)
 
 
 # ---------------------------------------------------------------------------
