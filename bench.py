@@ -397,6 +397,30 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
                          "pack_hbm_GBps": round(2 * nb / (pk * 1e-6) / 1e9, 1),
                          "unpack_hbm_GBps": round(2 * nb / (uk * 1e-6) / 1e9, 1)}
     del stc, blob
+    # (f4) the same lockstep step with bf16 token I/O (q, k, v, o)
+    db = lq.make_dims(B, H, dk, dv, W, wl.C, d.decay_mode, d.smooth, lq.LQ_IO_BF16)
+    layb = [lq.LayerState.allocate(db, h0.device) for _ in range(L)]
+    for st in layb:
+        lq.lq_gdn_state_quantize(st, h0)
+    ringb = [{k: (v.to(torch.bfloat16) if k in ("q", "k", "v") else v) for k, v in tk.items()} for tk in ring]
+    ob = torch.empty((B, H, dv), dtype=torch.bfloat16, device=h0.device)
+
+    def bf16_step():
+        for n in range(W - 1):
+            for l in range(L):
+                tk = ringb[l]
+                lq.lq_gdn_decode_step(layb[l], n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                      tk["beta"][n], ob)
+        for l in range(L):
+            tk, n = ringb[l], W - 1
+            lq.lq_gdn_decode_step_flush(layb[l], n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                        tk["beta"][n], ob)
+    tpsb, msb = timed(bf16_step, B * W * L)
+    decb = kernel_us(bf16_step, lq.LQ_KERNEL_DECODE)
+    out["bf16_io"] = {"tokens_per_s": round(tpsb, 1), "ms_per_step": round(msb, 4),
+                      "vs_fp32_io": round(tpsb / lq_value, 3), "decode_avg_launch_us": round(decb, 3)}
+    del layb, ringb
+    torch.cuda.empty_cache()
     # (f2) prefill of a 128-token prompt chunk: chunked fp32 form (lq_gdn_prefill,
     # without its final quantization) against the token-by-token fp32 recurrence
     Tp = 128
