@@ -79,14 +79,16 @@ def decode_flush_bytes(wl, N: int) -> int:
 
 
 def family(name: str):
-    """Kernel family of a rocprofv3 kernel name: decode, flush or decode_flush
-    (the flush kernel's instantiation with the fused decode, last template
-    argument true)."""
+    """Kernel family of a rocprofv3 kernel name: decode, prefill, flush or
+    decode_flush (the flush kernel's instantiation with the fused decode)."""
     if "decode_kernel" in name:
         return "decode"
+    if "prefill_kernel" in name:
+        return "prefill"
     m = re.search(r"flush_kernel<([^>]*)>", name)
     if m:
-        return "decode_flush" if m.group(1).replace(" ", "").endswith(",true") else "flush"
+        args = m.group(1).replace(" ", "").split(",")   # DK, DV, WM, KDA, DEC[, token type]
+        return "decode_flush" if len(args) > 4 and args[4] == "true" else "flush"
     return None
 
 
@@ -133,7 +135,7 @@ def trace_summary(out_md: str, stats_csv: str, command: str):
              "Command (from the repository root; rocprofv3 writes `*_kernel_stats.csv`):", "",
              "```", command, "```", "",
              "| kernel | calls | average us | min us | max us |", "|---|---:|---:|---:|---:|"]
-    fams = {"decode": [], "flush": [], "decode_flush": []}
+    fams = {"decode": [], "flush": [], "decode_flush": [], "prefill": []}
     other = 0
     for r in rows:
         if "lq::" not in r["Name"]:

@@ -56,12 +56,16 @@ struct PF {
     static constexpr int RT = DK / 16;                     // row tiles
     static constexpr int CTW = DV / 16 / NW;               // column tiles per wave
     static constexpr int NMAT = KDA ? 4 : 3;               // q, k, v [, alpha] rows per chunk
+    // token rows are DKP floats apart in LDS: the 16-byte pad puts row n's word
+    // c in bank (4n + c) mod 64, so reads of one column across rows, or of
+    // 16-byte pieces of 16 rows, do not collide
+    static constexpr int DKP = DK + 4;
     // LDS (floats)
-    static constexpr int TOK = 0;                          // [NMAT][CL][DK]: q | k | v [| alpha -> g]
-    static constexpr int XK = TOK + NMAT * CL * DK;        // per-key: e^g o k, e^g o q, e^{gL-g} o k
-    static constexpr int XQ = XK + (KDA ? CL * DK : 0);
-    static constexpr int KT = XQ + (KDA ? CL * DK : 0);
-    static constexpr int DL = KT + (KDA ? CL * DK : 0);    // per-key: e^{gL} [DK]
+    static constexpr int TOK = 0;                          // [NMAT][CL][DKP]: q | k | v [| alpha -> g]
+    static constexpr int XK = TOK + NMAT * CL * DKP;       // per-key: e^g o k, e^g o q, e^{gL-g} o k
+    static constexpr int XQ = XK + (KDA ? CL * DKP : 0);
+    static constexpr int KT = XQ + (KDA ? CL * DKP : 0);
+    static constexpr int DL = KT + (KDA ? CL * DKP : 0);   // per-key: e^{gL} [DK]
     static constexpr int AB = DL + (KDA ? DK : 0);         // alpha [CL] | beta [CL] (raw)
     static constexpr int G = AB + 2 * CL;                  // scalar: g [CL]; beta masked [CL]
     static constexpr int SA = G + 2 * CL;                  // A = beta rr (strictly lower) [CL][CL]
@@ -79,12 +83,12 @@ __global__ __launch_bounds__((PF<DK, DV, KDA, TI>::NT))
 __attribute__((amdgpu_waves_per_eu(PF<DK, DV, KDA, TI>::WPE, PF<DK, DV, KDA, TI>::WPE)))
 void prefill_kernel(PrefillArgs a) {
     using P = PF<DK, DV, KDA, TI>;
-    constexpr int NW = P::NW, NT = P::NT, RT = P::RT, CTW = P::CTW;
+    constexpr int NW = P::NW, NT = P::NT, RT = P::RT, CTW = P::CTW, DKP = P::DKP;
     __shared__ __align__(16) float sm[P::FLOATS];
     float* sQ = sm + P::TOK;
-    float* sK = sQ + CL * DK;
-    float* sV = sK + CL * DK;
-    float* sAl = sV + CL * DV;                // per-key alpha, then g (in place)
+    float* sK = sQ + CL * DKP;
+    float* sV = sK + CL * DKP;
+    float* sAl = sV + CL * DKP;               // per-key alpha, then g (in place)
     float* sXk = sm + P::XK;
     float* sXq = sm + P::XQ;
     float* sKt = sm + P::KT;
@@ -119,34 +123,46 @@ void prefill_kernel(PrefillArgs a) {
         const int L = min(CL, T - c0);        // tokens of this chunk; the rest are identity steps
         // ---- chunk tokens -> LDS (rows past T repeat the last token; they are masked) ----
         {
-            // q, k, v rows (TI; bf16 into the staging rows), then per-key alpha rows (fp32)
-            constexpr int RB = DK * (int)sizeof(TI);     // bytes per token row
-            constexpr int RPC = 1024 / RB;               // rows per wave-wide 16-byte copy
-            constexpr int NCOPY = (3 * CL + RPC - 1) / RPC;
-            char* tdst = reinterpret_cast<char*>(sizeof(TI) == 4 ? sQ : sm + P::STG);
-            const int rin = lane / (RB / 16), off = 16 * (lane % (RB / 16));
-            for (int cp = w; cp < NCOPY; cp += NW) {
-                const int row = cp * RPC + rin;          // row of the [3][CL] stack
-                if (row >= 3 * CL) continue;
-                const int mat = row / CL, n = row % CL;
-                const size_t th = (size_t)min(c0 + n, T - 1) * heads + head;
-                const void* src = mat == 0 ? a.q : mat == 1 ? a.k : a.v;
-                lds_dma16(reinterpret_cast<const char*>(src) + th * RB + off, tdst + cp * 1024);
-            }
-            if constexpr (KDA) {
-                constexpr int RPCA = 256 / DK;
-                const int rina = lane / (DK / 4), offa = 4 * (lane % (DK / 4));
-                for (int cp = w; cp < CL / RPCA; cp += NW) {
-                    const int n = cp * RPCA + rina;
+            if constexpr (sizeof(TI) == 4) {
+                // one copy per row into its padded LDS row (DK/4 lanes of 16 bytes)
+                for (int row = w; row < P::NMAT * CL; row += NW) {
+                    const int mat = row / CL, n = row % CL;
                     const size_t th = (size_t)min(c0 + n, T - 1) * heads + head;
-                    lds_dma16(a.alpha + th * DK + offa, sAl + cp * 256);
+                    const float* src = mat == 0 ? static_cast<const float*>(a.q) + th * DK
+                                     : mat == 1 ? static_cast<const float*>(a.k) + th * DK
+                                     : mat == 2 ? static_cast<const float*>(a.v) + th * DV
+                                                : a.alpha + th * DK;
+                    if (lane < DK / 4) lds_dma16(src + 4 * lane, sQ + row * DKP);
+                }
+            } else {
+                // bf16 q, k, v rows as they are into the staging rows, whole copies
+                constexpr int RB = DK * 2;                   // bytes per token row
+                constexpr int RPC = 1024 / RB;               // rows per wave-wide 16-byte copy
+                constexpr int NCOPY = (3 * CL + RPC - 1) / RPC;
+                char* tdst = reinterpret_cast<char*>(sm + P::STG);
+                const int rin = lane / (RB / 16), off = 16 * (lane % (RB / 16));
+                for (int cp = w; cp < NCOPY; cp += NW) {
+                    const int row = cp * RPC + rin;          // row of the [3][CL] stack
+                    if (row >= 3 * CL) continue;
+                    // one matrix per copy when its rows divide the chunk (a scalar choice)
+                    const int mat = CL % RPC == 0 ? cp * RPC / CL : row / CL, n = row % CL;
+                    const size_t th = (size_t)min(c0 + n, T - 1) * heads + head;
+                    const void* src = mat == 0 ? a.q : mat == 1 ? a.k : a.v;
+                    lds_dma16(reinterpret_cast<const char*>(src) + th * RB + off, tdst + cp * 1024);
+                }
+                if constexpr (KDA) {
+                    for (int n = w; n < CL; n += NW) {
+                        const size_t th = (size_t)min(c0 + n, T - 1) * heads + head;
+                        if (lane < DK / 4) lds_dma16(a.alpha + th * DK + 4 * lane, sAl + n * DKP);
+                    }
                 }
             }
             if (w == 0 && lane < 2 * CL) {
+                // lanes 0..15: scalar alpha (per-key: unused), lanes 16..31: beta
                 const int n = lane % CL;
                 const size_t th = (size_t)min(c0 + n, T - 1) * heads + head;
-                const float* src = lane < CL ? (KDA ? a.beta + th : a.alpha + th) : a.beta + th;
-                lds_dma4(src, sAB);
+                if (lane < CL) lds_dma4((KDA ? a.beta : a.alpha) + th, sAB);
+                else lds_dma4(a.beta + th, sAB);
             }
         }
         all_loads_barrier();
@@ -156,8 +172,9 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll 1
             for (int e = t; e < 3 * CL * DK / 2; e += NT) {
                 const uint32_t x = stg[e];
-                *reinterpret_cast<float2*>(sQ + 2 * e) = make_float2(__uint_as_float(x << 16),
-                                                                     __uint_as_float(x & 0xffff0000u));
+                const int row = 2 * e / DK, col = 2 * e % DK;
+                *reinterpret_cast<float2*>(sQ + row * DKP + col) =
+                    make_float2(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
             }
             lds_barrier();
         }
@@ -168,17 +185,17 @@ void prefill_kernel(PrefillArgs a) {
                 float g = 0.0f;
 #pragma unroll
                 for (int n = 0; n < CL; ++n) {
-                    g += n < L ? logf(sAl[n * DK + t]) : 0.0f;
-                    sAl[n * DK + t] = g;
+                    g += n < L ? logf(sAl[n * DKP + t]) : 0.0f;
+                    sAl[n * DKP + t] = g;
                 }
                 sDl[t] = __expf(g);
 #pragma unroll
                 for (int n = 0; n < CL; ++n) {
-                    const float gn = sAl[n * DK + t];
+                    const float gn = sAl[n * DKP + t];
                     const float e = __expf(gn);
-                    sXk[n * DK + t] = e * sK[n * DK + t];
-                    sXq[n * DK + t] = e * sQ[n * DK + t];
-                    sKt[n * DK + t] = __expf(g - gn) * sK[n * DK + t];
+                    sXk[n * DKP + t] = e * sK[n * DKP + t];
+                    sXq[n * DKP + t] = e * sQ[n * DKP + t];
+                    sKt[n * DKP + t] = __expf(g - gn) * sK[n * DKP + t];
                 }
             }
         } else if (t == 0) {
@@ -201,11 +218,11 @@ void prefill_kernel(PrefillArgs a) {
                 if (i <= n) {
                     for (int c = 0; c < DK; c += 4) {
                         float kn[4], ki[4], qn[4], gn[4], gi[4];
-                        load_floats<4>(sK + n * DK + c, kn);
-                        load_floats<4>(sK + i * DK + c, ki);
-                        load_floats<4>(sQ + n * DK + c, qn);
-                        load_floats<4>(sAl + n * DK + c, gn);
-                        load_floats<4>(sAl + i * DK + c, gi);
+                        load_floats<4>(sK + n * DKP + c, kn);
+                        load_floats<4>(sK + i * DKP + c, ki);
+                        load_floats<4>(sQ + n * DKP + c, qn);
+                        load_floats<4>(sAl + n * DKP + c, gn);
+                        load_floats<4>(sAl + i * DKP + c, gi);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float x = ki[e] * __expf(gn[e] - gi[e]);
@@ -227,7 +244,7 @@ void prefill_kernel(PrefillArgs a) {
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
                 for (int ks = 0; ks < DK / 4; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[li * DK + 4 * ks + lg], sK[li * DK + 4 * ks + lg],
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[li * DKP + 4 * ks + lg], sK[li * DKP + 4 * ks + lg],
                                                                acc, 0, 0, 0);
                 // D[n = 4lg+v][i = li]
 #pragma unroll
@@ -276,8 +293,8 @@ void prefill_kernel(PrefillArgs a) {
             for (int rt = 0; rt < RT; ++rt) {
                 // A operands of rows rt*16 + 4*lg + (0..3): one 16-byte read per vector
                 float ak[4], aq[4];
-                load_floats<4>((KDA ? sXk : sK) + li * DK + rt * 16 + 4 * lg, ak);
-                load_floats<4>((KDA ? sXq : sQ) + li * DK + rt * 16 + 4 * lg, aq);
+                load_floats<4>((KDA ? sXk : sK) + li * DKP + rt * 16 + 4 * lg, ak);
+                load_floats<4>((KDA ? sXq : sQ) + li * DKP + rt * 16 + 4 * lg, aq);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     hk = __builtin_amdgcn_mfma_f32_16x16x4f32(KDA ? ak[v] : ak[v] * eg, H[rt][ct][v], hk, 0, 0, 0);
@@ -290,7 +307,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int n = 4 * lg + v;
-                r[v] = sBm[n] * (sV[n * DV + col] - hk[v]);
+                r[v] = sBm[n] * (sV[n * DKP + col] - hk[v]);
             }
 #pragma unroll
             for (int kv = 0; kv < 4; ++kv)
@@ -318,7 +335,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int kv = 0; kv < 4; ++kv) {
                     const int n = 4 * lg + kv, row = rt * 16 + li;
-                    const float av = KDA ? sKt[n * DK + row] : sK[n * DK + row] * ekt[kv];
+                    const float av = KDA ? sKt[n * DKP + row] : sK[n * DKP + row] * ekt[kv];
                     H[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, m[kv], H[rt][ct], 0, 0, 0);
                 }
                 if (rt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
