@@ -537,6 +537,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the fp32-state and per-token int8 comparisons")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as eager launches instead of replaying it as a HIP graph")
     ap.add_argument("--no-fuse", action="store_true",
                     help="end each window with lq_gdn_decode_step + lq_gdn_window_flush "
                          "instead of the fused lq_gdn_decode_step_flush")
@@ -620,18 +622,35 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    def time_steps(run, k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(k):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    # The step is captured once as a HIP graph and replayed, as a serving loop
+    # does, so the host's per-call cost (argument checks, ctypes, launch) is
+    # out of the timed loop; the eager rate is reported beside it.
+    run = step
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(max(1, args.warmup)):
+            run()
+        torch.cuda.synchronize()
+
     # ---- timed region ---------------------------------------------------------
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        step()
-    t_end.record()
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
+    ms = time_steps(run, args.steps)
     tokens_per_step = wl.B * W * L
     value = tokens_per_step / (ms * 1e-3)
+    eager_ms = time_steps(step, max(4, min(16, args.steps))) if not args.eager else ms
 
     # ---- per-launch kernel durations ---------------------------------------------
     # The library's timing hook gives each launch a start/stop event pair bound
@@ -662,21 +681,14 @@ def main():
     fl_gbs = fl_alg / (fl_avg_us * 1e-6) / 1e9
     fl_tfs = flush_flops(wl, W) / (fl_avg_us * 1e-6) / 1e12
     # the same step ending each window with a decode launch and a flush launch
+    # (eager, like the eager rate of the fused step it is set against)
     two_call = None
     if fuse and not args.no_compare:
-        k2 = max(4, min(16, args.steps))
         step(False)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(k2):
-            step(False)
-        e1.record()
-        torch.cuda.synchronize()
-        ms2 = e0.elapsed_time(e1) / k2
+        ms2 = time_steps(lambda: step(False), max(4, min(16, args.steps)))
         two_call = {"ms_per_step": round(ms2, 4), "tokens_per_s": round(tokens_per_step / (ms2 * 1e-3), 1),
-                    "speedup_fused": round(ms2 / ms, 3),
-                    "step": "last token by lq_gdn_decode_step, then lq_gdn_window_flush"}
+                    "speedup_fused": round(ms2 / eager_ms, 3),
+                    "step": "last token by lq_gdn_decode_step, then lq_gdn_window_flush (eager)"}
 
     hsh = kernel_hash()
     traffic = read_traffic(wl, hsh)
@@ -698,6 +710,9 @@ def main():
                             if fuse else f"{W} decode tokens + 1 flush") + f" for each of {L} layers",
                    "value_per": "tokens through one GDN layer per second",
                    "prefill": wl.prefill},
+        "launch": {"mode": "eager" if args.eager else "hip_graph_replay",
+                   "eager_ms_per_step": round(eager_ms, 4),
+                   "eager_tokens_per_s": round(tokens_per_step / (eager_ms * 1e-3), 1)},
         "roofline": roof,
         "state_GBps": round(dec_gbs, 1),
         ("decode_flush" if fuse else "flush"): {
@@ -710,8 +725,9 @@ def main():
     if not args.no_compare:
         del layers
         torch.cuda.empty_cache()
-        res["comparisons"] = comparisons(wl, L, d, h_prefill, ring, value, dec_total_s * 1e6 / ND,
-                                         max(4, min(16, args.steps)))
+        # every comparison runs eager launches, so it is set against the eager rate
+        res["comparisons"] = comparisons(wl, L, d, h_prefill, ring, tokens_per_step / (eager_ms * 1e-3),
+                                         dec_total_s * 1e6 / ND, max(4, min(16, args.steps)))
         if two_call:
             res["comparisons"]["two_call_window_end"] = two_call
     del h_prefill

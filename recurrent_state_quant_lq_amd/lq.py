@@ -129,6 +129,9 @@ def _stream(stream):
 
 
 def _check(t: torch.Tensor, name: str, shape, dtype):
+    # one fast test of the usual case; the detailed messages below otherwise
+    if t is not None and t.dtype == dtype and t.shape == shape and t.is_cuda and t.is_contiguous():
+        return
     if t is None:
         raise ValueError(f"{name} is required")
     if not t.is_cuda:
@@ -144,6 +147,9 @@ def _check(t: torch.Tensor, name: str, shape, dtype):
 def _raise(fn, rc):
     if rc != LQ_OK:
         raise LQError(fn, rc)
+
+
+_STATE_FIELDS = ("sq", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_k", "buf_m", "buf_g")
 
 
 @dataclass
@@ -186,9 +192,19 @@ class LayerState:
             _check(self.buf_g, "buf_g", (B, H, W, gd), torch.float32)
 
     def c_state(self) -> lq_state:
-        return lq_state(*[_ptr(getattr(self, n)) for n in
-                          ("sq", "row_scale", "col_scale", "comp_idx", "comp_val",
-                           "buf_k", "buf_m", "buf_g")])
+        return lq_state(*[_ptr(getattr(self, n)) for n in _STATE_FIELDS])
+
+    def ready(self, with_buffer=True) -> lq_state:
+        """The C struct of this state, validated (shapes, dtypes, device) once
+        for the tensors the fields hold; a field replaced by another tensor is
+        validated again.  In-place writes to the tensors need no revalidation."""
+        key = (tuple(id(getattr(self, n)) for n in _STATE_FIELDS), with_buffer)
+        c = self.__dict__.get("_ready")
+        if c is None or c[0] != key:
+            self.check(with_buffer)
+            c = (key, self.c_state())
+            self.__dict__["_ready"] = c
+        return c[1]
 
     def codec(self) -> dict:
         """Host copies of the codec arrays, int8 matrix row-major [B,H,dk,dv]
@@ -211,20 +227,27 @@ class LayerState:
             self.comp_val[..., :C, :].copy_(torch.as_tensor(cd["cv"]))
 
 
+_SHAPES: dict = {}
+
+
 def _token_shapes(d: lq_dims, T=None):
-    pre = (d.B, d.H) if T is None else (T, d.B, d.H)
-    ash = pre + ((d.dk,) if d.decay_mode == LQ_DECAY_PER_KEY else ())
-    return dict(q=pre + (d.dk,), k=pre + (d.dk,), v=pre + (d.dv,), alpha=ash, beta=pre,
-                o=pre + (d.dv,))
+    key = (d.B, d.H, d.dk, d.dv, d.decay_mode, T)
+    sh = _SHAPES.get(key)
+    if sh is None:
+        pre = (d.B, d.H) if T is None else (T, d.B, d.H)
+        ash = pre + ((d.dk,) if d.decay_mode == LQ_DECAY_PER_KEY else ())
+        sh = {k: torch.Size(v) for k, v in dict(q=pre + (d.dk,), k=pre + (d.dk,), v=pre + (d.dv,),
+                                                alpha=ash, beta=pre, o=pre + (d.dv,)).items()}
+        _SHAPES[key] = sh
+    return sh
 
 
 def lq_gdn_decode_step(st: LayerState, pos: int, q, k, v, alpha, beta, o, stream=None):
     d = st.dims
-    st.check()
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
         _check(t, name, sh[name], _dtype_of(d, name))
-    cs = st.c_state()
+    cs = st.ready()
     rc = load().lq_gdn_decode_step(ct.byref(d), ct.byref(cs), int(pos), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
     _raise("lq_gdn_decode_step", rc)
@@ -232,10 +255,9 @@ def lq_gdn_decode_step(st: LayerState, pos: int, q, k, v, alpha, beta, o, stream
 
 def lq_gdn_window_flush(st: LayerState, n_buffered: int, h_out=None, stream=None):
     d = st.dims
-    st.check()
     if h_out is not None:
         _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
-    cs = st.c_state()
+    cs = st.ready()
     rc = load().lq_gdn_window_flush(ct.byref(d), ct.byref(cs), int(n_buffered), _ptr(h_out),
                                     _stream(stream))
     _raise("lq_gdn_window_flush", rc)
@@ -245,13 +267,12 @@ def lq_gdn_decode_step_flush(st: LayerState, pos: int, q, k, v, alpha, beta, o, 
                              stream=None):
     """Decode of one token into slot pos, then the flush of pos + 1 slots (one launch)."""
     d = st.dims
-    st.check()
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
         _check(t, name, sh[name], _dtype_of(d, name))
     if h_out is not None:
         _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
-    cs = st.c_state()
+    cs = st.ready()
     rc = load().lq_gdn_decode_step_flush(ct.byref(d), ct.byref(cs), int(pos), _ptr(q), _ptr(k),
                                          _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(h_out),
                                          _stream(stream))
@@ -262,14 +283,13 @@ def lq_gdn_decode_step_flush_ragged(st: LayerState, pos, q, k, v, alpha, beta, o
                                     stream=None):
     """pos: device int32 [B]; rows with pos in [0, W) decode slot pos and flush pos + 1 slots."""
     d = st.dims
-    st.check()
     _check(pos, "pos", (d.B,), torch.int32)
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
         _check(t, name, sh[name], _dtype_of(d, name))
     if h_out is not None:
         _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
-    cs = st.c_state()
+    cs = st.ready()
     rc = load().lq_gdn_decode_step_flush_ragged(ct.byref(d), ct.byref(cs), _ptr(pos), _ptr(q), _ptr(k),
                                                 _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(h_out),
                                                 _stream(stream))
@@ -279,12 +299,11 @@ def lq_gdn_decode_step_flush_ragged(st: LayerState, pos, q, k, v, alpha, beta, o
 def lq_gdn_decode_step_ragged(st: LayerState, pos, q, k, v, alpha, beta, o, stream=None):
     """pos: device int32 [B], the window position of each batch row."""
     d = st.dims
-    st.check()
     _check(pos, "pos", (d.B,), torch.int32)
     sh = _token_shapes(d)
     for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("o", o)):
         _check(t, name, sh[name], _dtype_of(d, name))
-    cs = st.c_state()
+    cs = st.ready()
     rc = load().lq_gdn_decode_step_ragged(ct.byref(d), ct.byref(cs), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream))
     _raise("lq_gdn_decode_step_ragged", rc)
@@ -293,11 +312,10 @@ def lq_gdn_decode_step_ragged(st: LayerState, pos, q, k, v, alpha, beta, o, stre
 def lq_gdn_window_flush_ragged(st: LayerState, n_buffered, h_out=None, stream=None):
     """n_buffered: device int32 [B], slots to flush per batch row (0 = none)."""
     d = st.dims
-    st.check()
     _check(n_buffered, "n_buffered", (d.B,), torch.int32)
     if h_out is not None:
         _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
-    cs = st.c_state()
+    cs = st.ready()
     rc = load().lq_gdn_window_flush_ragged(ct.byref(d), ct.byref(cs), _ptr(n_buffered), _ptr(h_out),
                                            _stream(stream))
     _raise("lq_gdn_window_flush_ragged", rc)
@@ -305,18 +323,16 @@ def lq_gdn_window_flush_ragged(st: LayerState, n_buffered, h_out=None, stream=No
 
 def lq_gdn_state_quantize(st: LayerState, h, stream=None):
     d = st.dims
-    st.check(with_buffer=False)
     _check(h, "h", (d.B, d.H, d.dk, d.dv), torch.float32)
-    cs = st.c_state()
+    cs = st.ready(with_buffer=False)
     rc = load().lq_gdn_state_quantize(ct.byref(d), _ptr(h), ct.byref(cs), _stream(stream))
     _raise("lq_gdn_state_quantize", rc)
 
 
 def lq_gdn_state_dequantize(st: LayerState, h_out, stream=None):
     d = st.dims
-    st.check(with_buffer=False)
     _check(h_out, "h_out", (d.B, d.H, d.dk, d.dv), torch.float32)
-    cs = st.c_state()
+    cs = st.ready(with_buffer=False)
     rc = load().lq_gdn_state_dequantize(ct.byref(d), ct.byref(cs), _ptr(h_out), _stream(stream))
     _raise("lq_gdn_state_dequantize", rc)
 
@@ -345,8 +361,7 @@ def lq_gdn_prefill(d: lq_dims, st, h, T: int, q, k, v, alpha, beta, o=None, stre
         _check(o, "o", sh["o"], _dtype_of(d, "o"))
     cs = None
     if st is not None:
-        st.check(with_buffer=False)
-        cs = st.c_state()
+        cs = st.ready(with_buffer=False)
     rc = load().lq_gdn_prefill(ct.byref(d), ct.byref(cs) if cs is not None else None, _ptr(h), int(T),
                                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
                                _stream(stream))
@@ -360,18 +375,16 @@ def lq_checkpoint_bytes(d: lq_dims) -> int:
 def lq_gdn_state_pack(st: LayerState, blob, stream=None):
     """blob: device uint8 tensor of lq_checkpoint_bytes(st.dims) bytes."""
     d = st.dims
-    st.check(with_buffer=False)
     _check(blob, "blob", (lq_checkpoint_bytes(d),), torch.uint8)
-    cs = st.c_state()
+    cs = st.ready(with_buffer=False)
     _raise("lq_gdn_state_pack", load().lq_gdn_state_pack(ct.byref(d), ct.byref(cs), _ptr(blob),
                                                           _stream(stream)))
 
 
 def lq_gdn_state_unpack(st: LayerState, blob, stream=None):
     d = st.dims
-    st.check(with_buffer=False)
     _check(blob, "blob", (lq_checkpoint_bytes(d),), torch.uint8)
-    cs = st.c_state()
+    cs = st.ready(with_buffer=False)
     _raise("lq_gdn_state_unpack", load().lq_gdn_state_unpack(ct.byref(d), _ptr(blob), ct.byref(cs),
                                                               _stream(stream)))
 
