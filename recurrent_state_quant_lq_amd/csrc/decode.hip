@@ -236,12 +236,12 @@ void decode_kernel(DecodeArgs a) {
         const float en = __expf(gn);
         xq = rc * (en * qc);
         xk = rc * (en * kc);
-        a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = kc;
+        st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, kc);
         if constexpr (KDA) {
-            a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = gn;
+            st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, gn);
             s_en[t] = en;
         } else if (t == 0) {
-            a.bg[head * (size_t)W + n] = gn;
+            st_nt(a.bg + head * (size_t)W + n, gn);
         }
     }
     if (w < KS) {
@@ -371,7 +371,7 @@ void decode_kernel(DecodeArgs a) {
                 hk += (e * seg_ld<TI>(s_vec + D::SK * DK, ic)) * cvj;
             }
         const float mn = beta * (seg_ld<TI>(s_vec + D::SV * DK, j) - hk - sr);
-        a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
+        st_nt(a.bm + head * (size_t)W * DV + (size_t)n * DV + j, mn);
         tok_st<TI>(a.o, head * DV + j, hq + sa + s_a[n] * mn);
     }
 }

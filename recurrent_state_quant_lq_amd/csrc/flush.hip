@@ -194,7 +194,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                     h2 &= h2 - 1ull;
                 if (lane == c) mine = r;
             }
-        if (lane < C) out.idx[lane] = mine;
+        if (lane < C) st_nt(out.idx + lane, mine);
     }
     // compensator rows to LDS, residual rows zeroed
     {
@@ -240,13 +240,12 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
         for (int i = 0; i < NW * 4; ++i) mx = umax(mx, __float_as_uint(L.cm[i][t]));
         const float m = __uint_as_float(mx);
         const float sj = (smooth && m >= kTiny) ? m : 1.0f;
-        out.s[t] = sj;
+        st_nt(out.s + t, sj);
         L.sinv[t] = 1.0f / sj;
     }
     for (int e = t; e < C * (DV / 4); e += NT) {
         const int p = e / (DV / 4), j = 4 * (e % (DV / 4));
-        reinterpret_cast<float4*>(out.cv)[e] =
-            make_float4(L.cvt[j][p], L.cvt[j + 1][p], L.cvt[j + 2][p], L.cvt[j + 3][p]);
+        st_nt4(out.cv + 4 * e, L.cvt[j][p], L.cvt[j + 1][p], L.cvt[j + 2][p], L.cvt[j + 3][p]);
     }
     lds_barrier();
     // smoothing and row maxima
@@ -274,7 +273,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
         for (int k = 1; k < RPL; ++k) my = (li % RPL == k) ? rho[k] : my;
         const bool live = my >= kTiny;
         const float lmy = live ? 127.0f / my : 0.0f;
-        if (li < RPL) out.r[row0 + li] = live ? my / 127.0f : 0.0f;
+        if (li < RPL) st_nt(out.r + row0 + li, live ? my / 127.0f : 0.0f);
         row_bcast_all<RPL>(lmy, lam);
     }
     // rounding through the offset form; one column's RPL bytes per store.
@@ -287,10 +286,9 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
         for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
         int8_t* dst = out.sq + (size_t)(li * CT + ct) * DK + row0;
         if constexpr (RPL == 8)
-            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low4(z[0], z[1], z[2], z[3]),
-                                                        pack_low4(z[4], z[5], z[6], z[7]));
+            st_nt2(dst, pack_low4(z[0], z[1], z[2], z[3]), pack_low4(z[4], z[5], z[6], z[7]));
         else
-            *reinterpret_cast<uint32_t*>(dst) = pack_low4(z[0], z[1], z[2], z[3]);
+            st_nt(reinterpret_cast<uint32_t*>(dst), pack_low4(z[0], z[1], z[2], z[3]));
     }
 }
 
@@ -480,9 +478,9 @@ void flush_kernel(FlushArgs a) {
     if constexpr (DEC) {
         // slot n's key and log-decay
         if (t < DK) {
-            a.bk[head * (size_t)W * DK + (size_t)n * DK + t] = seg_ld<TI>(s_K + n * DK, t);
-            if constexpr (KDA) a.bg[head * (size_t)W * DK + (size_t)n * DK + t] = glast(t);
-            else if (t == 0) a.bg[head * (size_t)W + n] = gn_s;
+            st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, seg_ld<TI>(s_K + n * DK, t));
+            if constexpr (KDA) st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, glast(t));
+            else if (t == 0) st_nt(a.bg + head * (size_t)W + n, gn_s);
         }
     }
 
@@ -632,7 +630,7 @@ void flush_kernel(FlushArgs a) {
             }
             const float mn = __int_as_float(s_idx[8]) * (seg_ld<TI>(s_tv, j) - hk);
             s_M[n * DV + j] = mn;
-            a.bm[head * (size_t)W * DV + (size_t)n * DV + j] = mn;
+            st_nt(a.bm + head * (size_t)W * DV + (size_t)n * DV + j, mn);
             tok_st<TI>(a.o, head * DV + j, hq + aq * mn);
         }
         lds_barrier();

@@ -253,6 +253,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Streaming stores (non-temporal): results written once per launch and read
+// by a later one.  Written through to memory during the kernel instead of
+// staying dirty in the XCD's L2 until the end-of-kernel write-back.
+template <typename T>
+__device__ __forceinline__ void st_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt2(void* p, uint32_t a, uint32_t b) {
+    __builtin_nontemporal_store(u32x2{a, b}, static_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_nt4(float* p, float a, float b, float c, float d) {
+    __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4*>(p));
+}
+
 // Token vectors staged in LDS: fp32 (TI = float), or bf16 (TI = uint16_t)
 // packed into the first half of an fp32-sized segment.
 template <typename TI>
@@ -280,8 +294,8 @@ __device__ __forceinline__ void seg_ld_n(const float* seg, int i0, float (&x)[N]
 // One output element (fp32 or bf16, round to nearest even).
 template <typename TI>
 __device__ __forceinline__ void tok_st(void* base, size_t i, float x) {
-    if constexpr (sizeof(TI) == 4) reinterpret_cast<float*>(base)[i] = x;
-    else reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16(x);
+    if constexpr (sizeof(TI) == 4) st_nt(reinterpret_cast<float*>(base) + i, x);
+    else st_nt(reinterpret_cast<uint16_t*>(base) + i, f32_to_bf16(x));
 }
 // One input element from global memory.
 template <typename TI>
