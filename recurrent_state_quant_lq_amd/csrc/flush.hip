@@ -285,10 +285,14 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
 #pragma unroll
         for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
         int8_t* dst = out.sq + (size_t)(li * CT + ct) * DK + row0;
+        // (write-back stores: a column's 128 bytes come from 16 lanes of four
+        // waves, and L2 merges the pieces into whole lines; streamed, each
+        // piece would reach memory as a partial write)
         if constexpr (RPL == 8)
-            st_nt2(dst, pack_low4(z[0], z[1], z[2], z[3]), pack_low4(z[4], z[5], z[6], z[7]));
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low4(z[0], z[1], z[2], z[3]),
+                                                        pack_low4(z[4], z[5], z[6], z[7]));
         else
-            st_nt(reinterpret_cast<uint32_t*>(dst), pack_low4(z[0], z[1], z[2], z[3]));
+            *reinterpret_cast<uint32_t*>(dst) = pack_low4(z[0], z[1], z[2], z[3]);
     }
 }
 

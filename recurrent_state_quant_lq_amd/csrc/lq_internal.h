@@ -258,11 +258,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 // staying dirty in the XCD's L2 until the end-of-kernel write-back.
 template <typename T>
 __device__ __forceinline__ void st_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_nt2(void* p, uint32_t a, uint32_t b) {
-    __builtin_nontemporal_store(u32x2{a, b}, static_cast<u32x2*>(p));
-}
 __device__ __forceinline__ void st_nt4(float* p, float a, float b, float c, float d) {
     __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4*>(p));
 }
