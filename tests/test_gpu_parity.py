@@ -193,6 +193,7 @@ def test_fp32_recurrence_kernel(dk, kda):
     ("tiny_gdn", [(0, 0)], None, True),
     ("gdn_layer", [(0, h) for h in range(0, 16, 3)], 64, True),
     ("kda", [(0, 0), (31, 31)], 48, False),
+    ("kda", [(3, 7), (30, 2)], 48, True),
 ])
 def test_bf16_io_presets(name, sample, T, fused):
     """q, k, v and o in bf16: the resync harness with the oracle fed the bf16
@@ -524,10 +525,11 @@ def test_timing_hook_records_each_launch():
     assert lq.lq_timing_collect() == ([], [])
 
 
-@pytest.mark.parametrize("dk,per_key,mode", [(128, False, "two_call"), (64, True, "two_call"),
-                                              (16, False, "two_call"), (128, False, "fused"),
-                                              (64, True, "fused_2streams"), (16, False, "fused")])
-def test_ragged_windows(dk, per_key, mode):
+@pytest.mark.parametrize("dk,per_key,mode,bf16", [(128, False, "two_call", False), (64, True, "two_call", False),
+                                                   (16, False, "two_call", False), (128, False, "fused", False),
+                                                   (64, True, "fused_2streams", False), (16, False, "fused", False),
+                                                   (128, True, "fused", True), (64, False, "two_call", True)])
+def test_ragged_windows(dk, per_key, mode, bf16):
     """Batch rows at different window positions (the ragged entry points):
     row b's first window ends after first[b] tokens, later ones after W, the
     last at the end of the run; each flushed window is checked against the
@@ -539,10 +541,12 @@ def test_ragged_windows(dk, per_key, mode):
     through lq_gdn_decode_step_ragged (fused_2streams: the two calls on two
     streams at once, joined by events)."""
     B, H, W, C, T = 3, 4, 8, 2, 21
-    say(f"ragged dk={dk} per_key={per_key} mode={mode}")
-    d = lq.make_dims(B, H, dk, dk, W, C, int(per_key), 1)
+    say(f"ragged dk={dk} per_key={per_key} mode={mode} bf16={bf16}")
+    d = lq.make_dims(B, H, dk, dk, W, C, int(per_key), 1, lq.LQ_IO_BF16 if bf16 else lq.LQ_IO_F32)
     tok = inputs.host_tokens(321 + dk, T, B, H, dk, dk, per_key=per_key, beta_lo=0.1, beta_hi=0.9)
-    tk = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in tok.items()}
+    tk = io_tokens({k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in tok.items()}, bf16)
+    tok = {k: host(v) for k, v in tk.items()}           # the values the library sees
+    o_tol = O_TOL_BF16 if bf16 else O_TOL
     rng = np.random.default_rng(dk)
     H0 = (rng.standard_normal((B, H, dk, dk)) * 0.2).astype(np.float32)
     codec = {(b, h): O.quantize(H0[b, h], C, 1) for b in range(B) for h in range(H)}
@@ -552,7 +556,7 @@ def test_ragged_windows(dk, per_key, mode):
     first = [3, W, 5]
     wlen = list(first)                      # length of each row's current window
     pos, start = [0] * B, [0] * B
-    o = torch.empty((B, H, dk), device="cuda")
+    o = torch.empty((B, H, dk), dtype=lq.io_torch_dtype(d), device="cuda")
     h_out = torch.empty((B, H, dk, dk), device="cuda")
     outs = []
     flushed = 0
@@ -597,8 +601,8 @@ def test_ragged_windows(dk, per_key, mode):
             for h in range(H):
                 ht = O.head_tokens(tok, b, h, t0, t0 + N)
                 res = O.window(codec[(b, h)], ht, per_key, W, C, 1)
-                got_o = torch.stack([outs[i][b, h] for i in range(t0, t0 + N)]).cpu().numpy()
-                assert rel_err(got_o, res["o"]) <= O_TOL, (t, b, h)
+                got_o = host(torch.stack([outs[i][b, h] for i in range(t0, t0 + N)]))
+                assert rel_err(got_o, res["o"]) <= o_tol, (t, b, h)
                 ob = oracle_buffer(codec[(b, h)], res["buf"], N)
                 for key in ("k", "m", "g"):
                     g = getattr(st, "buf_" + key)[b, h, :N].cpu().numpy()
