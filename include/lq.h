@@ -42,8 +42,11 @@
  *     make no HIP call; on any error nothing is enqueued.  LQ_ERR_HIP means a
  *     launch failed; lq_last_hip_error() gives the hipError_t.
  *   - Non-finite inputs are not checked; they propagate.
- *   - Supported: dk = dv in {16, 64, 128}; 1 <= W <= 32; 0 <= C <= 8; all
- *     sequences of a batch share the window position (lockstep decode).
+ *   - Supported: dk = dv in {16, 64, 128}; 1 <= W <= 32; 0 <= C <= 8.  The
+ *     plain calls take one window position for the whole batch (lockstep);
+ *     the *_ragged calls take one per batch row from a device array.
+ *   - Token vectors q, k, v and outputs o are fp32 or bf16 (lq_dims.io_dtype);
+ *     everything else is fp32 (int8 / int32 where stated).
  */
 #ifndef LQ_H
 #define LQ_H
