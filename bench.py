@@ -423,6 +423,47 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
                       "vs_fp32_io": round(tpsb / lq_value, 3), "decode_avg_launch_us": round(decb, 3)}
     del layb, ringb
     torch.cuda.empty_cache()
+    # batch sweep of the decode kernel: at B/2 and 2B the same step (fresh
+    # states, the same token distribution); the slope between B and 2B is the
+    # kernel's marginal streaming rate, the intercept its fixed cost per launch
+    sweep = {}
+    for Bx in (B // 2, 2 * B):
+        dx = lq.make_dims(Bx, H, dk, dv, W, wl.C, d.decay_mode, d.smooth)
+        gx = torch.Generator(device=h0.device).manual_seed(Bx)
+        hx = torch.randn((Bx, H, dk, dv), device=h0.device, generator=gx) * 0.3
+        layx = [lq.LayerState.allocate(dx, h0.device) for _ in range(L)]
+        for st in layx:
+            lq.lq_gdn_state_quantize(st, hx)
+        ringx = [inputs.device_tokens(wl.seed * 17 + l, W, Bx, H, dk, dv, per_key=wl.per_key, beta_lo=wl.beta_lo,
+                                      beta_hi=wl.beta_hi, device=h0.device) for l in range(L)]
+        ox = torch.empty((Bx, H, dv), dtype=torch.float32, device=h0.device)
+
+        def stepx():
+            for n in range(W - 1):
+                for l in range(L):
+                    tk = ringx[l]
+                    lq.lq_gdn_decode_step(layx[l], n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                          tk["beta"][n], ox)
+            for l in range(L):
+                tk, n = ringx[l], W - 1
+                lq.lq_gdn_decode_step_flush(layx[l], n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                            tk["beta"][n], ox)
+        stepx()
+        us = kernel_us(stepx, lq.LQ_KERNEL_DECODE)
+        nbytes = sum(decode_bytes(wl.with_(B=Bx), n) for n in range(W - 1)) / (W - 1)
+        sweep[Bx] = (us, nbytes)
+        del layx, ringx, hx, ox
+        torch.cuda.empty_cache()
+    b1 = sum(decode_bytes(wl, n) for n in range(W - 1)) / (W - 1)
+    (u2, n2) = sweep[2 * B]
+    marginal = (n2 - b1) / ((u2 - lq_decode_us) * 1e-6) / 1e9
+    out["decode_batch_sweep"] = {
+        "B": [B // 2, B, 2 * B],
+        "decode_avg_launch_us": [round(sweep[B // 2][0], 3), round(lq_decode_us, 3), round(u2, 3)],
+        "GBps": [round(sweep[B // 2][1] / (sweep[B // 2][0] * 1e-6) / 1e9, 1), round(b1 / (lq_decode_us * 1e-6) / 1e9, 1),
+                 round(n2 / (u2 * 1e-6) / 1e9, 1)],
+        "marginal_GBps_B_to_2B": round(marginal, 1),
+        "fixed_us_per_launch": round(lq_decode_us - b1 / (marginal * 1e9) * 1e6, 3)}
     # (f2) prefill of a 128-token prompt chunk: chunked fp32 form (lq_gdn_prefill,
     # without its final quantization) against the token-by-token fp32 recurrence
     Tp = 128
