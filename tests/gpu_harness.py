@@ -231,3 +231,45 @@ def resync_run(wl: Workload, sample, *, host_tokens: bool, W=None, C=None, smoot
             say(f"  window {rep.windows}: o_err {rep.o_err:.2e} h_err {rep.h_err:.2e} "
                 f"buf_err {rep.buf_err:.2e} exact {rep.bytes_exact}")
     return rep
+
+
+def free_run(wl: Workload, sample, *, host_tokens: bool, T: int) -> dict:
+    """GPU path and oracle each run on their own for T tokens from the same
+    starting codec (no resync): per flush, the number of int8 state bytes
+    that differ between the two codecs of each sampled head, and the largest
+    relative output difference over all tokens.  Two correct fp32 paths differ
+    by ulps, which can flip a rounding at a .5 boundary; this measures how far
+    such flips carry."""
+    d = dims_of(wl)
+    W = d.W
+    src = TokenSource(wl, host_tokens)
+    st = lq.LayerState.allocate(d)
+    orc = prefill_state(wl, src, st, sample)          # both sides start from these codecs
+    o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+    flips, o_err, max_step = [], 0.0, 0
+    t = 0
+    while t < T:
+        N = min(W, T - t)
+        tk = src.tokens(wl.prefill + t, wl.prefill + t + N)
+        outs = torch.empty((N, wl.B, wl.H, wl.dv), dtype=torch.float32, device="cuda")
+        for n in range(N):
+            args = (tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o)
+            if n < N - 1:
+                lq.lq_gdn_decode_step(st, n, *args)
+            else:
+                lq.lq_gdn_decode_step_flush(st, n, *args)
+            outs[n].copy_(o)
+        torch.cuda.synchronize()
+        per = []
+        for (b, h) in sample:
+            ht = {k: host(v[:, b, h]) for k, v in tk.items()}
+            res = O.window(orc[(b, h)], ht, wl.per_key, W, d.C, d.smooth, route="wy")
+            o_err = max(o_err, rel_err(host(outs[:, b, h]), res["o"]))
+            orc[(b, h)] = res["codec"]
+            gc = head_codec(st, b, h)
+            diff = gc["sq"].astype(np.int32) - res["codec"]["sq"].astype(np.int32)
+            per.append(int(np.count_nonzero(diff)))
+            max_step = max(max_step, int(np.abs(diff).max()))
+        flips.append(per)
+        t += N
+    return dict(o_err=o_err, flips=flips, max_byte_diff=max_step, bytes_per_head=wl.dk * wl.dv)

@@ -17,8 +17,9 @@ from recurrent_state_quant_lq_amd.configs import PRESETS
 
 pytestmark = pytest.mark.gpu
 
-from gpu_harness import (BUF_TOL, H_TOL, O_TOL, O_TOL_BF16, codec_equal, dims_of, head_codec,  # noqa: E402
-                         host, io_tokens, oracle_buffer, rel_err, resync_run, say, upload_head_codec)
+from gpu_harness import (BUF_TOL, H_TOL, O_TOL, O_TOL_BF16, codec_equal, dims_of, free_run,  # noqa: E402
+                         head_codec, host, io_tokens, oracle_buffer, rel_err, resync_run, say,
+                         upload_head_codec)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -182,6 +183,34 @@ def test_fp32_recurrence_kernel(dk, kda):
                                             H0=H0[b, hh].astype(np.float64))
             assert rel_err(o[:, b, hh].cpu().numpy(), o_ref) < 1e-5
             assert np.abs(h[b, hh].cpu().numpy() - H_ref).max() / np.abs(H_ref).max() < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# free-running comparison (reported; gated only by loose sanity bounds)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,sample,T", [
+    ("tiny_gdn", [(0, 0)], 64),
+    ("gdn_layer", [(0, h) for h in range(16)], 256),
+    ("gdn_batched", [(0, 0), (17, 5), (63, 31)], 256),
+    ("kda", [(0, 0), (31, 31)], 256),
+])
+def test_free_running_divergence(name, sample, T):
+    """GPU and oracle each on their own for T tokens (no resync): the int8
+    bytes that differ per flush and the output difference are reported.  A
+    rounding flip at a .5 boundary is legitimate (the two sides' fp32 states
+    differ by ulps) and the states then drift apart by such flips, so only
+    gross divergence fails: outputs within 2e-2, under 10% of the state bytes
+    different at any flush."""
+    wl = PRESETS[name]
+    rep = free_run(wl, sample, host_tokens=wl.B * wl.H <= 16, T=T)
+    fl = np.array(rep["flips"])
+    say(f"free-running {name}: T={T} heads={len(sample)} max o diff {rep['o_err']:.3e}; "
+        f"differing int8 bytes per head and flush: mean {fl.mean():.2f}, max {fl.max()} "
+        f"of {rep['bytes_per_head']}, largest difference {rep['max_byte_diff']}; "
+        f"flushes with any {np.count_nonzero(fl.sum(axis=1))}/{len(fl)}")
+    assert rep["o_err"] < 2e-2
+    assert fl.max() < 0.1 * rep["bytes_per_head"]
 
 
 # ---------------------------------------------------------------------------
