@@ -485,6 +485,55 @@ def test_canaries_and_untouched_slots():
         assert (g[:GUARD] == 7).all() and (g[-GUARD:] == 7).all(), name
 
 
+@pytest.mark.parametrize("kda,bf16", [(True, False), (False, True)])
+def test_canaries_fused_ragged_prefill_checkpoint(kda, bf16):
+    """Guard regions around every array for the calls added to the decode
+    and flush: the fused last token (lockstep and ragged, one row skipped),
+    the prefill (ragged last chunk) and the checkpoint records.  Nothing is
+    written outside the arrays, and the fused call writes only slot n of the
+    buffer."""
+    B, H, dk, W, C, T = 3, 5, 128, 16, 4, 37
+    say(f"canaries fused/ragged/prefill/checkpoint kda={kda} bf16={bf16}")
+    d = lq.make_dims(B, H, dk, dk, W, C, int(kda), 1, lq.LQ_IO_BF16 if bf16 else lq.LQ_IO_F32)
+    gd = dk if kda else 1
+    spec = dict(sq=((B, H, dk, dk), torch.int8), row_scale=((B, H, dk), torch.float32),
+                col_scale=((B, H, dk), torch.float32), comp_idx=((B, H, C), torch.int32),
+                comp_val=((B, H, C, dk), torch.float32), buf_k=((B, H, W, dk), torch.float32),
+                buf_m=((B, H, W, dk), torch.float32), buf_g=((B, H, W, gd), torch.float32))
+    arrays = {name: _guarded(shape, dt, 7) for name, (shape, dt) in spec.items()}
+    st = lq.LayerState(d, *[arrays[n][1] for n in spec])
+    iot = lq.io_torch_dtype(d)
+    tok = inputs.host_tokens(8, T, B, H, dk, dk, per_key=kda, beta_lo=0.1, beta_hi=0.9)
+    tk = io_tokens({k: torch.from_numpy(v).cuda() for k, v in tok.items()}, bf16)
+    hb, h = _guarded((B, H, dk, dk), torch.float32, 7)
+    h.copy_(torch.from_numpy((np.random.default_rng(4).standard_normal((B, H, dk, dk)) * 0.1).astype(np.float32)))
+    pob, po = _guarded((T, B, H, dk), iot, 7)
+    lq.lq_gdn_prefill(d, st, h, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], po)
+    ob, o = _guarded((B, H, dk), iot, 7)
+    hob, hout = _guarded((B, H, dk, dk), torch.float32, 7)
+    for n in range(5):
+        lq.lq_gdn_decode_step(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o)
+    before = {k: getattr(st, "buf_" + k).clone() for k in ("k", "m", "g")}
+    n = 5
+    lq.lq_gdn_decode_step_flush(st, n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n], tk["beta"][n], o,
+                                h_out=hout)
+    torch.cuda.synchronize()
+    keep = [i for i in range(W) if i != n]
+    for k in ("k", "m", "g"):
+        assert torch.equal(getattr(st, "buf_" + k)[:, :, keep], before[k][:, :, keep]), k
+    pos = torch.tensor([W - 1, -1, 3], dtype=torch.int32, device="cuda")
+    lq.lq_gdn_decode_step_flush_ragged(st, pos, tk["q"][6], tk["k"][6], tk["v"][6], tk["alpha"][6],
+                                       tk["beta"][6], o, h_out=hout)
+    bb, blob = _guarded((lq.lq_checkpoint_bytes(d),), torch.uint8, 7)
+    lq.lq_gdn_state_pack(st, blob)
+    lq.lq_gdn_state_unpack(st, blob)
+    torch.cuda.synchronize()
+    extra = [("h", (hb, h)), ("prefill_o", (pob, po)), ("o", (ob, o)), ("h_out", (hob, hout)), ("blob", (bb, blob))]
+    for name, (base, view) in list(arrays.items()) + extra:
+        g = base.cpu()
+        assert (g[:GUARD] == 7).all() and (g[-GUARD:] == 7).all(), name
+
+
 def test_run_to_run_bitwise_determinism():
     wl = PRESETS["kda"].with_(B=4, H=8, T=20, prefill=0, seed=12)
     outs = []
