@@ -534,25 +534,37 @@ def test_canaries_fused_ragged_prefill_checkpoint(kda, bf16):
         assert (g[:GUARD] == 7).all() and (g[-GUARD:] == 7).all(), name
 
 
-def test_run_to_run_bitwise_determinism():
+@pytest.mark.parametrize("fused", [False, True])
+def test_run_to_run_bitwise_determinism(fused):
+    """Two runs of the same prefill and windows give identical bits (no
+    atomics or order-dependent reductions anywhere on the path)."""
     wl = PRESETS["kda"].with_(B=4, H=8, T=20, prefill=0, seed=12)
     outs = []
     for rep in range(2):
         d = dims_of(wl)
         st = lq.LayerState.allocate(d)
-        from recurrent_state_quant_lq_amd import inputs
-        tok = inputs.host_tokens(wl.seed, wl.T, wl.B, wl.H, wl.dk, wl.dv, per_key=True,
+        tok = inputs.host_tokens(wl.seed, wl.T + 24, wl.B, wl.H, wl.dk, wl.dv, per_key=True,
                                  beta_lo=0.1, beta_hi=0.9)
         tk = {k: torch.from_numpy(v).cuda() for k, v in tok.items()}
+        h = torch.zeros((wl.B, wl.H, wl.dk, wl.dv), device="cuda")
+        po = torch.empty((24, wl.B, wl.H, wl.dv), device="cuda")
+        pt = {k: v[wl.T:] for k, v in tk.items()}
+        lq.lq_gdn_prefill(d, st, h, 24, pt["q"], pt["k"], pt["v"], pt["alpha"], pt["beta"], po)
+        acc = [h.clone(), po.clone(), st.sq.clone().float()]
         o = torch.empty((wl.B, wl.H, wl.dv), device="cuda")
         hout = torch.empty((wl.B, wl.H, wl.dk, wl.dv), device="cuda")
-        acc = []
         for t in range(wl.T):
             n = t % wl.W
-            lq.lq_gdn_decode_step(st, n, tk["q"][t], tk["k"][t], tk["v"][t], tk["alpha"][t], tk["beta"][t], o)
+            last = n == wl.W - 1 or t == wl.T - 1
+            args = (tk["q"][t], tk["k"][t], tk["v"][t], tk["alpha"][t], tk["beta"][t], o)
+            if fused and last:
+                lq.lq_gdn_decode_step_flush(st, n, *args, h_out=hout)
+            else:
+                lq.lq_gdn_decode_step(st, n, *args)
+                if last:
+                    lq.lq_gdn_window_flush(st, n + 1, hout)
             acc.append(o.clone())
-            if n == wl.W - 1 or t == wl.T - 1:
-                lq.lq_gdn_window_flush(st, n + 1, hout)
+            if last:
                 acc.append(hout.clone())
                 acc.append(st.sq.clone().float())
         torch.cuda.synchronize()
