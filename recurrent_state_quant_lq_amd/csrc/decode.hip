@@ -26,8 +26,9 @@
 //   * each value lane loads its column of the buffered m_i;
 //   * the int8 state goes to VGPRs last, as the A operands of int8 MFMAs (it
 //     is stored value-column-major, sq[j][i]: 16 consecutive key channels of
-//     one value column are one 16-byte load); the first barrier waits for
-//     everything else, so phase A runs while it streams in.
+//     one value column are one 16-byte load).  The first barrier waits for
+//     every load: LDS copies and register loads do not complete in order with
+//     each other, so no load can be left in flight past the first LDS read.
 // Then:
 //   A. channel lanes: the int8 digits of r o e^g o q and r o e^g o k per
 //      64-channel block; all lanes, in slot groups: rr_i = <k, E_i o k_i>,
@@ -193,14 +194,13 @@ void decode_kernel(DecodeArgs a) {
     if (is_val) {
 #pragma unroll
         for (int i = 0; i < WM - 1; ++i)
-            if (i < n) mcol[i] = bmr[(size_t)i * DV + j];
+            if (i < n) mcol[i] = ld_nt(bmr + (size_t)i * DV + j);
     }
 
     // ---- int8 state -> VGPRs (MFMA A operands), issued last ---------------------------------
     // lane l of wave w: column j = tile*16 + l%16, channels ks*64 + 16*(l/16) .. +15.
-    // Every tile and K step is real when the shape divides evenly; the loads are
-    // then unconditional, and the first barrier waits for everything but these
-    // TPW*KS loads, which stream in while phase A runs.
+    // Every tile and K step is real when the shape divides evenly (the loads are then
+    // unconditional).
     constexpr bool FULL = (NTILE % D::NW == 0) && (DK % 64 == 0);
     __builtin_amdgcn_sched_barrier(0);
     v4i sqa[TPW][KS];
@@ -213,17 +213,17 @@ void decode_kernel(DecodeArgs a) {
                 const int tile = w * TPW + tw;
                 const int i0 = ks * 64 + 16 * (lane / 16);
                 if (FULL || (tile < NTILE && i0 < DK))
-                    sqa[tw][ks] = *reinterpret_cast<const v4i*>(sq + (size_t)(tile * 16 + lane % 16) * DK + i0);
+                    sqa[tw][ks] = ld_nt(reinterpret_cast<const v4i*>(sq + (size_t)(tile * 16 + lane % 16) * DK + i0));
                 else
                     sqa[tw][ks] = v4i{0, 0, 0, 0};
             }
     }
     __builtin_amdgcn_sched_barrier(0);
-    barrier_keep_loads<FULL ? TPW * KS : 0>();
+    all_loads_barrier();
 
     const float beta = __int_as_float(s_misc[8]);
     float gn_s = 0.0f;
-    if constexpr (!KDA) gn_s = (n > 0 ? __int_as_float(s_misc[10]) : 0.0f) + logf(__int_as_float(s_misc[9]));
+    if constexpr (!KDA) gn_s = (n > 0 ? __int_as_float(s_misc[10]) : 0.0f) + __logf(__int_as_float(s_misc[9]));
 
     // ---- A. digits of r o e^g o q and r o e^g o k; slot n's key and decay; dot products ----
     float xq = 0.0f, xk = 0.0f;                   // r o e^g o q, r o e^g o k (channel lanes)
@@ -231,7 +231,7 @@ void decode_kernel(DecodeArgs a) {
         const float qc = seg_ld<TI>(s_vec + D::SQ * DK, t), kc = seg_ld<TI>(s_vec + D::SK * DK, t);
         const float rc = s_vec[D::SR * DK + t];
         float gn;
-        if constexpr (KDA) gn = (n > 0 ? s_vec[D::SG * DK + t] : 0.0f) + logf(s_vec[D::SA * DK + t]);
+        if constexpr (KDA) gn = (n > 0 ? s_vec[D::SG * DK + t] : 0.0f) + __logf(s_vec[D::SA * DK + t]);
         else gn = gn_s;
         const float en = __expf(gn);
         xq = rc * (en * qc);
@@ -250,11 +250,11 @@ void decode_kernel(DecodeArgs a) {
         const float mq = __uint_as_float(wave_umax(__float_as_uint(xq) & 0x7fffffffu));
         const float mk = __uint_as_float(wave_umax(__float_as_uint(xk) & 0x7fffffffu));
         uint32_t d0, d1, d2;
-        digits3_words(xq, mq > 0.0f ? 127.0f / mq : 0.0f, d0, d1, d2);
+        digits3_words(xq, mq > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(mq) : 0.0f, d0, d1, d2);
         s_dig[0][t] = (int8_t)d0;
         s_dig[1][t] = (int8_t)d1;
         s_dig[2][t] = (int8_t)d2;
-        digits3_words(xk, mk > 0.0f ? 127.0f / mk : 0.0f, d0, d1, d2);
+        digits3_words(xk, mk > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(mk) : 0.0f, d0, d1, d2);
         s_dig[3][t] = (int8_t)d0;
         s_dig[4][t] = (int8_t)d1;
         s_dig[5][t] = (int8_t)d2;
@@ -267,6 +267,15 @@ void decode_kernel(DecodeArgs a) {
         float kq[CH], kk[CH];
         seg_ld_n<CH, TI>(s_vec + D::SQ * DK, c0, kq);
         seg_ld_n<CH, TI>(s_vec + D::SK * DK, c0, kk);
+        // per-key decay: g_n of this lane's channels, once for all its slots
+        float gnc[KDA ? CH : 1];
+        if constexpr (KDA) {
+            float al[CH], gp[CH];
+            load_floats<CH>(s_vec + D::SA * DK + c0, al);
+            if (n > 0) load_floats<CH>(s_vec + D::SG * DK + c0, gp);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) gnc[c] = (n > 0 ? gp[c] : 0.0f) + __logf(al[c]);
+        }
 #pragma unroll
         for (int rd = 0; rd < ROUNDS; ++rd) {
             const int slot = slot0 + rd * SPR;
@@ -276,13 +285,9 @@ void decode_kernel(DecodeArgs a) {
                 float ks[CH];
                 load_floats<CH>(s_vec + (D::SKB + slot) * DK + c0, ks);
                 if constexpr (KDA) {
-                    float al[CH], gp[CH];
-                    load_floats<CH>(s_vec + D::SA * DK + c0, al);
-                    if (n > 0) load_floats<CH>(s_vec + D::SG * DK + c0, gp);
 #pragma unroll
                     for (int c = 0; c < CH; ++c) {
-                        const float gnc = (n > 0 ? gp[c] : 0.0f) + logf(al[c]);
-                        const float x = ks[c] * __expf(gnc - gs[rd][c]);
+                        const float x = ks[c] * __expf(gnc[c] - gs[rd][c]);
                         rr += kk[c] * x;
                         aa += kq[c] * x;
                     }

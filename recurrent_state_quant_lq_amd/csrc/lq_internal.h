@@ -65,22 +65,17 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Waits until at most N vector-memory operations of this wave are still
-// outstanding (loads complete in issue order, LDS copies included), then a
-// workgroup barrier with full fences (no memory access moves across it).  The
-// N most recently issued loads stay in flight across the barrier; the
-// compiler waits for them where their registers are used.
-template <int N>
-__device__ __forceinline__ void barrier_keep_loads() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14));   // vmcnt(N) expcnt(0) lgkmcnt(0)
+// Waits for every outstanding memory operation of this wave (LDS copies
+// included), then a workgroup barrier with full fences.  Data copied to LDS by
+// global_load_lds are readable after it.  (LDS copies and register loads do
+// not complete in order with each other, so a partial vmcnt wait cannot tell
+// that an LDS copy has landed.)
+__device__ __forceinline__ void all_loads_barrier() {
+    __builtin_amdgcn_s_waitcnt(0);                              // vmcnt(0) expcnt(0) lgkmcnt(0)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
-
-// Waits for every outstanding load of this wave, then a full barrier.
-__device__ __forceinline__ void all_loads_barrier() { barrier_keep_loads<0>(); }
 
 // ---------------------------------------------------------------------------
 // cross-lane
@@ -252,6 +247,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
     return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
+
+// Streaming loads (non-temporal): data read once per launch (the int8 state,
+// the buffered rows), kept out of the caches' working set.
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
 
 // Streaming stores (non-temporal): results written once per launch and read
 // by a later one.  Written through to memory during the kernel instead of
