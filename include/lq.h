@@ -21,9 +21,13 @@
  * Stored state (the "codec"; [news ¶5]: 1.19 bytes per value at
  * dk = dv = 128, C = 4):  H = deq + sum_c e_{idx_c} cv_c^T with
  * deq_ij = sq_ij * row_scale_i * col_scale_j,  sq int8 in [-127, 127].
- * The int8 matrix is stored value-column-major: element (i, j) of H's
- * quantized residual is sq[j*dk + i], so each value column's dk key-channel
- * bytes are contiguous (the operand layout of the int8 matrix cores).
+ * The int8 matrix of a head is dk*dv bytes in the operand order of the int8
+ * matrix cores.  Element (i, j) of H's quantized residual (key channel i,
+ * value channel j) is byte
+ *     off(i, j) = ((((j/16)*KS + i/64)*G + (i%64)/16)*16 + j%16)*16 + i%16,
+ * with G = min(4, dk/16) and KS = ceil(dk/64).  16-channel runs of one value
+ * column are contiguous, and each 1 KB block is one column tile's operand for
+ * one 64-channel K step.  At dk = 16 this is value-column-major (j*dk + i).
  * It stays fixed for a window of W tokens ([news ¶3]); the window's updates
  * live in an fp32 buffer (see lq_gdn_decode_step) and the state is rebuilt
  * and requantized once at the window's end (lq_gdn_window_flush).
@@ -88,7 +92,7 @@ typedef struct lq_dims {
 
 /* Device arrays of one layer's quantized state and window buffer.
  * gd = dk for LQ_DECAY_PER_KEY, 1 for LQ_DECAY_SCALAR.
- *   sq        int8  [B,H,dv,dk]   quantized residual, value-column-major
+ *   sq        int8  [B,H,dk*dv]   quantized residual, byte off(i, j) per head
  *   row_scale fp32  [B,H,dk]      per-row scale (0 for an all-zero row)
  *   col_scale fp32  [B,H,dv]      per-column smoothing factor
  *   comp_idx  int32 [B,H,C]       compensator rows, ascending
@@ -231,7 +235,7 @@ int lq_gdn_state_quantize(const lq_dims *d, const float *h, const lq_state *st, 
  * with scales and correction terms), e.g. for prefix caching at window
  * boundaries.  The blob holds one record per head, in (b, h) order (the H
  * records of a sequence are adjacent), each lq_checkpoint_bytes(d) / (B*H)
- * bytes:  sq (dk*dv int8, value-column-major) | row_scale (4*dk) |
+ * bytes:  sq (dk*dv int8, stored order off(i, j)) | row_scale (4*dk) |
  * col_scale (4*dv) | comp_val (4*C*dv) | comp_idx (4*C) | zero padding to a
  * multiple of 16 bytes.  blob: device memory, 16-byte aligned, caller-owned.
  * Pack reads the codec arrays of st; unpack writes them (the window buffer

@@ -6,7 +6,7 @@
 // correction terms; this is that stored form, one contiguous record per head.
 //
 // Record of one head (head_bytes, a multiple of 16):
-//     sq   dk*dv bytes   int8, value-column-major (as the state stores it)
+//     sq   dk*dv bytes   int8, in the state's storage order (sq_off)
 //     r    4*dk          fp32 row scales
 //     s    4*dv          fp32 column scales
 //     cv   4*C*dv        fp32 compensator rows

@@ -24,9 +24,9 @@
 //     compensator rows) and the buffered keys go straight to LDS
 //     (global_load_lds_dwordx4, no registers);
 //   * each value lane loads its column of the buffered m_i;
-//   * the int8 state goes to VGPRs last, as the A operands of int8 MFMAs (it
-//     is stored value-column-major, sq[j][i]: 16 consecutive key channels of
-//     one value column are one 16-byte load).  The first barrier waits for
+//   * the int8 state goes to VGPRs last, as the A operands of int8 MFMAs; it
+//     is stored in that operand order (sq_off), so each of a wave's state
+//     loads reads 1 KB of contiguous bytes.  The first barrier waits for
 //     every load: LDS copies and register loads do not complete in order with
 //     each other, so no load can be left in flight past the first LDS read.
 // Then:
@@ -213,7 +213,7 @@ void decode_kernel(DecodeArgs a) {
                 const int tile = w * TPW + tw;
                 const int i0 = ks * 64 + 16 * (lane / 16);
                 if (FULL || (tile < NTILE && i0 < DK))
-                    sqa[tw][ks] = ld_nt(reinterpret_cast<const v4i*>(sq + (size_t)(tile * 16 + lane % 16) * DK + i0));
+                    sqa[tw][ks] = ld_nt(reinterpret_cast<const v4i*>(sq + sq_off<DK>(i0, tile * 16 + lane % 16)));
                 else
                     sqa[tw][ks] = v4i{0, 0, 0, 0};
             }

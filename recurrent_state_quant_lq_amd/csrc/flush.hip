@@ -21,7 +21,7 @@
 //     H[row(w, lg, rb, v)][li*CT + ct],   row = w*16*RBW + lg*4*RBW + rb*4 + v,
 // i.e. the MFMA accumulator layout with the rows permuted so that a lane's
 // 4*RBW rows are consecutive: one column's bytes of those rows are one 8-byte
-// access in the value-column-major state, and its CT columns are contiguous
+// access in the stored state (sq_off), and its CT columns are contiguous
 // in row-major fp32 arrays.
 //
 // The codec steps are single IEEE fp32 operations in a fixed order, so the
@@ -63,6 +63,8 @@ struct FS {
     static_assert(DK % 16 == 0 && RB % NW == 0 && (CT % NW == 0 || CT < NW), "tile shape");
     // every wave's rows lie in one 64-row half
     static_assert(16 * RBW <= 64 && 64 % (16 * RBW) == 0, "row halves");
+    // a lane's RPL rows of one column are one run of the stored state (sq_off)
+    static_assert(16 % RPL == 0, "row runs");
 };
 
 template <int DK, int DV>
@@ -107,7 +109,7 @@ struct CodecLds {
 };
 
 // Codec of the state held in D layout (H is overwritten).  Writes sq
-// (value-column-major), r, s, idx, cv of one head; h_out (nullable,
+// (stored order, sq_off), r, s, idx, cv of one head; h_out (nullable,
 // row-major fp32) receives H first.
 template <int DK, int DV, int RBW, int CT, int NW>
 __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const CodecOut& out,
@@ -284,7 +286,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
         uint32_t z[RPL];
 #pragma unroll
         for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
-        int8_t* dst = out.sq + (size_t)(li * CT + ct) * DK + row0;
+        int8_t* dst = out.sq + sq_off<DK>(row0, li * CT + ct);
         // (write-back stores: a column's 128 bytes come from 16 lanes of four
         // waves, and L2 merges the pieces into whole lines; streamed, each
         // piece would reach memory as a partial write)
@@ -466,7 +468,7 @@ void flush_kernel(FlushArgs a) {
     typename RBy::T hb[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-        hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + (size_t)(li * CT + ct) * DK + row0);
+        hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + sq_off<DK>(row0, li * CT + ct));
     all_loads_barrier();
 
     // log-decay of the last slot, g_{N-1}[row]: from the buffer, or (DEC) the
@@ -722,7 +724,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
     for (int e = t; e < DK * DV; e += 256) {
         const int row = e / DV, col = e % DV;
         const int p = s_pos[row];
-        float x = ((float)sq[(size_t)col * DK + row] * r[row]) * s[col];
+        float x = ((float)sq[sq_off<DK>(row, col)] * r[row]) * s[col];
         if (p >= 0) x += a.cv[(head * a.C + p) * (size_t)DV + col];
         h[e] = x;
     }

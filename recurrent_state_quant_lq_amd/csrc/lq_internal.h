@@ -361,6 +361,24 @@ __device__ __forceinline__ void digits3_words(float x, float inv, uint32_t& w0, 
     w2 = __float_as_uint(z2);
 }
 
+// ---------------------------------------------------------------------------
+// storage order of the int8 state
+// ---------------------------------------------------------------------------
+// Byte (i, j) of a head's dk x dv int8 state (key channel i, value channel j)
+// sits at sq_off<DK>(i, j) of the head's dk*dv bytes: the A-operand order of
+// the decode's v_mfma_i32_16x16x64_i8 tiles, so each wave reads 1 KB
+// contiguous bytes per MFMA operand.  Column tile T = j/16 and K step ks =
+// i/64 own a block of G*256 bytes (G = min(4, dk/16) groups of 16 channels);
+// within it, the 16-byte piece lg*16 + j%16 holds channels ks*64 + lg*16 ..
+// +15 of column j, lg = (i%64)/16.  Runs of up to 16 consecutive channels of
+// one column (aligned to their length) are contiguous.
+template <int DK>
+__host__ __device__ constexpr uint32_t sq_off(int i, int j) {
+    constexpr int G = DK / 16 < 4 ? DK / 16 : 4;
+    constexpr int KS = (DK + 63) / 64;
+    return (uint32_t)(((((j >> 4) * KS + (i >> 6)) * G + ((i & 63) >> 4)) * 16 + (j & 15)) * 16 + (i & 15));
+}
+
 // Window-size bucket a kernel is instantiated for.
 inline int wbucket(int W) { return W <= 4 ? 4 : W <= 8 ? 8 : W <= 16 ? 16 : 32; }
 

@@ -13,6 +13,7 @@ import ctypes as ct
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -151,11 +152,43 @@ def _raise(fn, rc):
 
 _STATE_FIELDS = ("sq", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_k", "buf_m", "buf_g")
 
+_SQ_ORDER: dict = {}
+
+
+def sq_order(dk: int) -> np.ndarray:
+    """off[i, j]: where byte (i, j) of a head's int8 state (key channel i,
+    value channel j) sits in the head's dk*dv stored bytes (the operand order
+    of the int8 matrix cores, as include/lq.h states it)."""
+    off = _SQ_ORDER.get(dk)
+    if off is None:
+        i = np.arange(dk, dtype=np.int64)[:, None]
+        j = np.arange(dk, dtype=np.int64)[None, :]
+        G, KS = min(4, dk // 16), (dk + 63) // 64
+        off = ((((j >> 4) * KS + (i >> 6)) * G + ((i & 63) >> 4)) * 16 + (j & 15)) * 16 + (i & 15)
+        off.setflags(write=False)
+        _SQ_ORDER[dk] = off
+    return off
+
+
+def sq_to_rows(sq: np.ndarray, dk: int) -> np.ndarray:
+    """Stored int8 state [..., dk*dv] -> row-major [..., dk, dv]."""
+    return np.ascontiguousarray(np.asarray(sq)[..., sq_order(dk)])
+
+
+def sq_from_rows(rows: np.ndarray) -> np.ndarray:
+    """Row-major int8 state [..., dk, dv] -> stored order [..., dk*dv]."""
+    rows = np.asarray(rows)
+    dk = rows.shape[-2]
+    out = np.empty(rows.shape[:-2] + (rows.shape[-2] * rows.shape[-1],), dtype=rows.dtype)
+    out[..., sq_order(dk).ravel()] = rows.reshape(out.shape)
+    return out
+
 
 @dataclass
 class LayerState:
     """Device tensors of one layer's codec and window buffer (torch-owned).
-    ``sq`` is value-column-major [B,H,dv,dk] as the library stores it."""
+    ``sq`` is [B,H,dk*dv], each head's bytes in the library's stored order
+    (sq_order; sq_to_rows / sq_from_rows convert)."""
     dims: lq_dims
     sq: torch.Tensor
     row_scale: torch.Tensor
@@ -171,7 +204,7 @@ class LayerState:
         B, H, dk, dv, W, C = d.B, d.H, d.dk, d.dv, d.W, d.C
         gd = dk if d.decay_mode == LQ_DECAY_PER_KEY else 1
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
-        return LayerState(d, z((B, H, dv, dk), torch.int8), z((B, H, dk), torch.float32),
+        return LayerState(d, z((B, H, dk * dv), torch.int8), z((B, H, dk), torch.float32),
                           z((B, H, dv), torch.float32), z((B, H, max(C, 1)), torch.int32),
                           z((B, H, max(C, 1), dv), torch.float32),
                           z((B, H, W, dk), torch.float32), z((B, H, W, dv), torch.float32),
@@ -181,7 +214,7 @@ class LayerState:
         d = self.dims
         B, H, dk, dv, W, C = d.B, d.H, d.dk, d.dv, d.W, d.C
         gd = dk if d.decay_mode == LQ_DECAY_PER_KEY else 1
-        _check(self.sq, "sq", (B, H, dv, dk), torch.int8)
+        _check(self.sq, "sq", (B, H, dk * dv), torch.int8)
         _check(self.row_scale, "row_scale", (B, H, dk), torch.float32)
         _check(self.col_scale, "col_scale", (B, H, dv), torch.float32)
         _check(self.comp_idx, "comp_idx", (B, H, max(C, 1)), torch.int32)
@@ -210,7 +243,7 @@ class LayerState:
         """Host copies of the codec arrays, int8 matrix row-major [B,H,dk,dv]
         (comp arrays cut to C)."""
         C = self.dims.C
-        return dict(sq=self.sq.transpose(-1, -2).contiguous().cpu().numpy(),
+        return dict(sq=sq_to_rows(self.sq.cpu().numpy(), self.dims.dk),
                     r=self.row_scale.cpu().numpy(),
                     s=self.col_scale.cpu().numpy(), idx=self.comp_idx[..., :C].cpu().numpy(),
                     cv=self.comp_val[..., :C, :].cpu().numpy())
@@ -219,7 +252,7 @@ class LayerState:
         """Uploads host codec arrays ([B,H,...], int8 matrix row-major
         [B,H,dk,dv], comp arrays with C entries)."""
         C = self.dims.C
-        self.sq.copy_(torch.as_tensor(cd["sq"]).transpose(-1, -2))
+        self.sq.copy_(torch.from_numpy(sq_from_rows(cd["sq"])))
         self.row_scale.copy_(torch.as_tensor(cd["r"]))
         self.col_scale.copy_(torch.as_tensor(cd["s"]))
         if C:

@@ -85,7 +85,7 @@ def oracle_buffer(cd: dict, buf: dict, N: int) -> dict:
 
 def upload_head_codec(st: lq.LayerState, b: int, h: int, cd: dict):
     C = st.dims.C
-    st.sq[b, h].copy_(torch.from_numpy(np.ascontiguousarray(cd["sq"].T)))
+    st.sq[b, h].copy_(torch.from_numpy(lq.sq_from_rows(cd["sq"])))
     st.row_scale[b, h].copy_(torch.from_numpy(cd["r"]))
     st.col_scale[b, h].copy_(torch.from_numpy(cd["s"]))
     if C:
@@ -95,7 +95,7 @@ def upload_head_codec(st: lq.LayerState, b: int, h: int, cd: dict):
 
 def head_codec(st: lq.LayerState, b: int, h: int) -> dict:
     C = st.dims.C
-    return dict(sq=np.ascontiguousarray(st.sq[b, h].cpu().numpy().T), r=st.row_scale[b, h].cpu().numpy(),
+    return dict(sq=lq.sq_to_rows(st.sq[b, h].cpu().numpy(), st.dims.dk), r=st.row_scale[b, h].cpu().numpy(),
                 s=st.col_scale[b, h].cpu().numpy(), idx=st.comp_idx[b, h, :C].cpu().numpy(),
                 cv=st.comp_val[b, h, :C].cpu().numpy())
 

@@ -229,3 +229,31 @@ def test_checkpoint_sizes_and_errors():
     assert L.lq_gdn_state_pack(ct.byref(d), ct.byref(st), ct.c_void_p(0x7000004), None) == lq.LQ_ERR_ALIGN
     assert L.lq_gdn_state_unpack(ct.byref(d), A, ct.byref(_fake_state(null="sq")), None) == lq.LQ_ERR_NULL
     assert L.lq_gdn_state_unpack(None, A, ct.byref(st), None) == lq.LQ_ERR_NULL
+
+
+@pytest.mark.parametrize("dk", [16, 64, 128])
+def test_state_storage_order(dk):
+    """The stored order of a head's int8 state (include/lq.h): a bijection of
+    the dk*dv bytes; byte (i, j) at the position the header's formula gives,
+    spelled out here digit by digit; 16-channel runs of a column contiguous;
+    value-column-major at dk = 16; row-major round trip through the binding."""
+    import numpy as np
+    off = lq.sq_order(dk)
+    assert off.shape == (dk, dk)
+    assert np.array_equal(np.sort(off.ravel()), np.arange(dk * dk))
+    G, KS = min(4, dk // 16), (dk + 63) // 64
+    for i in range(0, dk, 7):
+        for j in range(0, dk, 5):
+            tile, jj, ks, lg, e = j // 16, j % 16, i // 64, (i % 64) // 16, i % 16
+            assert off[i, j] == (((tile * KS + ks) * G + lg) * 16 + jj) * 16 + e
+    # a run of 16 channels of one column is 16 consecutive bytes
+    runs = off.T.reshape(dk, dk // 16, 16)
+    assert (np.diff(runs, axis=-1) == 1).all()
+    if dk == 16:
+        assert np.array_equal(off, np.arange(dk)[:, None] + dk * np.arange(dk)[None, :])
+    rng = np.random.default_rng(dk)
+    rows = rng.integers(-127, 128, size=(2, 3, dk, dk), dtype=np.int8)
+    stored = lq.sq_from_rows(rows)
+    assert stored.shape == (2, 3, dk * dk)
+    assert np.array_equal(lq.sq_to_rows(stored, dk), rows)
+    assert stored[1, 2, off[5, 3]] == rows[1, 2, 5, 3]

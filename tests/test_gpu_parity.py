@@ -455,7 +455,7 @@ def test_canaries_and_untouched_slots():
     d = lq.make_dims(3, 5, 128, 128, 16, 4, 1, 1)
     B, H, dk, W, C = 3, 5, 128, 16, 4
     arrays = {}
-    spec = dict(sq=((B, H, dk, dk), torch.int8), row_scale=((B, H, dk), torch.float32),
+    spec = dict(sq=((B, H, dk * dk), torch.int8), row_scale=((B, H, dk), torch.float32),
                 col_scale=((B, H, dk), torch.float32), comp_idx=((B, H, C), torch.int32),
                 comp_val=((B, H, C, dk), torch.float32), buf_k=((B, H, W, dk), torch.float32),
                 buf_m=((B, H, W, dk), torch.float32), buf_g=((B, H, W, dk), torch.float32))
@@ -496,7 +496,7 @@ def test_canaries_fused_ragged_prefill_checkpoint(kda, bf16):
     say(f"canaries fused/ragged/prefill/checkpoint kda={kda} bf16={bf16}")
     d = lq.make_dims(B, H, dk, dk, W, C, int(kda), 1, lq.LQ_IO_BF16 if bf16 else lq.LQ_IO_F32)
     gd = dk if kda else 1
-    spec = dict(sq=((B, H, dk, dk), torch.int8), row_scale=((B, H, dk), torch.float32),
+    spec = dict(sq=((B, H, dk * dk), torch.int8), row_scale=((B, H, dk), torch.float32),
                 col_scale=((B, H, dk), torch.float32), comp_idx=((B, H, C), torch.int32),
                 comp_val=((B, H, C, dk), torch.float32), buf_k=((B, H, W, dk), torch.float32),
                 buf_m=((B, H, W, dk), torch.float32), buf_g=((B, H, W, gd), torch.float32))
