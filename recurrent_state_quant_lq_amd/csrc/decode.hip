@@ -110,7 +110,7 @@ void decode_kernel(DecodeArgs a) {
     __shared__ __align__(16) float s_vec[D::NSEG * DK];
     __shared__ __align__(16) float s_rr[WM];
     __shared__ __align__(16) float s_a[WM];
-    __shared__ __align__(16) float s_en[KDA ? DK : 1];       // e^{g_n} per key channel
+    __shared__ __align__(16) float s_cqk[2][CMAX];            // e^{g_n}[idx_c] q[idx_c], ... k[idx_c]
     __shared__ __align__(16) int8_t s_dig[6][KS * 64];       // digits of q~'' (0..2), k~'' (3..5)
     __shared__ __align__(16) float s_msc[2][KS];
     __shared__ __align__(16) float s_gem[2][DV];             // sq^T q~'', sq^T k~''
@@ -237,12 +237,20 @@ void decode_kernel(DecodeArgs a) {
         xq = rc * (en * qc);
         xk = rc * (en * kc);
         st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, kc);
-        if constexpr (KDA) {
-            st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, gn);
-            s_en[t] = en;
-        } else if (t == 0) {
-            st_nt(a.bg + head * (size_t)W + n, gn);
-        }
+        if constexpr (KDA) st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, gn);
+        else if (t == 0) st_nt(a.bg + head * (size_t)W + n, gn);
+    }
+    // the compensator rows' coefficients, by the last CMAX lanes (value lanes): the
+    // decayed query and key entries at the compensator rows (the same expression the
+    // channel lane of row idx_c evaluates)
+    if (t >= NT - CMAX && t - (NT - CMAX) < C) {
+        const int c = t - (NT - CMAX);
+        const int ic = s_misc[c] & (DK - 1);
+        float e;
+        if constexpr (KDA) e = __expf((n > 0 ? s_vec[D::SG * DK + ic] : 0.0f) + __logf(s_vec[D::SA * DK + ic]));
+        else e = __expf(gn_s);
+        s_cqk[0][c] = e * seg_ld<TI>(s_vec + D::SQ * DK, ic);
+        s_cqk[1][c] = e * seg_ld<TI>(s_vec + D::SK * DK, ic);
     }
     if (w < KS) {
         // wave w's 64 lanes are one 64-channel block (lanes past dk hold zeros):
@@ -364,16 +372,13 @@ void decode_kernel(DecodeArgs a) {
     // ---- C. m_n and the output ------------------------------------------------------------------
     if (is_val) {
         const float sj = s_vec[D::SS * DK + j];
-        const float eg = KDA ? 0.0f : __expf(gn_s);
         float hq = sj * s_gem[0][j], hk = sj * s_gem[1][j];
 #pragma unroll
         for (int c = 0; c < CMAX; ++c)
             if (c < C) {
-                const int ic = s_misc[c] & (DK - 1);
-                const float e = KDA ? s_en[ic] : eg;
                 const float cvj = s_vec[(D::SCV + c) * DK + j];
-                hq += (e * seg_ld<TI>(s_vec + D::SQ * DK, ic)) * cvj;
-                hk += (e * seg_ld<TI>(s_vec + D::SK * DK, ic)) * cvj;
+                hq += s_cqk[0][c] * cvj;
+                hk += s_cqk[1][c] * cvj;
             }
         const float mn = beta * (seg_ld<TI>(s_vec + D::SV * DK, j) - hk - sr);
         st_nt(a.bm + head * (size_t)W * DV + (size_t)n * DV + j, mn);
