@@ -496,8 +496,9 @@ def fidelity(wl, d, h0, Bs: int = 8, T: int = 64):
     H, dk, dv = wl.H, wl.dk, wl.dv
     dev = h0.device
     h = h0[:Bs].clone()          # the reference advances its own copy in place
+    out = inputs.make_outliers(wl.seed, H, dk, dv) if wl.outliers else None
     tok = inputs.device_tokens(wl.seed * 31 + 5, T, Bs, H, dk, dv, per_key=wl.per_key,
-                               beta_lo=wl.beta_lo, beta_hi=wl.beta_hi, device=dev)
+                               beta_lo=wl.beta_lo, beta_hi=wl.beta_hi, device=dev, outliers=out)
     dref = lq.make_dims(Bs, H, dk, dv, wl.W, wl.C, d.decay_mode, wl.smooth)
     o_ref = torch.empty((T, Bs, H, dv), dtype=torch.float32, device=dev)
     lq.lq_gdn_fp32_recurrence(dref, h, T, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], o_ref)
@@ -519,6 +520,90 @@ def fidelity(wl, d, h0, Bs: int = 8, T: int = 64):
     return {"sample": f"B={Bs} H={H} T={T} tokens from the prefilled state",
             f"windowed_W{wl.W}_C{wl.C}_smooth{wl.smooth}": run(wl.W, wl.C, wl.smooth),
             "per_token_W1_C0_nosmooth": run(1, 0, 0)}
+
+
+def w_sweep(steps: int, L: int = 2):
+    """The outlier-stress workload (B=256, H=32, d=128, C=4, outlier key
+    channels and value columns, 2048-token fp32 prefill) at each window length
+    of its sweep: tokens/s of the step (W-1 decode tokens and the fused last
+    token with the flush, per layer, L layers rotated, replayed as a HIP
+    graph), the decode kernel's rate over its algorithmic bytes, the
+    algorithmic bytes per token with the flush amortised over the window, and
+    the output error against the fp32 recurrence (fidelity)."""
+    import torch
+    from recurrent_state_quant_lq_amd import inputs, lq
+    from recurrent_state_quant_lq_amd.configs import PRESETS
+    base = PRESETS["outlier_sweep"]
+    B, H, dk, dv, C = base.B, base.H, base.dk, base.dv, base.C
+    dev = torch.device("cuda:0")
+    out = inputs.make_outliers(base.seed, H, dk, dv)
+    gen = lambda seed, T: inputs.device_tokens(seed, T, B, H, dk, dv, per_key=False, beta_lo=base.beta_lo,
+                                               beta_hi=base.beta_hi, device=dev, outliers=out)
+    d0 = lq.make_dims(B, H, dk, dv, 16, C, lq.LQ_DECAY_SCALAR, base.smooth)
+    h = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=dev)
+    for c0 in range(0, base.prefill, 128):
+        T = min(128, base.prefill - c0)
+        tk = gen(base.seed * 100 + c0, T)
+        lq.lq_gdn_prefill(d0, None, h, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"])
+        del tk
+    res = {"workload": f"outlier_sweep: B={B} H={H} dk=dv={dk} C={C}, 4 key channels x30 and 2 value "
+                       f"columns x20 per head, {base.prefill}-token fp32 prefill, {L} layers rotated",
+           "W": [], "tokens_per_s": [], "decode_avg_launch_us": [], "decode_frac": [],
+           "bytes_per_token_with_flush": [], "max_rel_err": [], "mean_rel_err": []}
+    o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    for W in base.w_sweep:
+        wl = base.with_(W=W)
+        d = lq.make_dims(B, H, dk, dv, W, C, lq.LQ_DECAY_SCALAR, wl.smooth)
+        layers = [lq.LayerState.allocate(d, dev) for _ in range(L)]
+        for st in layers:
+            lq.lq_gdn_state_quantize(st, h)
+        ring = [gen(base.seed * 7 + 13 * W + l, W) for l in range(L)]
+
+        def step():
+            for n in range(W - 1):
+                for l in range(L):
+                    tk = ring[l]
+                    lq.lq_gdn_decode_step(layers[l], n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                          tk["beta"][n], o)
+            for l in range(L):
+                tk, n = ring[l], W - 1
+                lq.lq_gdn_decode_step_flush(layers[l], n, tk["q"][n], tk["k"][n], tk["v"][n], tk["alpha"][n],
+                                            tk["beta"][n], o)
+        step()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        lq.lq_timing_enable(True)
+        step()
+        lq.lq_timing_enable(False)
+        fam, t_ms = lq.lq_timing_collect()
+        dec = [x for f, x in zip(fam, t_ms) if f == lq.LQ_KERNEL_DECODE]
+        dec_bytes = sum(decode_bytes(wl, n) for n in range(W - 1)) * L
+        dec_s = sum(dec) * 1e-3
+        per_tok = (sum(decode_bytes(wl, n) for n in range(W - 1)) + decode_flush_bytes(wl, W)) / (W * B * H)
+        fid = fidelity(wl, d, h, Bs=8, T=64)[f"windowed_W{W}_C{C}_smooth{wl.smooth}"]
+        res["W"].append(W)
+        res["tokens_per_s"].append(round(B * W * L / (ms * 1e-3), 1))
+        res["decode_avg_launch_us"].append(round(1e3 * sum(dec) / max(1, len(dec)), 3))
+        res["decode_frac"].append(round(dec_bytes / dec_s / 1e9 / HBM_PEAK_GBS, 4))
+        res["bytes_per_token_with_flush"].append(round(per_tok, 1))
+        res["max_rel_err"].append(round(fid["max_rel_err"], 5))
+        res["mean_rel_err"].append(round(fid["mean_rel_err"], 5))
+        del layers, ring, graph
+        torch.cuda.empty_cache()
+    res["per_token_W1_C0_nosmooth"] = fidelity(base, d0, h, Bs=8, T=64)["per_token_W1_C0_nosmooth"]
+    del h
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(wl, windows: int, threads: int):
@@ -584,6 +669,8 @@ def main():
                     help="end each window with lq_gdn_decode_step + lq_gdn_window_flush "
                          "instead of the fused lq_gdn_decode_step_flush")
     ap.add_argument("--cpu-windows", type=int, default=128)
+    ap.add_argument("--no-w-sweep", action="store_true",
+                    help="skip the window sweep on the outlier-stress workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (for PMC calibration)")
     args = ap.parse_args()
@@ -772,6 +859,8 @@ def main():
         if two_call:
             res["comparisons"]["two_call_window_end"] = two_call
     del h_prefill
+    if not args.no_compare and not args.no_w_sweep:
+        res["w_sweep"] = w_sweep(max(4, min(16, args.steps)))
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_windows, threads)
