@@ -32,7 +32,9 @@
 // Then:
 //   A. channel lanes: the int8 digits of r o e^g o q and r o e^g o k per
 //      64-channel block; all lanes, in slot groups: rr_i = <k, E_i o k_i>,
-//      a_i = <q, E_i o k_i>; slot n's key and log-decay are stored
+//      a_i = <q, E_i o k_i>; slot n's key and log-decay are stored; the
+//      last CMAX lanes: the compensator coefficients e^{g_n}[idx_c] q[idx_c]
+//      and e^{g_n}[idx_c] k[idx_c]
 //   B. int8 MFMA: sq^T x digits for both vectors at once (wave w owns its
 //      column tiles); value lanes: sum_i rr_i m_i and sum_i a_i m_i
 //   C. value lanes: Hb^T q~, Hb^T k~ with the compensator rows, m_n and o.
