@@ -99,13 +99,27 @@ __device__ __forceinline__ int bits_below(u64 lo, u64 hi, int row) {
     return __popcll(lo & low_bits(row)) + __popcll(hi & low_bits(row - 64));
 }
 
+// Maxima over the four 16-lane rows of a wave for four values at once, with
+// the gfx950 row swaps (v_permlane32_swap: upper half of the first operand
+// <-> lower half of the second; v_permlane16_swap: odd rows of the first <->
+// even rows of the second).  Row r of the result holds the maximum over all
+// 64 lanes' rows of (a, b, c, d)[r], at the lane's position within the row.
+__device__ __forceinline__ uint32_t rows_umax4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(a, c, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(b, d, false, false);
+    // rows of x: max(a0,a2), max(a1,a3), max(c0,c2), max(c1,c3); of y: the same for b and d
+    const uint32_t x = umax(s0[0], s0[1]);
+    const uint32_t y = umax(s1[0], s1[1]);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    return umax(s2[0], s2[1]);
+}
+
 // LDS used by the codec stage.
 template <int DK, int DV, int NW>
 struct CodecLds {
     float m[DK];                 // row magnitudes
-    float cm[NW * 4][DV];        // column maxima per (wave, lane group)
+    uint32_t cm[NW][DV];         // column maxima per wave (bit patterns of non-negative floats)
     float sinv[DV];              // 1 / col_scale
-    float cvt[DV][CMAX];         // compensator rows (column-major), staged for the stores
 };
 
 // Codec of the state held in D layout (H is overwritten).  Writes sq
@@ -198,7 +212,8 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
             }
         if (lane < C) st_nt(out.idx + lane, mine);
     }
-    // compensator rows to LDS, residual rows zeroed
+    // compensator rows stored by the lanes that hold them (one row: CT
+    // consecutive columns from each of 16 lanes), residual rows zeroed
     {
         const u64 half = (w * 16 * RBW >= 64) ? hi : lo;
         const uint32_t bits = (uint32_t)(half >> (row0 & 63)) & ((1u << RPL) - 1u);
@@ -207,9 +222,16 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
 #pragma unroll
             for (int k = 0; k < RPL; ++k)
                 if ((bits >> k) & 1u) {
-                    float* dst = &L.cvt[li * CT][base + __popc(bits & ((1u << k) - 1u))];
+                    float* dst = out.cv + (size_t)(base + __popc(bits & ((1u << k) - 1u))) * DV + li * CT;
+                    if constexpr (CT % 4 == 0) {
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) dst[ct * CMAX] = H[k / 4][ct][k % 4];
+                        for (int c4 = 0; c4 < CT / 4; ++c4)
+                            st_nt4(dst + 4 * c4, H[k / 4][4 * c4][k % 4], H[k / 4][4 * c4 + 1][k % 4],
+                                   H[k / 4][4 * c4 + 2][k % 4], H[k / 4][4 * c4 + 3][k % 4]);
+                    } else {
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) st_nt(dst + ct, H[k / 4][ct][k % 4]);
+                    }
                 }
         }
         // zeroed by a 0/1 factor, branch-free (a -0 it may leave has
@@ -221,9 +243,10 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
             for (int ct = 0; ct < CT; ++ct) H[k / 4][ct][k % 4] = H[k / 4][ct][k % 4] * keep;
         }
     }
-    // column maxima of the residual, per lane group
+    // column maxima of the residual: over this lane's rows, then over the
+    // wave's four lane groups (the four lane groups hold the same columns)
     {
-        float cm[CT];
+        uint32_t cm[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             float mx = 0.0f;
@@ -231,23 +254,31 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
             for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) mx = fmaxf(mx, fabsf(H[rb][ct][v]));
-            cm[ct] = mx;
+            cm[ct] = __float_as_uint(mx);
         }
-        store_floats<CT>(&L.cm[w * 4 + lg][li * CT], cm);
+        if constexpr (CT % 4 == 0) {
+            // lane group lg receives column li*CT + 4m + lg
+#pragma unroll
+            for (int m4 = 0; m4 < CT / 4; ++m4)
+                L.cm[w][li * CT + 4 * m4 + lg] = rows_umax4(cm[4 * m4], cm[4 * m4 + 1], cm[4 * m4 + 2], cm[4 * m4 + 3]);
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                uint32_t x = umax(cm[ct], __float_as_uint(swz_xor16(__uint_as_float(cm[ct]))));
+                x = umax(x, (uint32_t)__shfl_xor((int)x, 32, 64));
+                if (lg == 0) L.cm[w][li * CT + ct] = x;
+            }
+        }
     }
     lds_barrier();
     if (t < DV) {
         uint32_t mx = 0u;
 #pragma unroll
-        for (int i = 0; i < NW * 4; ++i) mx = umax(mx, __float_as_uint(L.cm[i][t]));
+        for (int i = 0; i < NW; ++i) mx = umax(mx, L.cm[i][t]);
         const float m = __uint_as_float(mx);
         const float sj = (smooth && m >= kTiny) ? m : 1.0f;
         st_nt(out.s + t, sj);
         L.sinv[t] = 1.0f / sj;
-    }
-    for (int e = t; e < C * (DV / 4); e += NT) {
-        const int p = e / (DV / 4), j = 4 * (e % (DV / 4));
-        st_nt4(out.cv + 4 * e, L.cvt[j][p], L.cvt[j + 1][p], L.cvt[j + 2][p], L.cvt[j + 3][p]);
     }
     lds_barrier();
     // smoothing and row maxima
@@ -357,8 +388,9 @@ struct FlushLds {
     static constexpr int TOK = GB + (KDA ? NPAD * DK * 4 : 0);     // token q | v | alpha (DEC)
     static constexpr int CODEC = TOK + (DEC ? (2 * DK + DV) * 4 : 0);   // codec stage; GEMV partials (DEC)
     static constexpr int NWF = DK / 16 < 4 ? DK / 16 : 4;
-    static constexpr int BYTES = CODEC + (int)sizeof(CodecLds<DK, DV, NWF>);
-    static_assert(!DEC || (2 * DV + 1) * NWF * 4 <= (int)sizeof(CodecLds<DK, DV, NWF>), "GEMV partials");
+    static constexpr int CODEC_BYTES = (int)sizeof(CodecLds<DK, DV, NWF>);
+    static constexpr int GEMV_BYTES = DEC ? (2 * DV + 1) * NWF * 4 : 0;     // DEC partials share the region
+    static constexpr int BYTES = CODEC + (CODEC_BYTES > GEMV_BYTES ? CODEC_BYTES : GEMV_BYTES);
 };
 
 // DEC = true: first decode one token into slot n = N-1 (the window's last
