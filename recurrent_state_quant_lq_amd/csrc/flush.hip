@@ -18,11 +18,11 @@
 //
 // Register layout ("D layout") of H in one workgroup: NW waves; lane l
 // (li = l % 16, lg = l / 16) of wave w holds, for v4 register (rb, ct),
-//     H[row(w, lg, rb, v)][li*CT + ct],   row = w*16*RBW + lg*4*RBW + rb*4 + v,
-// i.e. the MFMA accumulator layout with the rows permuted so that a lane's
-// 4*RBW rows are consecutive: one column's bytes of those rows are one 8-byte
-// access in the stored state (sq_off), and its CT columns are contiguous
-// in row-major fp32 arrays.
+//     H[row(w, lg, rb, v)][16*ct + li],   row = w*16*RBW + lg*4*RBW + rb*4 + v,
+// i.e. the MFMA accumulator layout (tile ct = columns 16ct..16ct+15) with the
+// rows permuted so that a lane's 4*RBW rows are consecutive: one column's
+// bytes of those rows are one 8-byte piece of the stored state (sq_off), and
+// for one tile the pieces of a wave's 64 lanes are 512 contiguous bytes.
 //
 // The codec steps are single IEEE fp32 operations in a fixed order, so the
 // int8 bytes, scales and compensator rows are a function of the fp32 H.
@@ -87,6 +87,19 @@ struct RowBytes<4> {
     static __device__ float get(const uint32_t& x, int k) { return sbyte(x, k); }
 };
 
+// A lane's values of one row in the D layout, one per column tile:
+// x[ct] = p[16 ct] with p at the lane's column li.
+template <int CT>
+__device__ __forceinline__ void load_cols(const float* p, float (&x)[CT]) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) x[ct] = p[16 * ct];
+}
+template <int CT>
+__device__ __forceinline__ void store_cols(float* p, const float (&x)[CT]) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) p[16 * ct] = x[ct];
+}
+
 __device__ __forceinline__ u64 ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // Bits [0, n) set; n may be <= 0 or >= 64.
@@ -146,7 +159,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                 float x[CT];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) x[ct] = H[rb][ct][v];
-                store_floats<CT>(h_out + (size_t)(row0 + rb * 4 + v) * DV + li * CT, x);
+                store_cols<CT>(h_out + (size_t)(row0 + rb * 4 + v) * DV + li, x);
             }
     }
     // row magnitudes
@@ -212,8 +225,8 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
             }
         if (lane < C) st_nt(out.idx + lane, mine);
     }
-    // compensator rows stored by the lanes that hold them (one row: CT
-    // consecutive columns from each of 16 lanes), residual rows zeroed
+    // compensator rows stored by the lanes that hold them (one row: 16
+    // lanes, one column of each tile), residual rows zeroed
     {
         const u64 half = (w * 16 * RBW >= 64) ? hi : lo;
         const uint32_t bits = (uint32_t)(half >> (row0 & 63)) & ((1u << RPL) - 1u);
@@ -222,16 +235,9 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
 #pragma unroll
             for (int k = 0; k < RPL; ++k)
                 if ((bits >> k) & 1u) {
-                    float* dst = out.cv + (size_t)(base + __popc(bits & ((1u << k) - 1u))) * DV + li * CT;
-                    if constexpr (CT % 4 == 0) {
+                    float* dst = out.cv + (size_t)(base + __popc(bits & ((1u << k) - 1u))) * DV + li;
 #pragma unroll
-                        for (int c4 = 0; c4 < CT / 4; ++c4)
-                            st_nt4(dst + 4 * c4, H[k / 4][4 * c4][k % 4], H[k / 4][4 * c4 + 1][k % 4],
-                                   H[k / 4][4 * c4 + 2][k % 4], H[k / 4][4 * c4 + 3][k % 4]);
-                    } else {
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) st_nt(dst + ct, H[k / 4][ct][k % 4]);
-                    }
+                    for (int ct = 0; ct < CT; ++ct) st_nt(dst + 16 * ct, H[k / 4][ct][k % 4]);
                 }
         }
         // zeroed by a 0/1 factor, branch-free (a -0 it may leave has
@@ -257,16 +263,16 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
             cm[ct] = __float_as_uint(mx);
         }
         if constexpr (CT % 4 == 0) {
-            // lane group lg receives column li*CT + 4m + lg
+            // lane group lg receives column 16 (4m + lg) + li
 #pragma unroll
             for (int m4 = 0; m4 < CT / 4; ++m4)
-                L.cm[w][li * CT + 4 * m4 + lg] = rows_umax4(cm[4 * m4], cm[4 * m4 + 1], cm[4 * m4 + 2], cm[4 * m4 + 3]);
+                L.cm[w][16 * (4 * m4 + lg) + li] = rows_umax4(cm[4 * m4], cm[4 * m4 + 1], cm[4 * m4 + 2], cm[4 * m4 + 3]);
         } else {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 uint32_t x = umax(cm[ct], __float_as_uint(swz_xor16(__uint_as_float(cm[ct]))));
                 x = umax(x, (uint32_t)__shfl_xor((int)x, 32, 64));
-                if (lg == 0) L.cm[w][li * CT + ct] = x;
+                if (lg == 0) L.cm[w][16 * ct + li] = x;
             }
         }
     }
@@ -283,7 +289,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
     lds_barrier();
     // smoothing and row maxima
     float inv[CT];
-    load_floats<CT>(&L.sinv[li * CT], inv);
+    load_cols<CT>(&L.sinv[li], inv);
     float rho[RPL];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
@@ -309,7 +315,8 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
         if (li < RPL) st_nt(out.r + row0 + li, live ? my / 127.0f : 0.0f);
         row_bcast_all<RPL>(lmy, lam);
     }
-    // rounding through the offset form; one column's RPL bytes per store.
+    // rounding through the offset form; one column's RPL bytes per store,
+    // 512 contiguous bytes per tile and wave.
     // The clamp to +-127 never binds: |Y| <= rho and lam = RN(127/rho) give
     // |Y * lam| <= 127 (1 + 2^-24)^2, which rounds to at most 127.
 #pragma unroll
@@ -317,10 +324,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
         uint32_t z[RPL];
 #pragma unroll
         for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
-        int8_t* dst = out.sq + sq_off<DK>(row0, li * CT + ct);
-        // (write-back stores: a column's 128 bytes come from 16 lanes of four
-        // waves, and L2 merges the pieces into whole lines; streamed, each
-        // piece would reach memory as a partial write)
+        int8_t* dst = out.sq + sq_off<DK>(row0, 16 * ct + li);
         if constexpr (RPL == 8)
             *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low4(z[0], z[1], z[2], z[3]),
                                                         pack_low4(z[4], z[5], z[6], z[7]));
@@ -495,12 +499,12 @@ void flush_kernel(FlushArgs a) {
                                DK * (int)sizeof(TI) / 4);
         if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, W - 1, s_G, w, lane);
     }
-    // D-layout bytes of the base state: column li*CT + ct, this lane's RPL rows
+    // D-layout bytes of the base state: column 16 ct + li, this lane's RPL rows
     const int row0 = row_of<DK, DV>(w, lg, 0, 0);
     typename RBy::T hb[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-        hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + sq_off<DK>(row0, li * CT + ct));
+        hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + sq_off<DK>(row0, 16 * ct + li));
     all_loads_barrier();
 
     // log-decay of the last slot, g_{N-1}[row]: from the buffer, or (DEC) the
@@ -555,7 +559,7 @@ void flush_kernel(FlushArgs a) {
     v4f H[RBW][CT];
     {
         float sc[CT], rr[RPL], gm[RPL];
-        load_floats<CT>(s_s + li * CT, sc);
+        load_cols<CT>(s_s + li, sc);
         load_floats<RPL>(s_r + row0, rr);
         if constexpr (KDA) {
 #pragma unroll
@@ -583,7 +587,7 @@ void flush_kernel(FlushArgs a) {
             const bool cl = c < C;
             const int ic = cl ? s_idx[c] : -1;
             float bcv[CT];
-            load_floats<CT>(s_cv + (cl ? c : 0) * DV + li * CT, bcv);
+            load_cols<CT>(s_cv + (cl ? c : 0) * DV + li, bcv);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) bcv[ct] = cl ? bcv[ct] : 0.0f;
 #pragma unroll
@@ -604,7 +608,7 @@ void flush_kernel(FlushArgs a) {
         if (4 * ks < NM) {
             const bool live = 4 * ks + lg < NM;
             float bm[CT];
-            load_floats<CT>(&s_M[(4 * ks + lg) * DV + li * CT], bm);
+            load_cols<CT>(&s_M[(4 * ks + lg) * DV + li], bm);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) bm[ct] = live ? bm[ct] : 0.0f;
 #pragma unroll
@@ -641,19 +645,19 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) p[ct] = __builtin_fmaf(H[rb][ct][v], x[v], p[ct]);
             }
-            float* dst = s_pq + vec * NW * DV + w * DV + li * CT;
+            float* dst = s_pq + vec * NW * DV + w * DV + li;
             if constexpr (CT % 4 == 0) {
-                // row r of rows_sum4's result: the total of column 4m + r
+                // row r of rows_sum4's result: the total of tile 4m + r's column
 #pragma unroll
                 for (int m = 0; m < CT / 4; ++m)
-                    dst[4 * m + lg] = rows_sum4(p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]);
+                    dst[16 * (4 * m + lg)] = rows_sum4(p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]);
             } else {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     p[ct] += swz_xor16(p[ct]);
                     p[ct] += __shfl_xor(p[ct], 32, 64);
                 }
-                if (lg == 0) store_floats<CT>(dst, p);
+                if (lg == 0) store_cols<CT>(dst, p);
             }
         }
         lds_barrier();
@@ -674,7 +678,7 @@ void flush_kernel(FlushArgs a) {
         lds_barrier();
         {
             float mv[CT];
-            load_floats<CT>(s_M + n * DV + li * CT, mv);
+            load_cols<CT>(s_M + n * DV + li, mv);
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 float xk[4];
@@ -720,7 +724,7 @@ __global__ __launch_bounds__((FS<DK, DV>::NT)) void quantize_kernel(QuantArgs a)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             float x[CT];
-            load_floats<CT>(h + (size_t)row_of<DK, DV>(w, lg, rb, v) * DV + li * CT, x);
+            load_cols<CT>(h + (size_t)row_of<DK, DV>(w, lg, rb, v) * DV + li, x);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) H[rb][ct][v] = x[ct];
         }
