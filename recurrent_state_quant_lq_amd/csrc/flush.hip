@@ -13,8 +13,8 @@
 //     H = Gamma Hb + Kt^T M            (dk x dv,  contraction over N)
 // with Kt[i][c] = exp(g_{N-1}[c] - g_i[c]) k_i[c], M = [m_0; ...; m_{N-1}] and
 // Gamma = diag exp(g_{N-1}).  Gamma Hb is dequantized into the accumulators
-// of v_mfma_f32_16x16x4_f32; the compensator rows Gamma P^T cv are one more
-// fp32 MFMA K step whose K dimension runs over the compensator rows.
+// of v_mfma_f32_16x16x4_f32; each compensator row gamma(idx_c) cv_c is added
+// to row idx_c by the 16 lanes that hold it.
 //
 // Register layout ("D layout") of H in one workgroup: NW waves; lane l
 // (li = l % 16, lg = l / 16) of wave w holds, for v4 register (rb, ct),
@@ -240,14 +240,15 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                     for (int ct = 0; ct < CT; ++ct) st_nt(dst + 16 * ct, H[k / 4][ct][k % 4]);
                 }
         }
-        // zeroed by a 0/1 factor, branch-free (a -0 it may leave has
-        // magnitude 0 and rounds to byte 0 like +0)
+        // zeroed; a register is visited only if some lane of the wave holds a
+        // compensator row in it
 #pragma unroll
-        for (int k = 0; k < RPL; ++k) {
-            const float keep = ((bits >> k) & 1u) ? 0.0f : 1.0f;
+        for (int k = 0; k < RPL; ++k)
+            if (ballot((bits >> k) & 1u)) {
+                const bool z = (bits >> k) & 1u;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) H[k / 4][ct][k % 4] = H[k / 4][ct][k % 4] * keep;
-        }
+                for (int ct = 0; ct < CT; ++ct) H[k / 4][ct][k % 4] = z ? 0.0f : H[k / 4][ct][k % 4];
+            }
     }
     // column maxima of the residual: over this lane's rows, then over the
     // wave's four lane groups (the four lane groups hold the same columns)
@@ -416,7 +417,6 @@ void flush_kernel(FlushArgs a) {
     constexpr int NPAD = WM <= 16 ? 16 : 32;   // slots padded to the MFMA size
     using RBy = RowBytes<RPL>;
     using LY = FlushLds<DK, DV, NPAD, KDA, DEC>;
-    constexpr int KC = CMAX / 4;
 
     __shared__ __align__(16) char smem[LY::BYTES];
     float* s_r = reinterpret_cast<float*>(smem + LY::RS);
@@ -578,28 +578,26 @@ void flush_kernel(FlushArgs a) {
                 for (int ct = 0; ct < CT; ++ct) H[rb][ct][v] = (RBy::get(hb[ct], rb * 4 + v) * rg) * sc[ct];
             }
     }
-    // compensator rows: H += Gamma P^T cv, one K step per 4 rows with
-    // A[rowa][c] = gamma(rowa) [rowa == idx_c] and B[c][col] = cv_c[col]
+    // compensator rows: H[idx_c] += gamma(idx_c) cv_c, added by the 16 lanes
+    // that hold row idx_c (a uniform branch picks the register)
+    for (int c = 0; c < C; ++c) {
+        const int ic = __builtin_amdgcn_readfirstlane(s_idx[c]);
+        const int r = ic - w * 16 * RBW;                  // row among this wave's rows
+        if (r < 0 || r >= 16 * RBW) continue;             // another wave's row
+        const float g = __expf(glast(ic));
+        float cvv[CT];
+        load_cols<CT>(s_cv + c * DV + li, cvv);
+        if (lg == r / RPL) {
+            const int k = r % RPL;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-        if (4 * kc < C) {
-            const int c = 4 * kc + lg;
-            const bool cl = c < C;
-            const int ic = cl ? s_idx[c] : -1;
-            float bcv[CT];
-            load_cols<CT>(s_cv + (cl ? c : 0) * DV + li, bcv);
+            for (int kk = 0; kk < RPL; ++kk)
+                if (kk == k) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) bcv[ct] = cl ? bcv[ct] : 0.0f;
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
-                const float g = __expf(glast(rowa));
-                const float av = ic == rowa ? g : 0.0f;
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bcv[ct], H[rb][ct], 0, 0, 0);
-            }
+                    for (int ct = 0; ct < CT; ++ct)
+                        H[kk / 4][ct][kk % 4] = __builtin_fmaf(g, cvv[ct], H[kk / 4][ct][kk % 4]);
+                }
         }
+    }
 
     // window terms: B = M rows (rows from NM on are zero; the buffer may hold
     // anything there)
