@@ -142,7 +142,6 @@ template <int DK, int DV, int RBW, int CT, int NW>
 __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const CodecOut& out,
                             float* __restrict__ h_out, int C, int smooth) {
     constexpr int RPL = FS<DK, DV>::RPL;
-    constexpr int NT = 64 * NW;
     // the lane indices are recomputed here (an opaque copy of the thread id), so
     // the compiler keeps no codec address live through the caller's registers
     int t = threadIdx.x;
@@ -413,7 +412,7 @@ __global__ __launch_bounds__((FS<DK, DV>::NT))
 __attribute__((amdgpu_waves_per_eu(WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2), WM <= 16 ? (KDA ? 3 : 4) : (KDA ? 1 : 2))))
 void flush_kernel(FlushArgs a) {
     using S = FS<DK, DV>;
-    constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, RPL = S::RPL, NT = S::NT;
+    constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, RPL = S::RPL;
     constexpr int NPAD = WM <= 16 ? 16 : 32;   // slots padded to the MFMA size
     using RBy = RowBytes<RPL>;
     using LY = FlushLds<DK, DV, NPAD, KDA, DEC>;

@@ -74,8 +74,11 @@ struct PF {
     static constexpr int STG = ST + CL * CL;               // bf16 q | k | v rows as loaded [3][CL][DK]
     static constexpr int FLOATS = STG + (sizeof(TI) == 2 ? 3 * CL * DK / 2 : 0);
     // waves per SIMD the registers are sized for (4: 128 registers, the state
-    // tiles take 64 of them at d = 128)
-    static constexpr int WPE = 4;
+    // tiles take 64 of them at d = 128).  Per-key decay at d = 128 keeps
+    // 63-75 KB of LDS per workgroup, i.e. two workgroups (two waves per SIMD)
+    // per CU, and is given the registers of that occupancy; at d = 16 with bf16
+    // rows it needs 129 registers, i.e. three waves.
+    static constexpr int WPE = !KDA ? 4 : DK == 128 ? 2 : (DK == 16 && sizeof(TI) == 2) ? 3 : 4;
 };
 
 template <int DK, int DV, bool KDA, typename TI>
@@ -106,7 +109,6 @@ void prefill_kernel(PrefillArgs a) {
     const size_t head = blockIdx.x;
     const size_t heads = (size_t)a.heads;
     const int T = a.T;
-    constexpr int GD = KDA ? DK : 1;
 
     // state tiles: H[rt][ct][v] = H[rt*16 + 4*lg + v][col(ct)], col(ct) = (w*CTW + ct)*16 + li
     float* hp = a.h + head * (size_t)DK * DV;
