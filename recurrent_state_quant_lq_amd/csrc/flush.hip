@@ -58,7 +58,6 @@ struct FS {
     static constexpr int NT = 64 * NW;
     static constexpr int RBW = RB / NW;
     static constexpr int RPL = 4 * RBW;                // consecutive rows per lane group
-    static constexpr int TPW = CT / NW > 0 ? CT / NW : 1;   // contraction-1 tiles per wave
     static constexpr int KS = (DK + 63) / 64;
     static_assert(DK % 16 == 0 && RB % NW == 0 && (CT % NW == 0 || CT < NW), "tile shape");
     // every wave's rows lie in one 64-row half
