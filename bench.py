@@ -104,16 +104,17 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(wl, hsh: str):
+def read_traffic(hsh: str, alg_bytes: int):
     """Measured HBM bytes per decode launch from the committed rocprofv3 PMC
-    summary, if it was taken on the current decode kernel."""
+    summary, if it was taken on the current decode kernel and on a workload
+    with the same algorithmic bytes per launch (i.e. the same workload)."""
     if not os.path.exists(PMC_FILE):
         return None
     for line in open(PMC_FILE):
         line = line.strip()
         if line.startswith("{") and '"kernel_hash"' in line:
             rec = json.loads(line)
-            if rec.get("kernel_hash") == hsh:
+            if rec.get("kernel_hash") == hsh and rec.get("algorithmic_bytes_per_launch") == alg_bytes:
                 return rec.get("hbm_bytes_per_launch")
     return None
 
@@ -819,10 +820,11 @@ def main():
                     "step": "last token by lq_gdn_decode_step, then lq_gdn_window_flush (eager)"}
 
     hsh = kernel_hash()
-    traffic = read_traffic(wl, hsh)
+    traffic = read_traffic(hsh, int(sum(dec_bytes) / ND))
     roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic if fuse else None,
-            "kernel": f"lq_gdn_decode_step (decode_kernel<128,128,16,GDN>, slots 0..{ND - 1})",
+            "kernel": f"lq_gdn_decode_step (decode_kernel<{wl.dk},{wl.dv},{16 if W <= 16 else 32},"
+                      f"{'KDA' if wl.per_key else 'GDN'}>, slots 0..{ND - 1})",
             "avg_launch_us": round(dec_total_s * 1e6 / ND, 3),
             "bytes_per_launch_avg": int(sum(dec_bytes) / ND)}
 
