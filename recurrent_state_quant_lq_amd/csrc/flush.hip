@@ -406,11 +406,11 @@ struct FlushLds {
 // m_n = beta (v - H'^T k), o = H'^T q + <q, k> m_n, and H = H' + k m_n^T.
 // The GEMVs run on the fp32 registers (fma, lane-group rows summed with the
 // row swaps, waves through LDS).
-// Registers sized for 4 workgroups per CU (one wave per SIMD each) with up to
-// 16 slots, 2 (scalar decay) or 1 (per-key decay) with 32.
+// Registers sized for the workgroups per CU (one wave per SIMD each) that the
+// LDS allows: 4 with up to 16 slots; with 32, 3 (scalar decay) or 2 (per-key).
 template <int DK, int DV, int WM, bool KDA, bool DEC, typename TI>
 __global__ __launch_bounds__((FS<DK, DV>::NT))
-__attribute__((amdgpu_waves_per_eu(WM <= 16 ? 4 : (KDA ? 1 : 2), WM <= 16 ? 4 : (KDA ? 1 : 2))))
+__attribute__((amdgpu_waves_per_eu(WM <= 16 ? 4 : (KDA ? 2 : 3), WM <= 16 ? 4 : (KDA ? 2 : 3))))
 void flush_kernel(FlushArgs a) {
     using S = FS<DK, DV>;
     constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, RPL = S::RPL;
