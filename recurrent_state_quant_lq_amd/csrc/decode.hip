@@ -96,8 +96,9 @@ struct Dec {
     static constexpr int SEGL = DK / 4;                  // lanes (16-byte chunks) per segment
     static_assert(DK % 4 == 0 && 64 % SEGL == 0 && SCV * SEGL <= NT, "segments");
     // waves per SIMD the register budget is sized for (8: all 8 workgroups of a
-    // CU resident; per-key decay needs more registers for its decay rows)
-    static constexpr int WPE = WM <= 16 ? (KDA ? 6 : 8) : 4;
+    // CU resident; per-key decay needs more registers for its decay rows; with
+    // 32 slots, 6 for scalar decay, whose 77 registers fit there without spills)
+    static constexpr int WPE = WM <= 16 ? (KDA ? 6 : 8) : (KDA ? 4 : 6);
 };
 
 template <int DK, int DV, int WM, bool KDA, int NB, typename TI>
