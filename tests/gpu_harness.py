@@ -1,4 +1,4 @@
-"""Shared driver of the GPU parity tests: runs the HIP path and the CPU oracle
+"""Shared runner of the GPU parity tests: runs the HIP path and the CPU oracle
 side by side on the same seeded inputs, window by window (resync protocol).
 
 Per window both sides start from the ORACLE's codec bytes.  The HIP path runs

@@ -10,7 +10,7 @@
   step, output, quantize); with smoothing off it is the textbook per-row int8
   state.
 * The buffer depends on the window's tokens only, an early (partial) flush
-  equals the plain recurrence, and the C whole-run driver equals the
+  equals the plain recurrence, and the C whole-run runner equals the
   per-window composition of the primitives.
 """
 import numpy as np
@@ -143,7 +143,7 @@ def test_early_flush_equals_recurrence(orc, N):
 
 
 @pytest.mark.parametrize("per_key", [False, True])
-def test_c_driver_equals_window_composition(orc, per_key):
+def test_c_runner_equals_window_composition(orc, per_key):
     dk, dv, W, C, T = 32, 32, 8, 2, 8 * 5
     tok = _tok(700 + per_key, T, dk, dv, per_key)
     cd0 = orc.quantize(np.random.default_rng(7).standard_normal((dk, dv)).astype(np.float32), C)
