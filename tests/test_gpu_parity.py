@@ -83,7 +83,9 @@ def test_outlier_sweep_full_size_sampled(W):
     (64, 32, 3, False, 1, 70),
     (128, 1, 0, False, 0, 7),     # W = 1: per-token quantization
     (128, 16, 4, True, 1, 37),
+    (128, 16, 8, False, 1, 37),   # eight compensator rows: several per wave
     (128, 32, 8, True, 0, 33),
+    (128, 32, 6, False, 1, 40),
     (128, 5, 2, False, 1, 12),    # W not a power of two
 ])
 def test_shapes_and_edges(dk, W, C, kda, smooth, T):
@@ -750,7 +752,9 @@ def test_fused_decode_flush_presets(name, sample, T):
     (64, 8, 8, True, 1, 21),
     (64, 32, 3, False, 1, 70),
     (128, 1, 0, False, 0, 7),     # W = 1: the fused call is the whole window
+    (128, 16, 8, False, 1, 37),   # eight compensator rows: several per wave
     (128, 32, 8, True, 0, 33),
+    (128, 32, 6, False, 1, 40),
     (128, 5, 2, False, 1, 12),
 ])
 def test_fused_decode_flush_shapes(dk, W, C, kda, smooth, T):
