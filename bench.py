@@ -842,7 +842,10 @@ def main():
                    "prefill": wl.prefill},
         "launch": {"mode": "eager" if args.eager else "hip_graph_replay",
                    "eager_ms_per_step": round(eager_ms, 4),
-                   "eager_tokens_per_s": round(tokens_per_step / (eager_ms * 1e-3), 1)},
+                   "eager_tokens_per_s": round(tokens_per_step / (eager_ms * 1e-3), 1),
+                   # the step's kernels back to back, from the per-launch durations:
+                   # against ms_per_step it shows how much of the timed step is kernel time
+                   "kernel_ms_per_step": round(L * (sum(dec_avg_us) + fl_avg_us) * 1e-3, 4)},
         "roofline": roof,
         "state_GBps": round(dec_gbs, 1),
         ("decode_flush" if fuse else "flush"): {
