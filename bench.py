@@ -647,6 +647,8 @@ def main():
             k = argv.index("--")
             cmd = " ".join(argv[k + 1:])
             argv = argv[:k]
+        if not cmd.strip():
+            sys.exit(f"bench.py {sys.argv[1]}: give the commands that made the data after --")
         if sys.argv[1] == "--trace-summary":
             trace_summary(argv[0], argv[1], cmd)
         elif sys.argv[1] == "--counter-summary":
