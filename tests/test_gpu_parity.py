@@ -72,6 +72,20 @@ def test_outlier_sweep_full_size_sampled(W):
            f"outlier_sweep W={W}")
 
 
+@pytest.mark.parametrize("name,fused", [("gdn_batched", True), ("gdn_batched", False), ("kda", True),
+                                         ("outlier_sweep", True)])
+@pytest.mark.parametrize("seed", [101, 202])
+def test_full_size_other_seeds(name, fused, seed):
+    """The full-size presets with other input seeds and heads drawn from a
+    seeded generator (three windows, each resynchronised to the oracle)."""
+    wl = PRESETS[name].with_(seed=seed)
+    rng = np.random.default_rng(seed + len(name))
+    sample = sorted({(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(3)})
+    T = 2 * wl.W + 3 if name == "outlier_sweep" else 3 * wl.W
+    _check(resync_run(wl, sample, host_tokens=False, T=T, fused=fused),
+           f"{name} seed={seed} fused={fused} heads={sample}")
+
+
 # ---------------------------------------------------------------------------
 # smaller shapes, ragged windows, degenerate settings
 # ---------------------------------------------------------------------------
