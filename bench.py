@@ -266,12 +266,16 @@ def counter_summary(out_md: str, dirs, command: str):
     print(json.dumps(rec))
 
 
-def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
+def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps, lq_graph_value=None):
     """The same workload through (1) a dense fp32-state decode step (the
     library's fp32 recurrence, one token per launch: reads and writes the
     64 KB fp32 state of every head) and (2) per-token int8 requantization
     (W = 1, no compensators, no smoothing), plus the output error of both int8
-    schemes against the fp32 recurrence on a sample of heads."""
+    schemes against the fp32 recurrence on a sample of heads.  Rates are eager
+    launches set against the eager rate lq_value; the bf16-I/O step is also
+    replayed as a HIP graph and set against the graph-replay rate
+    lq_graph_value, since eager launches here are close to host-bound and
+    their rate moves with the host."""
     import torch
     from recurrent_state_quant_lq_amd import inputs, lq
     W = wl.W
@@ -420,8 +424,17 @@ def comparisons(wl, L, d, h0, ring, lq_value, lq_decode_us, steps):
                                         tk["beta"][n], ob)
     tpsb, msb = timed(bf16_step, B * W * L)
     decb = kernel_us(bf16_step, lq.LQ_KERNEL_DECODE)
-    out["bf16_io"] = {"tokens_per_s": round(tpsb, 1), "ms_per_step": round(msb, 4),
-                      "vs_fp32_io": round(tpsb / lq_value, 3), "decode_avg_launch_us": round(decb, 3)}
+    out["bf16_io"] = {"eager_tokens_per_s": round(tpsb, 1), "eager_ms_per_step": round(msb, 4),
+                      "eager_vs_fp32_io": round(tpsb / lq_value, 3), "decode_avg_launch_us": round(decb, 3)}
+    if lq_graph_value:
+        gb = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gb):
+            bf16_step()
+        torch.cuda.synchronize()
+        tpsg, msg = timed(gb.replay, B * W * L)
+        out["bf16_io"].update({"graph_tokens_per_s": round(tpsg, 1), "graph_ms_per_step": round(msg, 4),
+                               "graph_vs_fp32_io": round(tpsg / lq_graph_value, 3)})
+        del gb
     del layb, ringb
     torch.cuda.empty_cache()
     # batch sweep of the decode kernel: at B/2 and 2B the same step (fresh
@@ -860,9 +873,11 @@ def main():
     if not args.no_compare:
         del layers
         torch.cuda.empty_cache()
-        # every comparison runs eager launches, so it is set against the eager rate
+        # the comparisons run eager launches, set against the eager rate (the
+        # bf16-I/O step also as a graph replay, set against the graph rate)
         res["comparisons"] = comparisons(wl, L, d, h_prefill, ring, tokens_per_step / (eager_ms * 1e-3),
-                                         dec_total_s * 1e6 / ND, max(4, min(16, args.steps)))
+                                         dec_total_s * 1e6 / ND, max(4, min(16, args.steps)),
+                                         None if args.eager else value)
         if two_call:
             res["comparisons"]["two_call_window_end"] = two_call
     del h_prefill
