@@ -50,3 +50,17 @@ def test_headline_step_figures():
     assert sum(bench.decode_bytes(wl, n) for n in range(wl.W - 1)) // (wl.W - 1) == 60932096
     assert bench.decode_flush_bytes(wl, wl.W) == 117653504
     assert bench.flush_bytes(wl, wl.W) == heads * 55392
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})])
+def test_more_than_one_gpu_is_refused(argv, env):
+    """The benchmark times one GPU's share; asked for several (a flag or a
+    launcher's WORLD_SIZE) it exits with status 2 and says why, before
+    touching a device."""
+    import subprocess
+    e = dict(os.environ, **env)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], env=e,
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "runs on one GPU" in r.stderr
+    assert r.stdout == ""
