@@ -85,7 +85,12 @@ def test_textbook_per_row_int8_matches_torch(orc):
                                      torch.qint8).int_repr().numpy()
     diff = np.abs(ref.astype(int) - cd["sq"].astype(int))
     assert diff.max() <= 1
-    assert (diff > 0).sum() <= 3          # only exact-half cases may round apart
+    # torch divides by the scale, the codec multiplies by 127/rho: the two
+    # products differ by an ulp or two, so they may round apart only where
+    # the exact quotient lies within a few ulps of a half-integer
+    x = H.astype(np.float64) / (amax.astype(np.float64)[:, None] / 127.0)
+    near_tie = np.abs(np.abs(x - np.trunc(x)) - 0.5) < 1e-4
+    assert not (diff > 0)[~near_tie].any()
     # the row maximum lands on +-127
     rows = np.arange(64)
     assert (np.abs(cd["sq"][rows, np.abs(H).argmax(1)]) == 127).all()
@@ -189,3 +194,92 @@ def test_tiny_magnitudes_stay_finite(orc, smooth):
         err = np.abs(orc.dequantize(cd) - M.astype(np.float64))
         lsb = cd["r"].astype(np.float64)[:, None] * cd["s"].astype(np.float64)[None, :]
         assert (err <= np.maximum(lsb * (0.5 + 1e-4), 2.0 ** -120)).all()
+
+
+# Half-integer quotients: the row maximum is 127 (smoothing off), so the row
+# multiplier 127/rho is exactly 1 and every entry below is its own quotient.
+_TIES = np.array([127.0, 0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5, 62.5, 125.5, 126.5,
+                  -126.5, 0.25, -0.75, 0.0], np.float32)
+_TIES_HALF_EVEN = np.array([127, 0, 2, 2, 4, 0, -2, -2, -4, 62, 126, 126, -126, 0, -1, 0])
+
+
+@pytest.mark.parametrize("C", [0, 1])
+def test_exact_ties_round_half_to_even(orc, C):
+    """The int8 rounding takes exact half-way quotients to the even integer
+    (the reading that fixes the otherwise unstated rounding mode).  Rounding
+    half away from zero would give 1, 3, 4, -1, ... on the second row."""
+    H = np.stack([_TIES * np.float32(0.5), _TIES, -_TIES[::-1]])
+    if C:
+        H = np.concatenate([np.full((1, _TIES.size), 1000.0, np.float32), H])
+    cd = orc.quantize(H, C, smooth=0)
+    sq = cd["sq"][C:].astype(int)
+    assert cd["r"][C:].tolist() == [0.5, 1.0, 1.0]
+    # row 1 is _TIES itself: rho = 127, multiplier 1
+    assert (sq[1] == _TIES_HALF_EVEN).all()
+    assert (sq[2] == -_TIES_HALF_EVEN[::-1]).all()
+    # row 0 is _TIES / 2: rho = 63.5, multiplier 2, quotients = _TIES again
+    assert (sq[0] == _TIES_HALF_EVEN).all()
+
+
+def test_exact_ties_match_torch_rounding(orc):
+    """Library pin of the same rounding: torch's per-channel int8 quantizer at
+    scale 1 rounds the exact half-way values identically."""
+    torch = pytest.importorskip("torch")
+    cd = orc.quantize(_TIES[None, :], 0, smooth=0)
+    assert cd["r"][0] == np.float32(1.0)
+    ref = torch.quantize_per_channel(torch.from_numpy(_TIES[None, :].copy()),
+                                     torch.tensor([1.0], dtype=torch.double),
+                                     torch.zeros(1, dtype=torch.long), 0, torch.qint8).int_repr().numpy()
+    assert (cd["sq"].astype(int) == ref.astype(int)).all()
+
+
+def test_exact_ties_with_smoothing(orc):
+    """Exact ties survive smoothing when every column maximum is a power of
+    two: row 0 holds 128 in every column (s_j = 128, an exact division), and
+    a row whose largest entry is 127 gets rho = 127/128 and multiplier 128,
+    so its quotients are its own entries again."""
+    dv = _TIES.size
+    H = np.stack([np.full(dv, 128.0, np.float32), _TIES])
+    cd = orc.quantize(H, 0, smooth=1)
+    assert (cd["s"] == np.float32(128.0)).all()
+    assert (cd["sq"][1].astype(int) == _TIES_HALF_EVEN).all()
+
+
+def test_smoothing_worked_example(orc):
+    """A hand-worked 4 x 3 case of compensator extraction then smoothing.
+
+        H = [[ 50, -60, 70  ],      row maxima 70, 2, 4, 2: C = 1 takes row 0
+             [  1,  -2, 0.5 ],
+             [ -4,   1, 0.25],
+             [  2,   0, -1  ]]
+
+    The smoothing factors are the column maxima of the residual (rows 1-3):
+    s = [4, 2, 1], not the column maxima of H ([50, 60, 70]).  Then
+    Y = R / s = [[.25, -1, .5], [-1, .5, .25], [.5, 0, -1]], each residual row
+    has rho = 1 (r = 1/127) and sq = rint(127 Y): 31.75 -> 32, 63.5 -> 64."""
+    H = np.array([[50, -60, 70], [1, -2, 0.5], [-4, 1, 0.25], [2, 0, -1]], np.float32)
+    cd = orc.quantize(H, 1, smooth=1)
+    assert list(cd["idx"]) == [0]
+    assert cd["cv"][0].tolist() == [50, -60, 70]
+    assert cd["s"].tolist() == [4.0, 2.0, 1.0]
+    assert (cd["r"] == np.float32([0.0, 1 / 127, 1 / 127, 1 / 127])).all()
+    assert cd["sq"].tolist() == [[0, 0, 0], [32, -127, 64], [-127, 64, 32], [64, 0, -127]]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_smoothing_reaches_full_range_in_every_residual_column(orc, seed):
+    """Smoothing by the residual's column maxima puts a value of magnitude
+    (about) 1 in every nonzero residual column, in a row whose own maximum it
+    then is, so every such column holds a byte of magnitude 127.  The outlier
+    rows carry every column's maximum of H here: had the factors come from H,
+    the residual columns would reach only about 127/40."""
+    rng = np.random.default_rng(300 + seed)
+    H = _rand(rng, 64, 48)
+    rows = rng.choice(64, 4, replace=False)
+    H[rows] = (rng.choice([-1, 1], (4, 48)) * 40 * np.abs(H).max()).astype(np.float32)
+    cd = orc.quantize(H, 4, smooth=1)
+    assert sorted(cd["idx"]) == sorted(rows)
+    keep = np.setdiff1d(np.arange(64), rows)
+    colmax = np.abs(H[keep]).max(0)
+    assert (cd["s"] == colmax).all()
+    assert (np.abs(cd["sq"][keep].astype(int)).max(0) == 127).all()

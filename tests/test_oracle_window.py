@@ -215,3 +215,34 @@ def test_projected_buffer_form(orc):
             np.testing.assert_allclose(m[n], want_m, rtol=0, atol=1e-12 * max(1.0, np.abs(m).max()))
             o = Hb.T @ (eg * q) + a @ m[:n + 1]
             np.testing.assert_allclose(o, res["o"][n], rtol=0, atol=1e-12 * max(1.0, np.abs(o).max()))
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+@pytest.mark.parametrize("flush_tail", [False, True])
+def test_runner_partial_last_window(orc, per_key, flush_tail):
+    """The C runner's last window of T mod W tokens is quantized only when
+    asked (an early flush at the end of a sequence).  Asked, its codec is the
+    codec of the fp32-rounded state that the plain recurrence reaches from the
+    last full window's state over the tail tokens; not asked, the codec stays
+    the one the last full window left.  Either way the tail's outputs are the
+    recurrence's outputs from that state."""
+    dk, dv, W, C = 16, 12, 8, 2
+    T = 2 * W + 5
+    tok = _tok(900 + per_key, T, dk, dv, per_key)
+    cd0 = orc.quantize((np.random.default_rng(9).standard_normal((dk, dv)) * 0.5).astype(np.float32), C)
+    o, cd, _, hf = orc.run_head(dk, dv, per_key, W, C, 1, route=0, use_codec=True, tok=tok,
+                                codec=cd0, flush_tail=flush_tail)
+    head = {k: v[:2 * W] for k, v in tok.items()}
+    _, cd2, _, _ = orc.run_head(dk, dv, per_key, W, C, 1, route=0, use_codec=True, tok=head,
+                                codec=cd0)
+    Hs = orc.dequantize(cd2)
+    for t in range(2 * W, T):
+        ot = orc.step(Hs, tok["q"][t], tok["k"][t], tok["v"][t], tok["alpha"][t], tok["beta"][t],
+                      per_key)
+        assert np.array_equal(ot, o[t])
+    want = orc.quantize(Hs.astype(np.float32), C, 1) if flush_tail else cd2
+    for key in want:
+        assert np.array_equal(cd[key], want[key]), key
+    if flush_tail:
+        assert np.array_equal(hf, Hs.astype(np.float32))
+        assert not np.array_equal(cd["sq"], cd2["sq"])
