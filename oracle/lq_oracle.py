@@ -15,7 +15,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liblq_oracle.so")
+# LQ_ORACLE_LIB may name another build of the same source (the sanitizer build)
+_LIB_PATH = os.environ.get("LQ_ORACLE_LIB") or os.path.join(_HERE, "liblq_oracle.so")
 _lib = None
 
 _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")

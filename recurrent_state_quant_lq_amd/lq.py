@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblq.so")
+# LQ_LIB may name another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("LQ_LIB") or os.path.join(_PKG, "liblq.so")
 
 LQ_OK, LQ_ERR_NULL, LQ_ERR_DIMS, LQ_ERR_UNSUPPORTED, LQ_ERR_WINDOW_FULL, LQ_ERR_POS, \
     LQ_ERR_ALIGN, LQ_ERR_HIP = range(8)
