@@ -15,7 +15,10 @@ and the oracle's own next codec is uploaded into those heads.
 """
 from __future__ import annotations
 
+import os
 import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -107,6 +110,7 @@ class TokenSource:
 
     def __init__(self, wl: Workload, host: bool, chunk: int = 256):
         self.wl, self.host, self.chunk = wl, host, chunk
+        self._last = (None, None)         # the last device chunk drawn: (index, tensors)
         self.out = inputs.make_outliers(wl.seed, wl.H, wl.dk, wl.dv) if wl.outliers else None
         self._host = None
         if host:
@@ -124,9 +128,13 @@ class TokenSource:
         parts = []
         c0, c1 = t0 // self.chunk, (t1 - 1) // self.chunk
         for c in range(c0, c1 + 1):
-            tk = inputs.device_tokens(wl.seed * 1000 + c, self.chunk, wl.B, wl.H, wl.dk, wl.dv,
-                                      per_key=wl.per_key, beta_lo=wl.beta_lo, beta_hi=wl.beta_hi,
-                                      device="cuda", outliers=self.out)
+            if self._last[0] == c:
+                tk = self._last[1]
+            else:
+                tk = inputs.device_tokens(wl.seed * 1000 + c, self.chunk, wl.B, wl.H, wl.dk, wl.dv,
+                                          per_key=wl.per_key, beta_lo=wl.beta_lo, beta_hi=wl.beta_hi,
+                                          device="cuda", outliers=self.out)
+                self._last = (c, tk)
             a = max(t0, c * self.chunk) - c * self.chunk
             b = min(t1, (c + 1) * self.chunk) - c * self.chunk
             parts.append({k: v[a:b] for k, v in tk.items()})
@@ -273,3 +281,100 @@ def free_run(wl: Workload, sample, *, host_tokens: bool, T: int) -> dict:
         flips.append(per)
         t += N
     return dict(o_err=o_err, flips=flips, max_byte_diff=max_step, bytes_per_head=wl.dk * wl.dv)
+
+
+def oracle_threads() -> int:
+    """Worker threads for per-head oracle work (ctypes releases the GIL in
+    each call); at most 16, the host share of a one-GPU machine."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def every_head_window(wl: Workload, *, prefill: int, fused: bool, W=None, log=True) -> Report:
+    """One full-size window checked against the oracle on EVERY head.
+
+    Start: for every head, the oracle's own fp64 recurrence from a zero state
+    over ``prefill`` tokens of the workload's input distribution, rounded to
+    fp32 and quantized by the oracle (heads spread over a thread pool); the
+    codecs are uploaded in one copy per array.  The GPU then runs one window
+    of W tokens (decode steps, then the fused last token or a decode step and
+    a flush) on all heads, and every head is checked as in resync_run:
+    outputs, buffer rows, the flush's fp32 state and the codec bytes."""
+    d = dims_of(wl, W)
+    W = d.W
+    B, H, dk, dv, C = wl.B, wl.H, wl.dk, wl.dv, d.C
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    nthr = oracle_threads()
+    t_start = time.time()
+    src = TokenSource(wl, host=False)
+    pre = {k: v.cpu().numpy() for k, v in src.tokens(0, prefill).items()} if prefill else None
+    win_dev = src.tokens(prefill, prefill + W)
+    win = {k: v.cpu().numpy() for k, v in win_dev.items()}
+
+    def start_codec(bh):
+        b, h = bh
+        if pre is None:
+            Hs = np.zeros((dk, dv))
+        else:
+            _, _, Hs, _ = O.run_head(dk, dv, wl.per_key, prefill, 0, 1, route=0, use_codec=False,
+                                     tok=O.head_tokens(pre, b, h), H0=np.zeros((dk, dv)))
+        return O.quantize(Hs.astype(np.float32), C, d.smooth)
+
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        codecs = list(ex.map(start_codec, heads))
+    cb = dict(sq=np.empty((B, H, dk, dv), np.int8), r=np.empty((B, H, dk), np.float32),
+              s=np.empty((B, H, dv), np.float32), idx=np.empty((B, H, C), np.int32),
+              cv=np.empty((B, H, C, dv), np.float32))
+    for (b, h), cd in zip(heads, codecs):
+        for key in cb:
+            cb[key][b, h] = cd[key]
+    if log:
+        say(f"  every-head start codecs: {len(heads)} heads, {prefill} prefill tokens, "
+            f"{nthr} threads, {time.time() - t_start:.1f} s")
+    st = lq.LayerState.allocate(d)
+    st.load_codec(cb)
+    o = torch.empty((B, H, dv), dtype=torch.float32, device="cuda")
+    h_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    outs = torch.empty((W, B, H, dv), dtype=torch.float32, device="cuda")
+    for n in range(W):
+        args = (win_dev["q"][n], win_dev["k"][n], win_dev["v"][n], win_dev["alpha"][n],
+                win_dev["beta"][n], o)
+        if fused and n == W - 1:
+            lq.lq_gdn_decode_step_flush(st, n, *args, h_out=h_out)
+        else:
+            lq.lq_gdn_decode_step(st, n, *args)
+        outs[n].copy_(o)
+    if not fused:
+        lq.lq_gdn_window_flush(st, W, h_out)
+    torch.cuda.synchronize()
+    g_o = outs.cpu().numpy()
+    g_h = h_out.cpu().numpy()
+    g_buf = {k: getattr(st, "buf_" + k).cpu().numpy() for k in ("k", "m", "g")}
+    g_cd = st.codec()
+
+    def check(i):
+        b, h = heads[i]
+        res = O.window(codecs[i], O.head_tokens(win, b, h), wl.per_key, W, C, d.smooth, route="wy")
+        oe = rel_err(g_o[:, b, h], res["o"])
+        he = float(np.abs(g_h[b, h] - res["H"]).max() / max(np.abs(res["H"]).max(), 1e-30))
+        ob = oracle_buffer(codecs[i], res["buf"], W)
+        be = max(rel_err(g_buf[key][b, h, :W], ob[key]) for key in ("k", "m", "g"))
+        exact = codec_equal({key: g_cd[key][b, h] for key in g_cd}, O.quantize(g_h[b, h], C, d.smooth))
+        return oe, he, be, exact
+
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        per = list(ex.map(check, range(len(heads))))
+    rep = Report(heads=len(heads), windows=1)
+    for (b, h), (oe, he, be, exact) in zip(heads, per):
+        rep.o_err = max(rep.o_err, oe)
+        rep.h_err = max(rep.h_err, he)
+        rep.buf_err = max(rep.buf_err, be)
+        if not exact:
+            rep.bytes_exact = False
+            rep.mismatches.append((prefill, b, h))
+    if log:
+        say(f"  every-head window checked in {time.time() - t_start:.1f} s")
+    return rep

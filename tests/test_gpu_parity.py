@@ -17,9 +17,9 @@ from recurrent_state_quant_lq_amd.configs import PRESETS
 
 pytestmark = pytest.mark.gpu
 
-from gpu_harness import (BUF_TOL, H_TOL, O_TOL, O_TOL_BF16, codec_equal, dims_of, free_run,  # noqa: E402
-                         head_codec, host, io_tokens, oracle_buffer, rel_err, resync_run, say,
-                         upload_head_codec)
+from gpu_harness import (BUF_TOL, H_TOL, O_TOL, O_TOL_BF16, codec_equal, dims_of,  # noqa: E402
+                         every_head_window, free_run, head_codec, host, io_tokens, oracle_buffer,
+                         rel_err, resync_run, say, upload_head_codec)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,15 +53,27 @@ def test_gdn_layer_all_heads():
 
 
 def test_gdn_batched_full_size_sampled():
+    """B=64 H=32 d=128 W=16: every one of the 64 windows of T = 1024 tokens
+    (the bench's schedule: the last token of each window fused with the flush)."""
     wl = PRESETS["gdn_batched"]
     sample = [(0, 0), (17, 5), (40, 31), (63, 31)]
-    _check(resync_run(wl, sample, host_tokens=False, T=256, log_every=8), "gdn_batched")
+    _check(resync_run(wl, sample, host_tokens=False, log_every=16, fused=True), "gdn_batched")
 
 
 def test_kda_full_size_sampled():
+    """B=32 H=32 d=128 per-key decay: all 32 windows of T = 512 tokens."""
     wl = PRESETS["kda"]
     sample = [(0, 0), (9, 20), (31, 31)]
-    _check(resync_run(wl, sample, host_tokens=False, T=128, log_every=4), "kda")
+    _check(resync_run(wl, sample, host_tokens=False, log_every=8), "kda")
+
+
+def test_outlier_sweep_w16_full_T_sampled():
+    """B=256 H=32 d=128 with outlier channels, W = 16: all 64 windows of
+    T = 1024 tokens after the 2048-token prefill."""
+    wl = PRESETS["outlier_sweep"]
+    sample = [(0, 3), (131, 17), (255, 31)]
+    _check(resync_run(wl, sample, host_tokens=False, W=16, log_every=16, fused=True),
+           "outlier_sweep W=16 T=1024")
 
 
 @pytest.mark.parametrize("W", [8, 16, 32])
@@ -70,6 +82,21 @@ def test_outlier_sweep_full_size_sampled(W):
     sample = [(0, 3), (255, 31)]
     _check(resync_run(wl, sample, host_tokens=False, W=W, T=2 * W + 3, log_every=0),
            f"outlier_sweep W={W}")
+
+
+# One full-size window on EVERY head.  The starting codec of each head is the
+# oracle's own: its fp64 recurrence over a prefill of the workload's
+# distribution, quantized.  The outlier preset's prefill is cut to 128 tokens
+# (its 2048 would cost minutes of host time on 8,192 heads): with decays near
+# 0.95 a state keeps ~20 tokens of memory, so both give states of the same
+# distribution.
+@pytest.mark.parametrize("name,prefill,fused", [
+    ("gdn_batched", 512, True), ("gdn_batched", 512, False), ("kda", 512, True),
+    ("outlier_sweep", 128, True)])
+def test_every_head_full_size_window(name, prefill, fused):
+    wl = PRESETS[name]
+    _check(every_head_window(wl, prefill=prefill, fused=fused, W=16),
+           f"{name} every head, prefill {prefill}, fused={fused}")
 
 
 @pytest.mark.parametrize("name,fused", [("gdn_batched", True), ("gdn_batched", False), ("kda", True),
