@@ -58,6 +58,29 @@ def decode_bytes(wl, n: int) -> int:
     return wl.B * wl.H * (codec + io + (n + 1) * slot)
 
 
+def scope_table_decode_bytes(wl, n: int) -> int:
+    """The decode step's algorithmic bytes at slot n as the hot-path scope
+    table counts them, for the WY buffer with both factors stored: per slot
+    4 (2 dk + dv + a) bytes (k, y, u, g), n slots read and slot n written.
+    23,068 + 1,540 n per head at d = 128 (GDN).  This build's buffer stores
+    one projected vector m per slot instead of y and u (4 (dk + dv + a) bytes),
+    which decode_bytes counts."""
+    dk, dv, C = wl.dk, wl.dv, wl.C
+    a = dk if wl.per_key else 1
+    codec = dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4)
+    io = 4 * (2 * dk + dv + a + 1) + 4 * dv
+    return wl.B * wl.H * (codec + io + (n + 1) * 4 * (2 * dk + dv + a))
+
+
+def decode_read_write_bytes(wl, n: int):
+    """(read, written) bytes per head of one decode launch at slot n."""
+    dk, dv, C = wl.dk, wl.dv, wl.C
+    a = dk if wl.per_key else 1
+    codec = dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4)
+    slot = 4 * (dk + dv + a)
+    return codec + 4 * (2 * dk + dv + a + 1) + n * slot, slot + 4 * dv
+
+
 def flush_bytes(wl, N: int) -> int:
     """Algorithmic HBM bytes of one flush of N slots: read and write the codec,
     read the N buffered slots."""
@@ -620,6 +643,68 @@ def w_sweep(steps: int, L: int = 2):
     return res
 
 
+def stream_read_ceiling(wl, slots: int, L: int, reps: int = 6):
+    """What a bare read of the decode's bytes costs on this GPU: the library's
+    streaming-read reference kernels (lq_measure_stream_read) read, per head,
+    the bytes one decode launch reads per head (mean over slots 0..slots-1,
+    rounded to 16) and write the bytes it writes, over L rotated buffers (the
+    same rotation past the Infinity Cache as the layers).  one_shot is the
+    decode's launch shape (one 256-lane workgroup per head, all loads issued
+    first); persistent walks the same slices with two workgroups per CU."""
+    import torch
+    from recurrent_state_quant_lq_amd import lq
+    heads = wl.B * wl.H
+    rw = [decode_read_write_bytes(wl, n) for n in range(slots)]
+    rd = 16 * round(sum(r for r, _ in rw) / slots / 16)
+    wr = 16 * round(sum(w for _, w in rw) / slots / 16)
+    dev = torch.device("cuda:0")
+    srcs = [torch.randint(0, 255, (heads * rd,), dtype=torch.uint8, device=dev) for _ in range(L)]
+    sinks = [torch.empty((heads * wr,), dtype=torch.uint8, device=dev) for _ in range(L)]
+    grid = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {"bytes_per_launch": heads * (rd + wr), "read_bytes_per_head": rd, "write_bytes_per_head": wr}
+    for mode, name in ((0, "one_shot"), (1, "persistent")):
+        for l in range(L):           # warm-up pass
+            lq.lq_measure_stream_read(srcs[l], rd, heads, mode, grid, sinks[l], wr)
+        lq.lq_timing_enable(True)
+        for _ in range(reps):
+            for l in range(L):
+                lq.lq_measure_stream_read(srcs[l], rd, heads, mode, grid, sinks[l], wr)
+        lq.lq_timing_enable(False)
+        _, t_ms = lq.lq_timing_collect()
+        us = 1e3 * sum(t_ms) / len(t_ms)
+        gbs = heads * (rd + wr) / (us * 1e-6) / 1e9
+        out[name] = {"avg_launch_us": round(us, 3), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    out["persistent"]["grid"] = grid
+    del srcs, sinks
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_cpu():
+    """The host's CPU model, logical CPU count, the CPUs this process may run
+    on, and the cgroup CPU quota if one is set."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    quota = None
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()
+        if q != "max":
+            quota = float(q) / float(per)
+    except (OSError, ValueError):
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable, "cgroup_cpu_quota": quota}
+
+
 def cpu_baseline(wl, windows: int, threads: int):
     """The oracle (plain C, as it is) on the host: the windowed int8 scheme
     for all B*H heads of one layer, `windows` consecutive windows per head
@@ -635,21 +720,49 @@ def cpu_baseline(wl, windows: int, threads: int):
     cd0 = O.quantize(H0, wl.C, wl.smooth)
     heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
 
-    def one(bh):
+    def one(bh, windows=windows):
         t = O.head_tokens(tok, bh[0], bh[1])
         cd = cd0
         for _ in range(windows):
             cd = O.run_head(wl.dk, wl.dv, wl.per_key, wl.W, wl.C, wl.smooth, route=0, use_codec=True,
                             tok=t, codec=cd)[1]
 
+    # the unquantized fp64 sequential recurrence (the fp32-state scheme's
+    # arithmetic), all threads, a sixteenth of the windows
+    seq_windows = max(1, windows // 16)
+
+    def seq(bh):
+        t = O.head_tokens(tok, bh[0], bh[1])
+        H = O.dequantize(cd0)
+        for _ in range(seq_windows):
+            H = O.run_head(wl.dk, wl.dv, wl.per_key, wl.W, 0, 1, route=0, use_codec=False, tok=t, H0=H)[2]
+
     from concurrent.futures import ThreadPoolExecutor
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(one, heads))
-    dt = time.perf_counter() - t0
-    return dict(value=wl.B * wl.W * windows / dt, unit="tokens/s", cores=threads, kind="oracle",
+
+    def timed(fn, items, nthr):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=nthr) as ex:
+            list(ex.map(fn, items))
+        return time.perf_counter() - t0
+
+    dt = timed(one, heads, threads)
+    # one core, on the first 64 heads over a quarter of the windows
+    one_heads, one_windows = heads[:64], max(1, windows // 4)
+    dt1 = timed(lambda bh: one(bh, one_windows), one_heads, 1)
+    dts = timed(seq, heads, threads)
+    info = host_cpu()
+    return dict(value=round(wl.B * wl.W * windows / dt, 1), unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"one layer, all {len(heads)} heads, {windows} windows of {wl.W} tokens "
-                       f"(plain recurrence + codec, fp64/fp32), {dt:.2f} s wall")
+                       f"(plain recurrence + codec, fp64/fp32), {dt:.2f} s wall on {threads} threads",
+                host=info,
+                single_core={"value": round(len(one_heads) / wl.H * wl.W * one_windows / dt1, 1),
+                             "unit": "tokens/s", "sample": f"{len(one_heads)} heads, {one_windows} windows, "
+                                                           f"{dt1:.2f} s wall on 1 thread",
+                             "all_core_speedup": round((wl.B * wl.W * windows / dt) /
+                                                       (len(one_heads) / wl.H * wl.W * one_windows / dt1), 2)},
+                seq_fp64_recurrence={"value": round(wl.B * wl.W * seq_windows / dts, 1), "unit": "tokens/s",
+                                     "sample": f"all {len(heads)} heads, {seq_windows} windows, no codec, "
+                                               f"{dts:.2f} s wall on {threads} threads"})
 
 
 def main():
@@ -836,12 +949,30 @@ def main():
 
     hsh = kernel_hash()
     traffic = read_traffic(hsh, int(sum(dec_bytes) / ND))
+    frac = dec_gbs / HBM_PEAK_GBS
+    st_bytes = sum(scope_table_decode_bytes(wl, n) for n in range(ND))
+    st_frac = st_bytes / dec_total_s / 1e9 / HBM_PEAK_GBS
+    ceiling = stream_read_ceiling(wl, ND, L)
     roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic if fuse else None,
+            "frac": round(frac, 4), "traffic": traffic if fuse else None,
             "kernel": f"lq_gdn_decode_step (decode_kernel<{wl.dk},{wl.dv},{16 if W <= 16 else 32},"
                       f"{'KDA' if wl.per_key else 'GDN'}>, slots 0..{ND - 1})",
             "avg_launch_us": round(dec_total_s * 1e6 / ND, 3),
-            "bytes_per_launch_avg": int(sum(dec_bytes) / ND)}
+            "duration_source": "each launch's own execution interval: start/stop events bound to the "
+                               "dispatch (hipExtLaunchKernelGGL), the dispatch timestamps rocprofv3's "
+                               f"kernel trace reads; mean over {reps} eager steps x {L} layers after the "
+                               "timed graph replays",
+            "bytes_per_launch_avg": int(sum(dec_bytes) / ND),
+            "bytes_note": "the kernel's own algorithmic bytes: its buffer slot holds k, m, g "
+                          "(4 (dk + dv + a) bytes); the WY buffer of the scope table stores y and u "
+                          "(4 (2 dk + dv + a) bytes), counted under scope_table",
+            "scope_table": {"bytes_per_launch_avg": int(st_bytes / ND),
+                            "achieved": round(st_bytes / dec_total_s / 1e9, 1), "frac": round(st_frac, 4)},
+            "target": {"frac": 0.70, "met": bool(frac >= 0.70), "met_on_scope_table_bytes": bool(st_frac >= 0.70),
+                       "max_avg_launch_us_for_target": round(sum(dec_bytes) / ND / (0.70 * HBM_PEAK_GBS * 1e3), 3)},
+            "stream_read_ceiling": ceiling,
+            "frac_of_one_shot_read": round(ceiling["one_shot"]["avg_launch_us"] / (dec_total_s * 1e6 / ND) *
+                                           (sum(dec_bytes) / ND) / ceiling["bytes_per_launch"], 4)}
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -884,7 +1015,11 @@ def main():
     if not args.no_compare and not args.no_w_sweep:
         res["w_sweep"] = w_sweep(max(4, min(16, args.steps)))
     if not args.no_cpu:
-        threads = min(16, os.cpu_count() or 1)
+        # every CPU this process may use (within a cgroup CPU quota, if one is set)
+        hc = host_cpu()
+        threads = hc["usable_cpus"]
+        if hc["cgroup_cpu_quota"]:
+            threads = max(1, min(threads, int(hc["cgroup_cpu_quota"])))
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_windows, threads)
     else:
         res["cpu_baseline"] = None

@@ -319,7 +319,8 @@ enum {
     LQ_KERNEL_FP32_RECURRENCE = 4,
     LQ_KERNEL_CHECKPOINT = 5,   /* lq_gdn_state_pack / lq_gdn_state_unpack */
     LQ_KERNEL_DECODE_FLUSH = 6, /* lq_gdn_decode_step_flush */
-    LQ_KERNEL_PREFILL = 7       /* lq_gdn_prefill (its quantization: LQ_KERNEL_QUANTIZE) */
+    LQ_KERNEL_PREFILL = 7,      /* lq_gdn_prefill (its quantization: LQ_KERNEL_QUANTIZE) */
+    LQ_KERNEL_MEASURE = 8       /* lq_measure_stream_read */
 };
 
 /* on = 1: drop earlier records and start recording (at most 65536 launches;
@@ -332,6 +333,27 @@ int lq_timing_enable(int32_t on);
  * host arrays, may be NULL if max_records = 0), sets *count = n and drops the
  * records.  Errors: LQ_ERR_NULL, LQ_ERR_HIP. */
 int lq_timing_collect(int32_t max_records, int32_t *family, float *ms, int32_t *count);
+
+/*
+ * Streaming-read reference (measurement support, not part of the method):
+ * what a bare read of a launch's bytes costs on the GPU at hand, the ceiling
+ * for a kernel of the same launch shape.  Reads n_slices slices of
+ * slice_bytes contiguous bytes each from src (n_slices * slice_bytes bytes in
+ * all, non-temporal 16-byte loads) and writes write_bytes bytes per slice to
+ * sink (the XOR of the slice's 16-byte pieces, so no load is dead).
+ *   mode 0: one 256-lane workgroup per slice, every load issued before any
+ *           is used (the shape of a decode launch: one workgroup per head);
+ *   mode 1: `grid` workgroups walking the slices in grid stride.
+ * src, sink: device, 16-byte aligned; slice_bytes a multiple of 16 in
+ * [16, 65536]; write_bytes a multiple of 16 in [0, 4096] (sink may be NULL
+ * when it is 0), sink holds n_slices * write_bytes bytes; n_slices >= 1;
+ * grid >= 1 (mode 1 only).  Timed like the other kernels
+ * (LQ_KERNEL_MEASURE).
+ * Errors: LQ_ERR_NULL, LQ_ERR_ALIGN, LQ_ERR_DIMS (a size out of range or a
+ * bad mode).
+ */
+int lq_measure_stream_read(const void *src, size_t slice_bytes, int32_t n_slices, int32_t mode,
+                           int32_t grid, void *sink, size_t write_bytes, void *stream);
 
 #ifdef __cplusplus
 }

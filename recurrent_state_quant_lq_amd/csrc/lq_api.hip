@@ -309,4 +309,15 @@ const char* lq_status_str(int status) {
 
 int lq_last_hip_error(void) { return g_last_hip; }
 
+int lq_measure_stream_read(const void* src, size_t slice_bytes, int32_t n_slices, int32_t mode, int32_t grid,
+                           void* sink, size_t write_bytes, void* stream) {
+    if (!src || (write_bytes > 0 && !sink)) return LQ_ERR_NULL;
+    if (!aligned16(src) || (sink && !aligned16(sink))) return LQ_ERR_ALIGN;
+    if (slice_bytes < 16 || slice_bytes > 65536 || slice_bytes % 16 != 0) return LQ_ERR_DIMS;
+    if (write_bytes > 4096 || write_bytes % 16 != 0) return LQ_ERR_DIMS;
+    if (n_slices < 1 || (mode != 0 && mode != 1) || (mode == 1 && grid < 1)) return LQ_ERR_DIMS;
+    return finish(lq::launch_stream_read(src, slice_bytes, n_slices, mode, grid, sink, write_bytes,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

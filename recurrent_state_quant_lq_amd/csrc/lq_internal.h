@@ -34,6 +34,10 @@ hipError_t launch_fp32_recurrence(const lq_dims& d, float* h, int T, const void*
                                   const void* k, const void* v, const float* alpha,
                                   const float* beta, void* o, hipStream_t s);
 
+// Streaming-read reference (lq_measure_stream_read); arguments validated.
+hipError_t launch_stream_read(const void* src, size_t slice_bytes, int n_slices, int mode, int grid,
+                              void* sink, size_t write_bytes, hipStream_t s);
+
 // Kernel timing (lq_timing_*): when recording is on, hands out the event
 // pair of the next launch of `family` and returns true.
 bool timing_slot(int family, hipEvent_t* start, hipEvent_t* stop);

@@ -32,10 +32,10 @@ EXPORTS = ("lq_gdn_decode_step", "lq_gdn_window_flush", "lq_gdn_decode_step_ragg
            "lq_buffer_bytes", "lq_status_str", "lq_last_hip_error", "lq_check_dims",
            "lq_timing_enable", "lq_timing_collect", "lq_checkpoint_bytes", "lq_gdn_state_pack",
            "lq_gdn_state_unpack", "lq_gdn_decode_step_flush", "lq_gdn_prefill",
-           "lq_gdn_decode_step_flush_ragged")
+           "lq_gdn_decode_step_flush_ragged", "lq_measure_stream_read")
 LQ_KERNEL_DECODE, LQ_KERNEL_FLUSH, LQ_KERNEL_QUANTIZE, LQ_KERNEL_DEQUANTIZE, \
     LQ_KERNEL_FP32_RECURRENCE, LQ_KERNEL_CHECKPOINT, LQ_KERNEL_DECODE_FLUSH, \
-    LQ_KERNEL_PREFILL = range(8)
+    LQ_KERNEL_PREFILL, LQ_KERNEL_MEASURE = range(9)
 
 
 class lq_dims(ct.Structure):
@@ -98,6 +98,8 @@ def load() -> ct.CDLL:
         L.lq_gdn_state_pack.restype = ct.c_int
         L.lq_gdn_state_unpack.argtypes = [D, P, S, P]
         L.lq_gdn_state_unpack.restype = ct.c_int
+        L.lq_measure_stream_read.argtypes = [P, ct.c_size_t, I, I, I, P, ct.c_size_t, P]
+        L.lq_measure_stream_read.restype = ct.c_int
         L.lq_timing_enable.argtypes = [ct.c_int32]
         L.lq_timing_enable.restype = ct.c_int
         L.lq_timing_collect.argtypes = [ct.c_int32, ct.POINTER(ct.c_int32), ct.POINTER(ct.c_float),
@@ -433,6 +435,20 @@ def lq_buffer_bytes(d: lq_dims) -> int:
 
 def lq_check_dims(d: lq_dims) -> int:
     return int(load().lq_check_dims(ct.byref(d)))
+
+
+def lq_measure_stream_read(src, slice_bytes: int, n_slices: int, mode: int, grid: int = 0,
+                           sink=None, write_bytes: int = 0, stream=None):
+    """Streaming-read reference (measurement only): src and sink device
+    tensors holding n_slices * slice_bytes and n_slices * write_bytes bytes."""
+    if src.numel() * src.element_size() < slice_bytes * n_slices or not src.is_cuda:
+        raise ValueError("src: a device tensor of n_slices * slice_bytes bytes is required")
+    if write_bytes and (sink is None or not sink.is_cuda or
+                        sink.numel() * sink.element_size() < write_bytes * n_slices):
+        raise ValueError("sink: a device tensor of n_slices * write_bytes bytes is required")
+    rc = load().lq_measure_stream_read(_ptr(src), int(slice_bytes), int(n_slices), int(mode), int(grid),
+                                       _ptr(sink), int(write_bytes), _stream(stream))
+    _raise("lq_measure_stream_read", rc)
 
 
 def lq_timing_enable(on: bool = True):

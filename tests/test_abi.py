@@ -257,3 +257,20 @@ def test_state_storage_order(dk):
     assert stored.shape == (2, 3, dk * dk)
     assert np.array_equal(lq.sq_to_rows(stored, dk), rows)
     assert stored[1, 2, off[5, 3]] == rows[1, 2, 5, 3]
+
+
+def test_measure_stream_read_argument_errors():
+    L = lq.load()
+    f = L.lq_measure_stream_read
+    src, sink = 0x100000, 0x200000
+    assert f(None, 1024, 4, 0, 0, sink, 16, None) == lq.LQ_ERR_NULL
+    assert f(src, 1024, 4, 0, 0, None, 16, None) == lq.LQ_ERR_NULL
+    assert f(src + 4, 1024, 4, 0, 0, sink, 16, None) == lq.LQ_ERR_ALIGN
+    assert f(src, 1024, 4, 0, 0, sink + 8, 16, None) == lq.LQ_ERR_ALIGN
+    for bad in (0, 8, 1000, 65552):
+        assert f(src, bad, 4, 0, 0, sink, 16, None) == lq.LQ_ERR_DIMS
+    assert f(src, 1024, 0, 0, 0, sink, 16, None) == lq.LQ_ERR_DIMS
+    assert f(src, 1024, 4, 2, 0, sink, 16, None) == lq.LQ_ERR_DIMS
+    assert f(src, 1024, 4, 1, 0, sink, 16, None) == lq.LQ_ERR_DIMS
+    assert f(src, 1024, 4, 0, 0, sink, 4112, None) == lq.LQ_ERR_DIMS
+    assert f(src, 1024, 4, 0, 0, sink, 24, None) == lq.LQ_ERR_DIMS

@@ -64,3 +64,25 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert r.returncode == 2
     assert "runs on one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_scope_table_figures():
+    """The scope table's per-head decode bytes at d = 128 (GDN): 23,068 +
+    1,540 n (the WY buffer with y and u stored), 69.3 MB per launch over slots
+    0..14 at B=64 H=32; the kernel's own count is 512 n + 512 bytes smaller
+    per head (one projected vector per slot instead of two)."""
+    wl = PRESETS["gdn_batched"]
+    heads = wl.B * wl.H
+    for n in range(wl.W):
+        assert bench.scope_table_decode_bytes(wl, n) == heads * (23068 + 1540 * n)
+        assert bench.scope_table_decode_bytes(wl, n) - bench.decode_bytes(wl, n) == heads * 512 * (n + 1)
+    mean = sum(bench.scope_table_decode_bytes(wl, n) for n in range(wl.W - 1)) / (wl.W - 1)
+    assert round(mean / 1e6, 1) == 69.3
+    rd, wr = bench.decode_read_write_bytes(wl, 5)
+    assert heads * (rd + wr) == bench.decode_bytes(wl, 5)
+
+
+def test_host_cpu_fields():
+    info = bench.host_cpu()
+    assert info["logical_cpus"] >= 1 and 1 <= info["usable_cpus"] <= info["logical_cpus"]
+    assert set(info) == {"model", "logical_cpus", "usable_cpus", "cgroup_cpu_quota"}
