@@ -114,10 +114,10 @@ typedef struct lq_state {
 } lq_state;
 
 /*
- * One decode token for every (b, h).  [abstract]: within a window, outputs
- * come from the fixed low-bit state together with high-precision buffered
- * updates; [forum] technique 2: compensator tokens share the update path of
- * real tokens.
+ * One decode token for every (b, h).  [abstract]: while a window is open the
+ * 8-bit state is left as it is and each output also uses the window's updates,
+ * kept in full precision; [forum] technique 2: compensator tokens are updated
+ * exactly like ordinary tokens.
  *
  * pos = n = number of tokens already buffered in this window (0..W-1).
  * With Hb the window-base state (the dequantized codec, fixed for the

@@ -91,9 +91,9 @@ void lqo_step(int dk, int dv, int per_key, double *H,
 /*
  * Quantize one fp32 state H into (sq, r, s, idx, cv).
  *
- * [forum] techniques 2 and 3, [abstract], [news ¶4]: the largest outliers
- * are kept as a few high-precision compensator tokens, the remaining residual
- * is smoothed, then the state is quantized to 8 bits.  The pages give no
+ * [forum] techniques 2 and 3, [abstract], [news ¶4]: a few of the state's
+ * biggest outlier entries stay in high precision as compensator tokens, what
+ * is left is smoothed, and that is rounded to 8 bits.  The pages give no
  * formulas; the steps below are this codec's definition:
  *
  *   Q1  m_i  = max_j |H_ij|                         (row magnitude)
@@ -206,9 +206,10 @@ void lqo_dequantize(int dk, int dv, int C, const int8_t *sq, const float *r,
 /* In-window buffered updates, WY form (fp64)                               */
 /* ------------------------------------------------------------------------ */
 /*
- * [abstract]: within a window the outputs are computed from the fixed
- * low-bit state together with high-precision buffered updates; [news ¶3]: no
- * update is skipped.  Writing the state after slot n of a window as
+ * [abstract]: while a window is open the 8-bit state stays as it is and the
+ * outputs also use the window's updates, held in full precision; [news ¶3]:
+ * every update is applied, only the rounding waits.  Writing the state after
+ * slot n of a window as
  *
  *     H_n = A_n Hb + U_n            (Hb = window-base state)
  *     A_n = Gamma_n - sum_{i<=n} (E_{n,i} o k_i) y_i^T

@@ -1,10 +1,11 @@
 // decode.hip -- one decode token over the int8 state (gfx950).
 //
-// LeapQuant abstract (HFEPX paper page, "Abstract"): inside a window the
-// output is computed from the fixed low-bit state plus high-precision
-// buffered updates; the compensator tokens share the update path of real
-// tokens.  News article ("A linear-attention method cuts state ...",
-// paragraph 3): no update is skipped.
+// LeapQuant abstract (HFEPX paper page, "Abstract"): while a window is open
+// the 8-bit state does not change, and each token's output combines it with
+// the window's updates kept in full precision; compensator tokens go through
+// the same update as ordinary tokens.  News article ("A linear-attention
+// method cuts state ...", paragraph 3): every update is applied, only the
+// rounding is deferred.
 //
 // Buffer form.  With the window-base state Hb (fixed for the window) and the
 // window-local log-decays g, slot i of the buffer holds k_i, g_i and

@@ -2,11 +2,11 @@
 // smooth, requantize (gfx950).  Also the standalone codec kernels.
 //
 // News article ("A linear-attention method cuts state ...", paragraph 3):
-// the state is reconstructed and quantized once at the window boundary.
-// Forum mirror ("Abstract (translated)", techniques 2 and 3) and paragraph 4
-// of the news article: the largest outliers are kept as a few
-// high-precision compensator tokens and the residual is smoothed before
-// quantization.
+// one rebuild and one rounding of the state per window, at its end.  Forum
+// mirror ("Abstract (translated)", techniques 2 and 3) and paragraph 4 of the
+// news article: the few biggest outlier entries of the state stay in high
+// precision as compensator tokens, and what is left is smoothed, then
+// rounded.
 //
 // Reconstruction from the window-base state Hb and N buffered slots
 // (k_i, g_i, m_i; m_i = u_i - Hb^T y_i, see decode.hip):

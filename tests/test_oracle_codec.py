@@ -161,8 +161,8 @@ def test_permutation_equivariance(orc):
 
 
 def test_compensators_and_smoothing_reduce_error(orc):
-    """The pages' claims: keeping the largest outliers in high precision and
-    smoothing the residual each lower the quantization error (forum mirror,
+    """The pages' claims: holding the biggest outlier entries aside in high
+    precision, and smoothing what is left, each lower the quantization error (forum mirror,
     'Abstract (translated)', techniques 2 and 3)."""
     rng = np.random.default_rng(80)
     H = _rand(rng, 128, 128, outlier_rows=(1, 20, 64, 90), outlier_cols=(3, 50))
