@@ -116,7 +116,8 @@ void decode_kernel(DecodeArgs a) {
     __shared__ __align__(16) float s_a[WM];
     __shared__ __align__(16) float s_cqk[2][CMAX];            // e^{g_n}[idx_c] q[idx_c], ... k[idx_c]
     __shared__ __align__(16) int8_t s_dig[6][KS * 64];       // digits of q~'' (0..2), k~'' (3..5)
-    __shared__ __align__(16) float s_msc[2][KS];
+    __shared__ __align__(16) float s_msc[2];                 // digit scales of q~'', k~''
+
     __shared__ __align__(16) float s_gem[2][DV];             // sq^T q~'', sq^T k~''
     // dwords 0..7: compensator rows; 8: beta; 9: alpha (scalar decay); 10: g_{n-1} (scalar decay)
     __shared__ __align__(16) int s_misc[16];
@@ -258,9 +259,22 @@ void decode_kernel(DecodeArgs a) {
     }
     if (w < KS) {
         // wave w's 64 lanes are one 64-channel block (lanes past dk hold zeros):
-        // scale M = max |x|, three int8 digits per channel
-        const float mq = __uint_as_float(wave_umax(__float_as_uint(xq) & 0x7fffffffu));
-        const float mk = __uint_as_float(wave_umax(__float_as_uint(xk) & 0x7fffffffu));
+        // one scale M = max |x| over all dk channels, three int8 digits per
+        // channel.  With two blocks each lane also forms the entry of channel
+        // t ^ 64 from LDS, so both waves find the same maximum without a barrier,
+        // and the int8 products of the two K steps can add up in int32.
+        uint32_t aq = __float_as_uint(xq) & 0x7fffffffu, ak = __float_as_uint(xk) & 0x7fffffffu;
+        if constexpr (KS == 2) {
+            const int p = t ^ 64;
+            float ep;
+            if constexpr (KDA) ep = __expf((n > 0 ? s_vec[D::SG * DK + p] : 0.0f) + __logf(s_vec[D::SA * DK + p]));
+            else ep = __expf(gn_s);
+            const float rp = s_vec[D::SR * DK + p];
+            aq = umax(aq, __float_as_uint(rp * (ep * seg_ld<TI>(s_vec + D::SQ * DK, p))) & 0x7fffffffu);
+            ak = umax(ak, __float_as_uint(rp * (ep * seg_ld<TI>(s_vec + D::SK * DK, p))) & 0x7fffffffu);
+        }
+        const float mq = __uint_as_float(wave_umax(aq));
+        const float mk = __uint_as_float(wave_umax(ak));
         uint32_t d0, d1, d2;
         digits3_words(xq, mq > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(mq) : 0.0f, d0, d1, d2);
         s_dig[0][t] = (int8_t)d0;
@@ -270,9 +284,9 @@ void decode_kernel(DecodeArgs a) {
         s_dig[3][t] = (int8_t)d0;
         s_dig[4][t] = (int8_t)d1;
         s_dig[5][t] = (int8_t)d2;
-        if (lane == 0) {
-            s_msc[0][w] = mq * (1.0f / 127.0f);
-            s_msc[1][w] = mk * (1.0f / 127.0f);
+        if (w == 0 && lane == 0) {
+            s_msc[0] = mq * (1.0f / 127.0f);
+            s_msc[1] = mk * (1.0f / 127.0f);
         }
     }
     {
@@ -327,39 +341,34 @@ void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
 
-    // ---- B. int8 MFMA: sq^T of both digit sets for this wave's column tiles; buffer sums -----
+    // ---- B. int8 MFMA: both digit sets times sq for this wave's column tiles; buffer sums ------
+    // A = the digits (rows 0..2: q~'', rows 4..6: k~'', other rows zero), B = the state
+    // bytes (a lane's 16 bytes are 16 channels of value column l % 16: the same bytes it
+    // would give as an A operand, so the loaded registers serve as they are).  Lane l
+    // then holds digit rows 4 (l/16) .. +3 of value column l % 16: lane group 0 the
+    // three digit sums of q~'', lane group 1 those of k~''.
     {
-        // B columns 0..2: digits of q~'', 3..5: digits of k~'', rest zero
-        const int dgt = lane % 16;
-        const int vec = dgt >= 3 ? 1 : 0;
-        const int dd = dgt - 3 * vec;
-        const float wd = dgt >= 6 ? 0.0f : dd == 0 ? 1.0f : dd == 1 ? kDigitW1 : kDigitW2;
-        float fk[KS];
-        v4i bop[KS];
+        const int li = lane % 16, lg = lane / 16;
+        const int drow = li < 3 ? li : (li >= 4 && li < 7) ? li - 1 : -1;
+        v4i aop[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            fk[ks] = wd * s_msc[vec][ks];
-            bop[ks] = dgt < 6 ? *reinterpret_cast<const v4i*>(&s_dig[dgt][ks * 64 + 16 * (lane / 16)])
-                              : v4i{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            aop[ks] = drow >= 0 ? *reinterpret_cast<const v4i*>(&s_dig[drow][ks * 64 + 16 * lg])
+                                : v4i{0, 0, 0, 0};
+        const float sc = lg < 2 ? s_msc[lg] : 0.0f;
 #pragma unroll
         for (int tw = 0; tw < TPW; ++tw) {
             const int tile = w * TPW + tw;
             if (tile >= NTILE) break;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            // |digit| <= 127 and |byte| <= 127 over at most 128 channels: the
+            // int32 sums stay below 2^21
+            v4i dv4 = v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const v4i dv4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(sqa[tw][ks], bop[ks],
-                                                                      v4i{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] += (float)dv4[v] * fk[ks];
-            }
-            // the digit-0 lanes of each vector (0 and 3) gather digits 1 and 2
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] += dpp<DPP_SHL1>(acc[v]) + dpp<DPP_SHL2>(acc[v]);
-            if (dd == 0 && dgt < 6)
-                *reinterpret_cast<float4*>(&s_gem[vec][tile * 16 + 4 * (lane / 16)]) =
-                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+            for (int ks = 0; ks < KS; ++ks)
+                dv4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[ks], sqa[tw][ks], dv4, 0, 0, 0);
+            const float x = __builtin_fmaf((float)dv4[2], kDigitW2, __builtin_fmaf((float)dv4[1], kDigitW1,
+                                                                                    (float)dv4[0]));
+            if (lg < 2) s_gem[lg][tile * 16 + li] = x * sc;
         }
     }
     float sr = 0.0f, sa = 0.0f;
