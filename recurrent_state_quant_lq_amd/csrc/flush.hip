@@ -126,6 +126,36 @@ __device__ __forceinline__ uint32_t rows_umax4(uint32_t a, uint32_t b, uint32_t 
     return umax(s2[0], s2[1]);
 }
 
+// Maxima over the 16 lanes of a lane group of N values per lane (non-negative
+// floats as bit patterns), by halving exchanges: at step S the lanes whose lane
+// bit 8 >> S is set keep the second half of their values and pass the first half
+// to their partner (row mirror, then half mirror, then quad swaps), the others
+// keep the first half; each keeps the maximum of its value and the partner's.
+// Once one value is left the remaining steps are plain maxima.  The result at
+// lane li is the maximum of value number sum_S bit_S(li) * (N >> (S + 1)), i.e.
+// value k sits at the lanes li = k * (16 / N) (+ any of the lower bits).
+template <int N, int S = 0>
+__device__ __forceinline__ uint32_t halve_umax(const uint32_t* x, int li) {
+    constexpr int ctrl = S == 0 ? DPP_MIRROR : S == 1 ? DPP_HALF_MIRROR : S == 2 ? DPP_XOR2 : DPP_XOR1;
+    if constexpr (S == 4) {
+        static_assert(N == 1, "16 lanes reduce at most 16 values");
+        return x[0];
+    } else if constexpr (N == 1) {
+        const uint32_t v = umax(x[0], (uint32_t)dpp_i<ctrl>((int)x[0]));
+        return halve_umax<1, S + 1>(&v, li);
+    } else {
+        const bool hi = (li & (8 >> S)) != 0;
+        uint32_t y[N / 2];
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            const uint32_t keep = hi ? x[j + N / 2] : x[j];
+            const uint32_t send = hi ? x[j] : x[j + N / 2];
+            y[j] = umax(keep, (uint32_t)dpp_i<ctrl>((int)send));
+        }
+        return halve_umax<N / 2, S + 1>(y, li);
+    }
+}
+
 // LDS used by the codec stage.
 template <int DK, int DV, int NW>
 struct CodecLds {
@@ -160,9 +190,11 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                 store_cols<CT>(h_out + (size_t)(row0 + rb * 4 + v) * DV + li, x);
             }
     }
-    // row magnitudes
+    // row magnitudes (a lane's maximum starts at +0 and takes only |H|, so its
+    // bit pattern orders like the value); lane li ends with row li / (16 / RPL)
+    constexpr int LPR = 16 / RPL;             // lanes holding each row's result
     {
-        float m[RPL];
+        uint32_t m[RPL];
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -170,9 +202,10 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                 float mx = 0.0f;
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) mx = fmaxf(mx, fabsf(H[rb][ct][v]));
-                m[rb * 4 + v] = group_absmax<16>(mx);
+                m[rb * 4 + v] = __float_as_uint(mx);
             }
-        if (li == 0) store_floats<RPL>(&L.m[row0], m);
+        const uint32_t mr = halve_umax<RPL>(m, li);
+        if (li % LPR == 0) L.m[row0 + li / LPR] = __uint_as_float(mr);
     }
     lds_barrier();
 
@@ -289,7 +322,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
     // smoothing and row maxima
     float inv[CT];
     load_cols<CT>(&L.sinv[li], inv);
-    float rho[RPL];
+    uint32_t rho[RPL];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -300,19 +333,17 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
                 H[rb][ct][v] = H[rb][ct][v] * inv[ct];
                 mx = fmaxf(mx, fabsf(H[rb][ct][v]));
             }
-            rho[rb * 4 + v] = group_absmax<16>(mx);
+            rho[rb * 4 + v] = __float_as_uint(mx);
         }
-    // row scales: lane li of a row group divides for row row0 + li % RPL,
-    // the 16 lanes then share the RPL multipliers
+    // row scales: lane li of a row group holds rho of row row0 + li / LPR and
+    // divides for it; the 16 lanes then share the RPL multipliers
     float lam[RPL];
     {
-        float my = rho[0];
-#pragma unroll
-        for (int k = 1; k < RPL; ++k) my = (li % RPL == k) ? rho[k] : my;
+        const float my = __uint_as_float(halve_umax<RPL>(rho, li));
         const bool live = my >= kTiny;
         const float lmy = live ? 127.0f / my : 0.0f;
-        if (li < RPL) st_nt(out.r + row0 + li, live ? my / 127.0f : 0.0f);
-        row_bcast_all<RPL>(lmy, lam);
+        if (li % LPR == 0) st_nt(out.r + row0 + li / LPR, live ? my / 127.0f : 0.0f);
+        row_bcast_all<RPL, LPR>(lmy, lam);
     }
     // rounding through the offset form; one column's RPL bytes per store,
     // 512 contiguous bytes per tile and wave.
@@ -604,11 +635,13 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NPAD / 4; ++ks) {
         if (4 * ks < NM) {
-            const bool live = 4 * ks + lg < NM;
             float bm[CT];
             load_cols<CT>(&s_M[(4 * ks + lg) * DV + li], bm);
+            if (4 * ks + 4 > NM) {                 // uniform: the step runs past slot NM - 1
+                const bool live = 4 * ks + lg < NM;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) bm[ct] = live ? bm[ct] : 0.0f;
+                for (int ct = 0; ct < CT; ++ct) bm[ct] = live ? bm[ct] : 0.0f;
+            }
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll

@@ -101,11 +101,11 @@ constexpr int DPP_SHL1 = 0x101;         // lane i <- lane i+1 within 16
 constexpr int DPP_SHL2 = 0x102;         // lane i <- lane i+2 within 16
 constexpr int DPP_ROW_BCAST = 0x150;    // + k: every lane of a 16-lane row <- lane k of that row
 
-// x of lane k of this lane's 16-lane row, for k = 0..N-1, into out[k].
-template <int N, int K = 0>
+// x of lane k * STRIDE of this lane's 16-lane row, for k = 0..N-1, into out[k].
+template <int N, int STRIDE = 1, int K = 0>
 __device__ __forceinline__ void row_bcast_all(float x, float* out) {
-    out[K] = dpp<DPP_ROW_BCAST + K>(x);
-    if constexpr (K + 1 < N) row_bcast_all<N, K + 1>(x, out);
+    out[K] = dpp<DPP_ROW_BCAST + K * STRIDE>(x);
+    if constexpr (K + 1 < N) row_bcast_all<N, STRIDE, K + 1>(x, out);
 }
 
 __device__ __forceinline__ float swz_xor16(float x) {
