@@ -399,10 +399,320 @@ void decode_kernel(DecodeArgs a) {
     }
 }
 
+// dk = dv = 128: the same step with the waves split by role, so that the token
+// work does not wait for the state bytes.  Waves 0-1 (token waves, lane t =
+// channel t = value column t) copy the per-head vectors, compensator rows and
+// buffered keys to LDS and load the buffered m columns; waves 2-3 (state waves)
+// load the int8 state, wave w the column tiles 4 (w - 2) .. + 3.  A wave's
+// counter of outstanding loads covers only its own loads, so the token waves'
+// first barrier waits for the small vectors only, and the state waves pass it
+// with their state loads still in flight.  Phase A (digits, slot dot products,
+// compensator coefficients) and the buffer sums then run while the state
+// streams in; after the state lands only the state waves' MFMAs and the token
+// waves' output step remain.  Each role is its own branch (the wave index is
+// uniform), so the register allocator never holds the state registers and the
+// m columns at once.
+template <int WM, bool KDA, int NB, typename TI>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(Dec<128, 128, WM, KDA>::WPE, Dec<128, 128, WM, KDA>::WPE)))
+void decode_split_kernel(DecodeArgs a) {
+    constexpr int DK = 128, DV = 128;
+    using D = Dec<DK, DV, WM, KDA>;
+    constexpr int TPS = D::TPS, CH = D::CH, SPR = D::SPR, ROUNDS = D::ROUNDS, SEGL = D::SEGL;
+    constexpr int GD = D::GD;
+    constexpr int TPSW = 4;                  // column tiles per state wave
+    static_assert(D::NT == 256 && D::KS == 2 && D::NTILE == 2 * TPSW, "two token and two state waves");
+
+    __shared__ __align__(16) float s_vec[D::NSEG * DK];
+    __shared__ __align__(16) float s_rr[WM];
+    __shared__ __align__(16) float s_a[WM];
+    __shared__ __align__(16) float s_cqk[2][CMAX];            // e^{g_n}[idx_c] q[idx_c], ... k[idx_c]
+    __shared__ __align__(16) int8_t s_dig[6][128];           // digits of q~'' (0..2), k~'' (3..5)
+    __shared__ __align__(16) float s_msc[2];                 // digit scales of q~'', k~''
+    __shared__ __align__(16) float s_gem[2][DV];             // sq^T q~'', sq^T k~''
+    // dwords 0..7: compensator rows; 8: beta; 9: alpha (scalar decay); 10: g_{n-1} (scalar decay)
+    __shared__ __align__(16) int s_misc[16];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const size_t head = blockIdx.x;
+    const int W = a.W, C = a.C;
+    int n = NB;
+    if constexpr (NB < 0) {
+        n = a.pos_dev ? a.pos_dev[head / (unsigned)a.H] : a.pos;
+        if (n < 0 || n >= W) return;              // a row outside its window: untouched
+    }
+    const float* __restrict__ bkr = a.bk + head * (size_t)W * DK;
+    const float* __restrict__ bmr = a.bm + head * (size_t)W * DV;
+    const float* __restrict__ bgr = a.bg + head * (size_t)W * GD;
+
+    // slot groups of the dot products (all 256 lanes take part)
+    const int slot0 = t / TPS;
+    const int c0 = (t % TPS) * CH;
+
+    // Dot products rr_i = <k, E_i o k_i>, a_i = <q, E_i o k_i> of this lane's slot
+    // group, a_n = <q, k>; results to s_rr, s_a.
+    auto dot_products = [&](const float (&gs)[ROUNDS][KDA ? CH : 1], const float (&gslot)[ROUNDS], float gn_s) {
+        float kq[CH], kk[CH];
+        seg_ld_n<CH, TI>(s_vec + D::SQ * DK, c0, kq);
+        seg_ld_n<CH, TI>(s_vec + D::SK * DK, c0, kk);
+        float gnc[KDA ? CH : 1];
+        if constexpr (KDA) {
+            float al[CH], gp[CH];
+            load_floats<CH>(s_vec + D::SA * DK + c0, al);
+            if (n > 0) load_floats<CH>(s_vec + D::SG * DK + c0, gp);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) gnc[c] = (n > 0 ? gp[c] : 0.0f) + __logf(al[c]);
+        }
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+            const int slot = slot0 + rd * SPR;
+            if (rd * SPR > n) break;                      // uniform: no slot <= n left
+            float rr = 0.0f, aa = 0.0f;
+            if (slot < n) {
+                float ks[CH];
+                load_floats<CH>(s_vec + (D::SKB + slot) * DK + c0, ks);
+                if constexpr (KDA) {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        const float x = ks[c] * __expf(gnc[c] - gs[rd][c]);
+                        rr += kk[c] * x;
+                        aa += kq[c] * x;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        rr += kk[c] * ks[c];
+                        aa += kq[c] * ks[c];
+                    }
+                    const float e = __expf(gn_s - gslot[rd]);
+                    rr *= e;
+                    aa *= e;
+                }
+            } else if (slot == n) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) aa += kq[c] * kk[c];
+            }
+            rr = group_sum<TPS>(rr);
+            aa = group_sum<TPS>(aa);
+            if ((t % TPS) == 0 && slot <= n) {
+                s_rr[slot] = rr;
+                s_a[slot] = aa;
+            }
+        }
+    };
+    // decay rows of this lane's slot groups (slot index clamped into the buffer)
+    auto load_decays = [&](float (&gs)[ROUNDS][KDA ? CH : 1], float (&gslot)[ROUNDS]) {
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+            const int slot = min(slot0 + rd * SPR, W - 1);
+            if constexpr (KDA) load_floats<CH>(bgr + (size_t)slot * DK + c0, gs[rd]);
+            else gslot[rd] = bgr[slot];
+        }
+    };
+
+    if (w < 2) {
+        // ================= token waves: lane t is channel t and value column t =================
+        {
+            // q k v r s [alpha gprev]: chunk c of segment c / SEGL (bf16 q, k, v fill the
+            // first half of their segments)
+            constexpr int NVS = D::SCV;
+#pragma unroll
+            for (int base = 0; base < NVS * SEGL; base += 128) {
+                const int c = base + t;
+                const int sg = c / SEGL, off = 4 * (c % SEGL);
+                const bool tin = sizeof(TI) == 4 || 2 * off < DK;
+                const float* src = nullptr;
+                switch (sg) {
+                    case D::SQ: if (tin) src = reinterpret_cast<const float*>(static_cast<const TI*>(a.q) + head * DK); break;
+                    case D::SK: if (tin) src = reinterpret_cast<const float*>(static_cast<const TI*>(a.k) + head * DK); break;
+                    case D::SV: if (tin) src = reinterpret_cast<const float*>(static_cast<const TI*>(a.v) + head * DV); break;
+                    case D::SR: src = a.r + head * DK; break;
+                    case D::SS: src = a.s + head * DV; break;
+                    default:
+                        if constexpr (KDA) {
+                            if (sg == D::SA) src = a.alpha + head * DK;
+                            else if (sg == D::SG && n > 0) src = bgr + (size_t)(n - 1) * DK;
+                        }
+                }
+                if (c < NVS * SEGL && src) lds_dma16(src + off, s_vec + 4 * (base + 64 * w));
+            }
+            // compensator rows: C*DV contiguous floats
+            const int ccv = C * DV / 4;
+            for (int base = 0; base < ccv; base += 128) {
+                const int c = base + t;
+                if (c < ccv) lds_dma16(a.cv + head * (size_t)C * DV + 4 * c, s_vec + D::SCV * DK + 4 * (base + 64 * w));
+            }
+            // buffered keys k_0 .. k_{n-1}: n*DK contiguous floats
+            const int ckb = n * DK / 4;
+            for (int base = 0; base < ckb; base += 128) {
+                const int c = base + t;
+                if (c < ckb) lds_dma16(bkr + 4 * c, s_vec + D::SKB * DK + 4 * (base + 64 * w));
+            }
+            if (w == 0) {
+                const void* src4 = nullptr;
+                if (lane < C) src4 = a.idx + head * C + lane;
+                else if (lane == 8) src4 = a.beta + head;
+                else if (!KDA && lane == 9) src4 = a.alpha + head;
+                else if (!KDA && lane == 10 && n > 0) src4 = bgr + (n - 1);
+                if (src4) lds_dma4(src4, s_misc);
+            }
+        }
+        float gs[ROUNDS][KDA ? CH : 1], gslot[ROUNDS];
+        load_decays(gs, gslot);
+        float mcol[WM > 1 ? WM - 1 : 1];          // m_i[t], i < n
+#pragma unroll
+        for (int i = 0; i < WM - 1; ++i)
+            if (i < n) mcol[i] = ld_nt(bmr + (size_t)i * DV + t);
+        all_loads_barrier();                                                        // (1)
+
+        const float beta = __int_as_float(s_misc[8]);
+        float gn_s = 0.0f;
+        if constexpr (!KDA) gn_s = (n > 0 ? __int_as_float(s_misc[10]) : 0.0f) + __logf(__int_as_float(s_misc[9]));
+        // ---- A. digits of r o e^g o q and r o e^g o k; slot n's key and decay ------------------
+        {
+            const float qc = seg_ld<TI>(s_vec + D::SQ * DK, t), kc = seg_ld<TI>(s_vec + D::SK * DK, t);
+            const float rc = s_vec[D::SR * DK + t];
+            float gn;
+            if constexpr (KDA) gn = (n > 0 ? s_vec[D::SG * DK + t] : 0.0f) + __logf(s_vec[D::SA * DK + t]);
+            else gn = gn_s;
+            const float en = __expf(gn);
+            const float xq = rc * (en * qc), xk = rc * (en * kc);
+            st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, kc);
+            if constexpr (KDA) st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, gn);
+            else if (t == 0) st_nt(a.bg + head * (size_t)W + n, gn);
+            // one scale M = max |x| over all 128 channels (each lane also forms the
+            // entry of channel t ^ 64 from LDS), three int8 digits per channel
+            uint32_t aq = __float_as_uint(xq) & 0x7fffffffu, ak = __float_as_uint(xk) & 0x7fffffffu;
+            {
+                const int p = t ^ 64;
+                float ep;
+                if constexpr (KDA) ep = __expf((n > 0 ? s_vec[D::SG * DK + p] : 0.0f) + __logf(s_vec[D::SA * DK + p]));
+                else ep = en;
+                const float rp = s_vec[D::SR * DK + p];
+                aq = umax(aq, __float_as_uint(rp * (ep * seg_ld<TI>(s_vec + D::SQ * DK, p))) & 0x7fffffffu);
+                ak = umax(ak, __float_as_uint(rp * (ep * seg_ld<TI>(s_vec + D::SK * DK, p))) & 0x7fffffffu);
+            }
+            const float mq = __uint_as_float(wave_umax(aq));
+            const float mk = __uint_as_float(wave_umax(ak));
+            uint32_t d0, d1, d2;
+            digits3_words(xq, mq > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(mq) : 0.0f, d0, d1, d2);
+            s_dig[0][t] = (int8_t)d0;
+            s_dig[1][t] = (int8_t)d1;
+            s_dig[2][t] = (int8_t)d2;
+            digits3_words(xk, mk > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(mk) : 0.0f, d0, d1, d2);
+            s_dig[3][t] = (int8_t)d0;
+            s_dig[4][t] = (int8_t)d1;
+            s_dig[5][t] = (int8_t)d2;
+            if (w == 0 && lane == 0) {
+                s_msc[0] = mq * (1.0f / 127.0f);
+                s_msc[1] = mk * (1.0f / 127.0f);
+            }
+        }
+        dot_products(gs, gslot, gn_s);
+        lds_barrier();                                                              // (2)
+        // ---- buffer sums --------------------------------------------------------------------
+        float sr = 0.0f, sa = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WM - 1; ++i)
+            if (i < n) {
+                sr += s_rr[i] * mcol[i];
+                sa += s_a[i] * mcol[i];
+            }
+        lds_barrier();                                                              // (3)
+        // ---- C. m_n and the output (value column t) -----------------------------------------
+        const int j = t;
+        const float sj = s_vec[D::SS * DK + j];
+        float hq = sj * s_gem[0][j], hk = sj * s_gem[1][j];
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c)
+            if (c < C) {
+                const float cvj = s_vec[(D::SCV + c) * DK + j];
+                hq += s_cqk[0][c] * cvj;
+                hk += s_cqk[1][c] * cvj;
+            }
+        const float mn = beta * (seg_ld<TI>(s_vec + D::SV * DK, j) - hk - sr);
+        st_nt(a.bm + head * (size_t)W * DV + (size_t)n * DV + j, mn);
+        tok_st<TI>(a.o, head * DV + j, hq + sa + s_a[n] * mn);
+    } else {
+        // ================= state waves ============================================================
+        float gs[ROUNDS][KDA ? CH : 1], gslot[ROUNDS];
+        load_decays(gs, gslot);
+        lds_barrier();                                                              // (1)
+        // The int8 state, requested once this head's token data has landed: every
+        // workgroup's token data then reaches the queue ahead of the state streams, so
+        // the token work of even the last heads is done before their state arrives.
+        // Tile T of this wave, K step ks; lane l: value column T*16 + l%16, channels
+        // ks*64 + 16*(l/16) .. +15 (1 KB contiguous per load and wave).
+        __builtin_amdgcn_sched_barrier(0);
+        v4i sqa[TPSW][2];
+        {
+            const int8_t* sq = a.sq + head * (DK * DV);
+#pragma unroll
+            for (int tw = 0; tw < TPSW; ++tw)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    sqa[tw][ks] = ld_nt(reinterpret_cast<const v4i*>(
+                        sq + sq_off<DK>(ks * 64 + 16 * (lane / 16), ((w - 2) * TPSW + tw) * 16 + lane % 16)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float gn_s = 0.0f;
+        if constexpr (!KDA) gn_s = (n > 0 ? __int_as_float(s_misc[10]) : 0.0f) + __logf(__int_as_float(s_misc[9]));
+        // the compensator rows' coefficients, by the last CMAX lanes: the decayed query
+        // and key entries at the compensator rows (the expression the channel lane of
+        // row idx_c evaluates)
+        if (t >= D::NT - CMAX && t - (D::NT - CMAX) < C) {
+            const int c = t - (D::NT - CMAX);
+            const int ic = s_misc[c] & (DK - 1);
+            float e;
+            if constexpr (KDA) e = __expf((n > 0 ? s_vec[D::SG * DK + ic] : 0.0f) + __logf(s_vec[D::SA * DK + ic]));
+            else e = __expf(gn_s);
+            s_cqk[0][c] = e * seg_ld<TI>(s_vec + D::SQ * DK, ic);
+            s_cqk[1][c] = e * seg_ld<TI>(s_vec + D::SK * DK, ic);
+        }
+        dot_products(gs, gslot, gn_s);
+        lds_barrier();                                                              // (2)
+        // ---- B. int8 MFMA: both digit sets times this wave's state tiles --------------------
+        // A = the digits (rows 0..2: q~'', rows 4..6: k~'', other rows zero), B = the state
+        // bytes as loaded; lane group 0 ends with the digit sums of q~'' for value column
+        // l % 16, lane group 1 those of k~''.
+        {
+            const int li = lane % 16, lg = lane / 16;
+            const int drow = li < 3 ? li : (li >= 4 && li < 7) ? li - 1 : -1;
+            v4i aop[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                aop[ks] = drow >= 0 ? *reinterpret_cast<const v4i*>(&s_dig[drow][ks * 64 + 16 * lg])
+                                    : v4i{0, 0, 0, 0};
+            const float sc = lg < 2 ? s_msc[lg] : 0.0f;
+#pragma unroll
+            for (int tw = 0; tw < TPSW; ++tw) {
+                // |digit| <= 127 and |byte| <= 127 over 128 channels: int32 sums below 2^21
+                v4i dv4 = v4i{0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    dv4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[ks], sqa[tw][ks], dv4, 0, 0, 0);
+                const float x = __builtin_fmaf((float)dv4[2], kDigitW2,
+                                               __builtin_fmaf((float)dv4[1], kDigitW1, (float)dv4[0]));
+                if (lg < 2) s_gem[lg][((w - 2) * TPSW + tw) * 16 + li] = x * sc;
+            }
+        }
+        lds_barrier();                                                              // (3)
+    }
+}
+
 template <int DK, int WM, bool KDA, int NB>
 hipError_t launch_nb(const lq_dims& d, const DecodeArgs& args, hipStream_t s) {
     constexpr int NT = Dec<DK, DK, WM, KDA>::NT;
     const unsigned grid = (unsigned)d.B * (unsigned)d.H;
+    if constexpr (DK == 128 && WM <= 16) {      // (with 32 slots the m columns need the registers)
+        if (d.io_dtype == LQ_IO_BF16)
+            return launch_kernel(LQ_KERNEL_DECODE, decode_split_kernel<WM, KDA, NB, uint16_t>, dim3(grid), dim3(NT),
+                                 s, args);
+        return launch_kernel(LQ_KERNEL_DECODE, decode_split_kernel<WM, KDA, NB, float>, dim3(grid), dim3(NT), s,
+                             args);
+    }
     if (d.io_dtype == LQ_IO_BF16)
         return launch_kernel(LQ_KERNEL_DECODE, decode_kernel<DK, DK, WM, KDA, NB, uint16_t>, dim3(grid), dim3(NT),
                              s, args);

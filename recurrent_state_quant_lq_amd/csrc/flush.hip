@@ -354,7 +354,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
         uint32_t z[RPL];
 #pragma unroll
         for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
-        int8_t* dst = out.sq + sq_off<DK>(row0, 16 * ct + li);
+        int8_t* dst = out.sq + sq_off<DK>(row0, li) + ct * sq_tile_stride<DK>();
         if constexpr (RPL == 8)
             *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low4(z[0], z[1], z[2], z[3]),
                                                         pack_low4(z[4], z[5], z[6], z[7]));
@@ -535,7 +535,7 @@ void flush_kernel(FlushArgs a) {
     typename RBy::T hb[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-        hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + sq_off<DK>(row0, 16 * ct + li));
+        hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + sq_off<DK>(row0, li) + ct * sq_tile_stride<DK>());
     all_loads_barrier();
 
     // log-decay of the last slot, g_{N-1}[row]: from the buffer, or (DEC) the

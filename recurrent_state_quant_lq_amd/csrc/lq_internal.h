@@ -104,7 +104,8 @@ constexpr int DPP_ROW_BCAST = 0x150;    // + k: every lane of a 16-lane row <- l
 // x of lane k * STRIDE of this lane's 16-lane row, for k = 0..N-1, into out[k].
 template <int N, int STRIDE = 1, int K = 0>
 __device__ __forceinline__ void row_bcast_all(float x, float* out) {
-    out[K] = dpp<DPP_ROW_BCAST + K * STRIDE>(x);
+    // every lane has a source lane here, so no fallback value is needed
+    out[K] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), DPP_ROW_BCAST + K * STRIDE, 0xf, 0xf, false));
     if constexpr (K + 1 < N) row_bcast_all<N, STRIDE, K + 1>(x, out);
 }
 
@@ -376,12 +377,23 @@ __device__ __forceinline__ void digits3_words(float x, float inv, uint32_t& w0, 
 // within it, the 16-byte piece lg*16 + j%16 holds channels ks*64 + lg*16 ..
 // +15 of column j, lg = (i%64)/16.  Runs of up to 16 consecutive channels of
 // one column (aligned to their length) are contiguous.
+// Bytes between the same (row, column-in-tile) of consecutive 16-column tiles:
+// sq_off(i, 16 t + c) = sq_off(i, c) + t * sq_tile_stride<DK>().
+template <int DK>
+__host__ __device__ constexpr uint32_t sq_tile_stride() {
+    return (uint32_t)(((DK + 63) / 64) * (DK / 16 < 4 ? DK / 16 : 4) * 256);
+}
+
 template <int DK>
 __host__ __device__ constexpr uint32_t sq_off(int i, int j) {
     constexpr int G = DK / 16 < 4 ? DK / 16 : 4;
     constexpr int KS = (DK + 63) / 64;
     return (uint32_t)(((((j >> 4) * KS + (i >> 6)) * G + ((i & 63) >> 4)) * 16 + (j & 15)) * 16 + (i & 15));
 }
+
+static_assert(sq_off<128>(77, 16 * 5 + 9) == sq_off<128>(77, 9) + 5 * sq_tile_stride<128>(), "tile stride");
+static_assert(sq_off<64>(33, 16 * 3 + 2) == sq_off<64>(33, 2) + 3 * sq_tile_stride<64>(), "tile stride");
+static_assert(sq_off<16>(11, 4) == sq_off<16>(11, 4) + 0 * sq_tile_stride<16>(), "tile stride");
 
 // Window-size bucket a kernel is instantiated for.
 inline int wbucket(int W) { return W <= 4 ? 4 : W <= 8 ? 8 : W <= 16 ? 16 : 32; }
