@@ -104,7 +104,7 @@ def decode_flush_bytes(wl, N: int) -> int:
 def family(name: str):
     """Kernel family of a rocprofv3 kernel name: decode, prefill, flush or
     decode_flush (the flush kernel's instantiation with the fused decode)."""
-    if "decode_kernel" in name:
+    if "decode_kernel" in name or "decode_split_kernel" in name:
         return "decode"
     if "prefill_kernel" in name:
         return "prefill"
@@ -955,8 +955,9 @@ def main():
     ceiling = stream_read_ceiling(wl, ND, L)
     roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(frac, 4), "traffic": traffic if fuse else None,
-            "kernel": f"lq_gdn_decode_step (decode_kernel<{wl.dk},{wl.dv},{16 if W <= 16 else 32},"
-                      f"{'KDA' if wl.per_key else 'GDN'}>, slots 0..{ND - 1})",
+            "kernel": ("lq_gdn_decode_step (" + (f"decode_split_kernel<{16 if W <= 16 else 32},"
+                       if wl.dk == 128 and W <= 16 else f"decode_kernel<{wl.dk},{wl.dv},{16 if W <= 16 else 32},")
+                       + f"{'KDA' if wl.per_key else 'GDN'}>, slots 0..{ND - 1})"),
             "avg_launch_us": round(dec_total_s * 1e6 / ND, 3),
             "duration_source": "each launch's own execution interval: start/stop events bound to the "
                                "dispatch (hipExtLaunchKernelGGL), the dispatch timestamps rocprofv3's "
