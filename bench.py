@@ -943,9 +943,28 @@ def main():
     if fuse and not args.no_compare:
         step(False)
         ms2 = time_steps(lambda: step(False), max(4, min(16, args.steps)))
+        # kernel time of the window's end both ways: the slot W-1 decode plus
+        # the flush, against the fused launch timed above
+        last_ms, flush_ms = 0.0, 0.0
+        for _ in range(reps):
+            lq.lq_timing_enable(True)
+            step(False)
+            lq.lq_timing_enable(False)
+            fam, t_ms = lq.lq_timing_collect(W * L + L)
+            assert fam == [lq.LQ_KERNEL_DECODE] * (W * L) + [lq.LQ_KERNEL_FLUSH] * L, \
+                "unexpected launch sequence"
+            last_ms += sum(t_ms[(W - 1) * L:W * L])
+            flush_ms += sum(t_ms[W * L:])
+        last_us, flush_us = 1e3 * last_ms / launches, 1e3 * flush_ms / launches
         two_call = {"ms_per_step": round(ms2, 4), "tokens_per_s": round(tokens_per_step / (ms2 * 1e-3), 1),
                     "speedup_fused": round(ms2 / eager_ms, 3),
-                    "step": "last token by lq_gdn_decode_step, then lq_gdn_window_flush (eager)"}
+                    "last_slot_decode_avg_launch_us": round(last_us, 3),
+                    "flush_avg_launch_us": round(flush_us, 3),
+                    "fused_avg_launch_us": round(fl_avg_us, 3),
+                    "kernel_speedup_fused": round((last_us + flush_us) / fl_avg_us, 3),
+                    "step": "last token by lq_gdn_decode_step, then lq_gdn_window_flush (eager); "
+                            "speedup_fused compares eager step times, kernel_speedup_fused the kernels' "
+                            "own durations"}
 
     hsh = kernel_hash()
     traffic = read_traffic(hsh, int(sum(dec_bytes) / ND))
