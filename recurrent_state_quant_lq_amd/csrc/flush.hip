@@ -101,6 +101,36 @@ __device__ __forceinline__ void store_cols(float* p, const float (&x)[CT]) {
 
 __device__ __forceinline__ u64 ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// Operands of v_mfma_f32_16x16x32_bf16.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Three-way bf16 split of 8 floats: x = x1 + x2 + x3 + e with x1 = bf16(x),
+// x2 = bf16(x - x1), x3 = bf16(x - x1 - x2) (round to nearest even); both
+// residuals are exact in fp32 and |e| <= 2^-27 |x|.  The six products
+// x1 y1, x1 y2, x2 y1, x1 y3, x2 y2, x3 y1 of two split numbers are exact in
+// fp32 and leave out terms of at most about 2^-25 |x y|.  Two values per dword,
+// element 2e in the low half (the MFMA operand order).
+__device__ __forceinline__ void split3_bf16(const float (&x)[8], uint4& p1, uint4& p2, uint4& p3) {
+    uint32_t a[4], b[4], c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const f32x2 v = {x[2 * e], x[2 * e + 1]};
+        const bf16x2 h1 = __builtin_convertvector(v, bf16x2);
+        const f32x2 r1 = v - __builtin_convertvector(h1, f32x2);
+        const bf16x2 h2 = __builtin_convertvector(r1, bf16x2);
+        const f32x2 r2 = r1 - __builtin_convertvector(h2, f32x2);
+        const bf16x2 h3 = __builtin_convertvector(r2, bf16x2);
+        a[e] = __builtin_bit_cast(uint32_t, h1);
+        b[e] = __builtin_bit_cast(uint32_t, h2);
+        c[e] = __builtin_bit_cast(uint32_t, h3);
+    }
+    p1 = make_uint4(a[0], a[1], a[2], a[3]);
+    p2 = make_uint4(b[0], b[1], b[2], b[3]);
+    p3 = make_uint4(c[0], c[1], c[2], c[3]);
+}
+
 // Bits [0, n) set; n may be <= 0 or >= 64.
 __device__ __forceinline__ u64 low_bits(int n) {
     return n <= 0 ? 0ull : n >= 64 ? ~0ull : ((1ull << n) - 1ull);
@@ -410,7 +440,17 @@ __device__ __forceinline__ void dma_rows(const float* src, int rmax, float* dst,
     }
 }
 
-// Workgroup LDS of the flush kernel (byte offsets).
+// The window contraction on bf16 MFMAs with three-way operand splits (d = 128,
+// up to 16 slots); the fp32 MFMA otherwise.
+template <int DK, int NPAD>
+struct Bx3 {
+    static constexpr bool on = DK == 128 && NPAD == 16;
+    static constexpr int SIDE = 3 * NPAD * DK * 2;                 // bytes of one side's three parts
+};
+
+// Workgroup LDS of the flush kernel (byte offsets).  With the bf16 contraction
+// the split operands (M parts, then Kt parts) overwrite the buffered rows
+// from MB on once they have been read into registers.
 template <int DK, int DV, int NPAD, bool KDA, bool DEC>
 struct FlushLds {
     static constexpr int RS = 0;                                   // r | s | cv rows
@@ -419,8 +459,12 @@ struct FlushLds {
     static constexpr int MB = GS + 4 * 32;                         // buffered m rows
     static constexpr int KB = MB + NPAD * DV * 4;                  // buffered keys
     static constexpr int GB = KB + NPAD * DK * 4;                  // per-key log-decays
-    static constexpr int TOK = GB + (KDA ? NPAD * DK * 4 : 0);     // token q | v | alpha (DEC)
-    static constexpr int CODEC = TOK + (DEC ? (2 * DK + DV) * 4 : 0);   // codec stage; GEMV partials (DEC)
+    static constexpr int ROWS_END = GB + (KDA ? NPAD * DK * 4 : 0);
+    static constexpr int PARTS = MB;                               // bf16 operand parts (aliasing)
+    static constexpr int PARTS_END = Bx3<DK, NPAD>::on ? MB + 2 * Bx3<DK, NPAD>::SIDE : 0;
+    static constexpr int TOK = ROWS_END > PARTS_END ? ROWS_END : PARTS_END;   // token q | v | k | alpha (DEC)
+    static constexpr int GAM = TOK + (DEC ? 4 * DK * 4 : 0);       // per-key Gamma (KDA)
+    static constexpr int CODEC = GAM + (KDA ? DK * 4 : 0);         // codec stage; GEMV partials (DEC)
     static constexpr int NWF = DK / 16 < 4 ? DK / 16 : 4;
     static constexpr int CODEC_BYTES = (int)sizeof(CodecLds<DK, DV, NWF>);
     static constexpr int GEMV_BYTES = DEC ? (2 * DV + 1) * NWF * 4 : 0;     // DEC partials share the region
@@ -446,6 +490,7 @@ void flush_kernel(FlushArgs a) {
     using S = FS<DK, DV>;
     constexpr int RBW = S::RBW, CT = S::CT, NW = S::NW, RPL = S::RPL;
     constexpr int NPAD = WM <= 16 ? 16 : 32;   // slots padded to the MFMA size
+    constexpr bool BX3 = Bx3<DK, NPAD>::on;
     using RBy = RowBytes<RPL>;
     using LY = FlushLds<DK, DV, NPAD, KDA, DEC>;
 
@@ -460,7 +505,9 @@ void flush_kernel(FlushArgs a) {
     float* s_G = reinterpret_cast<float*>(smem + LY::GB);          // [NPAD][DK] (per-key decay)
     float* s_tq = reinterpret_cast<float*>(smem + LY::TOK);        // token q [DK] (DEC)
     float* s_tv = s_tq + DK;                                       // token v [DV] (DEC)
-    float* s_tal = s_tv + DV;                                      // token alpha [DK] (DEC, per-key)
+    float* s_tk = s_tv + DV;                                       // token k [DK] (DEC)
+    float* s_tal = s_tk + DK;                                      // token alpha [DK] (DEC, per-key)
+    float* s_gam = reinterpret_cast<float*>(smem + LY::GAM);       // Gamma per row (per-key, bf16 path)
     float* s_pq = reinterpret_cast<float*>(smem + LY::CODEC);      // [2][NW][DV] GEMV partials (DEC)
     float* s_pk = s_pq + NW * DV;
     auto& L = *reinterpret_cast<CodecLds<DK, DV, NW>*>(smem + LY::CODEC);
@@ -497,8 +544,8 @@ void flush_kernel(FlushArgs a) {
             if (src) lds_dma16(src + 4 * (lane % SEGL), s_r + s0 * DK);
         }
         if constexpr (DEC) {
-            // token q, v [, alpha]
-            constexpr int NTS = KDA ? 3 : 2;
+            // token q, v, k [, alpha]
+            constexpr int NTS = KDA ? 4 : 3;
             for (int s0 = SPI * w; s0 < NTS; s0 += SPI * NW) {
                 const float* src = nullptr;
 #pragma unroll
@@ -506,11 +553,12 @@ void flush_kernel(FlushArgs a) {
                     const int sg = s0 + q;
                     const float* p = sg == 0 ? reinterpret_cast<const float*>(static_cast<const TI*>(a.q) + head * DK)
                                    : sg == 1 ? reinterpret_cast<const float*>(static_cast<const TI*>(a.v) + head * DV)
+                                   : sg == 2 ? reinterpret_cast<const float*>(static_cast<const TI*>(a.k) + head * DK)
                                    : sg < NTS ? a.alpha + head * DK : nullptr;
                     if (my == q) src = p;
                 }
-                // bf16 q and v fill the first half of their segments
-                const bool in_row = sizeof(TI) == 4 || s0 + my >= 2 || 8 * (lane % SEGL) < DK;
+                // bf16 q, v and k fill the first half of their segments
+                const bool in_row = sizeof(TI) == 4 || s0 + my >= 3 || 8 * (lane % SEGL) < DK;
                 if (src && in_row) lds_dma16(src + 4 * (lane % SEGL), s_tq + s0 * DK);
             }
         }
@@ -523,11 +571,7 @@ void flush_kernel(FlushArgs a) {
         }
         if (!KDA && w == NW - 1 && lane < NPAD) lds_dma4(a.bg + head * W + min(lane, W - 1), s_gs);
         dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, W - 1, s_M, w, lane);
-        // DEC: the token's key lands in row n
-        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane, DEC ? n : -1,
-                               DEC ? reinterpret_cast<const float*>(static_cast<const TI*>(a.k) + head * DK)
-                                   : nullptr,
-                               DK * (int)sizeof(TI) / 4);
+        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane);
         if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, W - 1, s_G, w, lane);
     }
     // D-layout bytes of the base state: column 16 ct + li, this lane's RPL rows
@@ -551,19 +595,53 @@ void flush_kernel(FlushArgs a) {
     if constexpr (DEC) {
         // slot n's key and log-decay
         if (t < DK) {
-            st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, seg_ld<TI>(s_K + n * DK, t));
+            st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, seg_ld<TI>(s_tk, t));
             if constexpr (KDA) st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, glast(t));
             else if (t == 0) st_nt(a.bg + head * (size_t)W + n, gn_s);
         }
     }
 
-    // ---- H = Gamma Hb + Kt^T M (fp32 MFMA, accumulating in place) -------------------------------
-    // A operands: Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg (0 from NM on).
+    // ---- H = Gamma Hb + Kt^T M (MFMA, accumulating in place) ------------------------------------
     // DEC: the MFMA terms cover slots < n; slot n (Kt row = k, its m from the decode) is a
     // rank-1 update afterwards.
     const int NM = DEC ? n : N;
-    float ka[RBW][NPAD / 4];
-    if constexpr (KDA) {
+    // fp32 MFMA: A operands Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg
+    // (0 from NM on).
+    [[maybe_unused]] float ka[RBW][NPAD / 4];
+    if constexpr (BX3) {
+        // bf16 MFMA: lane t splits M[s][j] and Kt[s][j] for the 8 slots s = 8 hs .. 8 hs + 7
+        // of its half (zero from NM on; the buffer may hold anything there) into three bf16
+        // parts each, stored as [part][half][column or row] runs of 8 slots.
+        char* parts = smem + LY::PARTS;
+        const int j = t & (DK - 1), hs = t / DK;
+        float mv[8], kv[8];
+        float gl = 0.0f;
+        if constexpr (KDA) {
+            gl = glast(j);
+            if (hs == 0) s_gam[j] = __expf(gl);
+        } else {
+            gl = glast(0);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sl = 8 * hs + e;
+            const bool live = sl < NM;
+            float dec;
+            if constexpr (KDA) dec = s_G[sl * DK + j];
+            else dec = s_gs[sl];
+            mv[e] = live ? s_M[sl * DV + j] : 0.0f;
+            kv[e] = live ? __expf(gl - dec) * s_K[sl * DK + j] : 0.0f;
+        }
+        lds_barrier();                          // buffered rows read: the parts overwrite them
+        uint4 p[3];
+        split3_bf16(mv, p[0], p[1], p[2]);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) *reinterpret_cast<uint4*>(parts + ((q * 2 + hs) * DV + j) * 16) = p[q];
+        split3_bf16(kv, p[0], p[1], p[2]);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            *reinterpret_cast<uint4*>(parts + Bx3<DK, NPAD>::SIDE + ((q * 2 + hs) * DK + j) * 16) = p[q];
+    } else if constexpr (KDA) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
             const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
@@ -592,7 +670,9 @@ void flush_kernel(FlushArgs a) {
         float sc[CT], rr[RPL], gm[RPL];
         load_cols<CT>(s_s + li, sc);
         load_floats<RPL>(s_r + row0, rr);
-        if constexpr (KDA) {
+        if constexpr (KDA && BX3) {
+            load_floats<RPL>(s_gam + row0, gm);
+        } else if constexpr (KDA) {
 #pragma unroll
             for (int k = 0; k < RPL; ++k) gm[k] = __expf(glast(row0 + k));
         } else {
@@ -615,7 +695,9 @@ void flush_kernel(FlushArgs a) {
         const int ic = __builtin_amdgcn_readfirstlane(s_idx[c]);
         const int r = ic - w * 16 * RBW;                  // row among this wave's rows
         if (r < 0 || r >= 16 * RBW) continue;             // another wave's row
-        const float g = __expf(glast(ic));
+        float g;
+        if constexpr (KDA && BX3) g = s_gam[ic];
+        else g = __expf(glast(ic));
         float cvv[CT];
         load_cols<CT>(s_cv + c * DV + li, cvv);
         if (lg == r / RPL) {
@@ -630,23 +712,54 @@ void flush_kernel(FlushArgs a) {
         }
     }
 
-    // window terms: B = M rows (rows from NM on are zero; the buffer may hold
-    // anything there)
+    // window terms
+    if constexpr (BX3) {
+        // three K = 32 steps, each lane group pairing one part of Kt with one part of M for
+        // its half of the slots: x1 y1, x2 y1, x1 y3 (lane groups 0, 1) and x1 y2, x2 y2,
+        // x3 y1 (lane groups 2, 3), x = Kt, y = M
+        lds_barrier();                          // parts written
+        const char* parts = smem + LY::PARTS;
+        const int hs = lg & 1, hi = lg >> 1;
+        if (NM > 0) {
 #pragma unroll
-    for (int ks = 0; ks < NPAD / 4; ++ks) {
-        if (4 * ks < NM) {
-            float bm[CT];
-            load_cols<CT>(&s_M[(4 * ks + lg) * DV + li], bm);
-            if (4 * ks + 4 > NM) {                 // uniform: the step runs past slot NM - 1
-                const bool live = 4 * ks + lg < NM;
+            for (int m = 0; m < 3; ++m) {
+                const int pa = m == 0 ? 0 : m == 1 ? 1 : (hi ? 2 : 0);
+                const int pb = m < 2 ? hi : (hi ? 0 : 2);
+                bf16x8 A[RBW];
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) bm[ct] = live ? bm[ct] : 0.0f;
+                for (int rb = 0; rb < RBW; ++rb) {
+                    const int rowa = row_of<DK, DV>(w, li >> 2, rb, li & 3);
+                    A[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                        parts + Bx3<DK, NPAD>::SIDE + ((pa * 2 + hs) * DK + rowa) * 16));
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                        parts + ((pb * 2 + hs) * DV + 16 * ct + li) * 16));
+#pragma unroll
+                    for (int rb = 0; rb < RBW; ++rb)
+                        H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rb], bv, H[rb][ct], 0, 0, 0);
+                }
             }
+        }
+    } else {
+        // fp32: B = M rows (rows from NM on are zero; the buffer may hold anything there)
 #pragma unroll
-            for (int rb = 0; rb < RBW; ++rb)
+        for (int ks = 0; ks < NPAD / 4; ++ks) {
+            if (4 * ks < NM) {
+                float bm[CT];
+                load_cols<CT>(&s_M[(4 * ks + lg) * DV + li], bm);
+                if (4 * ks + 4 > NM) {             // uniform: the step runs past slot NM - 1
+                    const bool live = 4 * ks + lg < NM;
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[rb][ks], bm[ct], H[rb][ct], 0, 0, 0);
+                    for (int ct = 0; ct < CT; ++ct) bm[ct] = live ? bm[ct] : 0.0f;
+                }
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        H[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[rb][ks], bm[ct], H[rb][ct], 0, 0, 0);
+            }
         }
     }
 
@@ -656,7 +769,7 @@ void flush_kernel(FlushArgs a) {
     if constexpr (DEC) {
         float* s_an = s_pk + NW * DV;                              // [NW] partial <q, k>
         {
-            float an = t < DK ? seg_ld<TI>(s_tq, t) * seg_ld<TI>(s_K + n * DK, t) : 0.0f;
+            float an = t < DK ? seg_ld<TI>(s_tq, t) * seg_ld<TI>(s_tk, t) : 0.0f;
             an = group_sum<64>(an);
             if (lane == 0) s_an[w] = an;
         }
@@ -670,7 +783,7 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 float x[4];
-                seg_ld_n<4, TI>(vec ? s_K + n * DK : s_tq, row0 + 4 * rb, x);
+                seg_ld_n<4, TI>(vec ? s_tk : s_tq, row0 + 4 * rb, x);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -713,7 +826,7 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 float xk[4];
-                seg_ld_n<4, TI>(s_K + n * DK, row0 + 4 * rb, xk);
+                seg_ld_n<4, TI>(s_tk, row0 + 4 * rb, xk);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
