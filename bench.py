@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F32_PEAK_TFS = 157.3      # MI355X dense fp32 matrix, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix, published
 METRIC = "decode tokens/s and state HBM GB/s (% of peak), int8 GDN, B=64 H=32 d=128"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_step_gdn_b64_h32_d128_w16_pmc.md")
 
@@ -118,6 +119,20 @@ def family(name: str):
 def flush_flops(wl, N: int) -> int:
     """The rebuild's contraction Kt^T M: N*dk*dv multiply-adds."""
     return wl.B * wl.H * 2 * N * wl.dk * wl.dv
+
+
+def flush_mfma(wl, W: int, tfs: float) -> dict:
+    """The contraction's rate against the matrix cores it runs on: at d = 128
+    with up to 16 slots, bf16 MFMAs over three-way operand splits (six bf16
+    products per fp32 product, 16 slots padded per K step); fp32 MFMAs
+    otherwise."""
+    if wl.dk == 128 and W <= 16:
+        executed = tfs * 6 * 16 / W
+        return {"contraction_TFLOPs": round(tfs, 2), "mfma": "bf16 x3 split",
+                "mfma_executed_TFLOPs": round(executed, 2),
+                "mfma_frac": round(executed / MFMA_BF16_PEAK_TFS, 4)}
+    return {"contraction_TFLOPs": round(tfs, 2), "mfma": "fp32",
+            "mfma_frac": round(tfs / MFMA_F32_PEAK_TFS, 4)}
 
 
 def kernel_hash() -> str:
@@ -1016,8 +1031,7 @@ def main():
         "state_GBps": round(dec_gbs, 1),
         ("decode_flush" if fuse else "flush"): {
             "avg_launch_us": round(fl_avg_us, 3), "algorithmic_bytes": fl_alg, "hbm_GBps": round(fl_gbs, 1),
-            "hbm_frac": round(fl_gbs / HBM_PEAK_GBS, 4), "mfma_f32_TFLOPs": round(fl_tfs, 2),
-            "mfma_frac": round(fl_tfs / MFMA_F32_PEAK_TFS, 4)},
+            "hbm_frac": round(fl_gbs / HBM_PEAK_GBS, 4), **flush_mfma(wl, W, fl_tfs)},
         "decode_us_by_slot": [round(x, 3) for x in dec_avg_us],
         "kernel_hash": hsh,
     }

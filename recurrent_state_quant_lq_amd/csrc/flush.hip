@@ -524,8 +524,8 @@ void flush_kernel(FlushArgs a) {
 
     const int8_t* sq = a.sq + head * (DK * DV);
 
-    // ---- loads (unconditional; buffer rows clamped to W-1, slots >= N masked
-    //      after the barrier) ------------------------------------------------------------------------
+    // ---- loads (unconditional; buffer rows clamped to the last one read, slots past
+    //      it masked after the barrier) ----------------------------------------------------------------
     {
         // r, s, compensator rows (DK/4 lanes per vector of 16-byte pieces)
         constexpr int SEGL = DK / 4, SPI = 64 / SEGL;
@@ -570,9 +570,12 @@ void flush_kernel(FlushArgs a) {
             if (src4) lds_dma4(src4, s_idx);
         }
         if (!KDA && w == NW - 1 && lane < NPAD) lds_dma4(a.bg + head * W + min(lane, W - 1), s_gs);
-        dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, W - 1, s_M, w, lane);
-        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, W - 1, s_K, w, lane);
-        if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, W - 1, s_G, w, lane);
+        // buffered rows up to the last one read (DEC: slot n's row is the token's); the
+        // rows past it repeat it, so they cost no further memory traffic
+        const int rlast = max((DEC ? n : N) - 1, 0);
+        dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, rlast, s_M, w, lane);
+        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, rlast, s_K, w, lane);
+        if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, rlast, s_G, w, lane);
     }
     // D-layout bytes of the base state: column 16 ct + li, this lane's RPL rows
     const int row0 = row_of<DK, DV>(w, lg, 0, 0);
@@ -622,15 +625,19 @@ void flush_kernel(FlushArgs a) {
         } else {
             gl = glast(0);
         }
+        // scalar decay: the half's 8 factors e^{g_last - g_s} (hs is uniform in a wave),
+        // one per lane, then read from lanes 0..7
+        [[maybe_unused]] float es = 0.0f;
+        if constexpr (!KDA) es = __expf(gl - s_gs[8 * hs + (lane & 7)]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int sl = 8 * hs + e;
             const bool live = sl < NM;
-            float dec;
-            if constexpr (KDA) dec = s_G[sl * DK + j];
-            else dec = s_gs[sl];
+            float ef;
+            if constexpr (KDA) ef = __expf(gl - s_G[sl * DK + j]);
+            else ef = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(es), e));
             mv[e] = live ? s_M[sl * DV + j] : 0.0f;
-            kv[e] = live ? __expf(gl - dec) * s_K[sl * DK + j] : 0.0f;
+            kv[e] = live ? ef * s_K[sl * DK + j] : 0.0f;
         }
         lds_barrier();                          // buffered rows read: the parts overwrite them
         uint4 p[3];
