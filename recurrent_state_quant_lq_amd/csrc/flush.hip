@@ -385,11 +385,13 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
 #pragma unroll
         for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
         int8_t* dst = out.sq + sq_off<DK>(row0, li) + ct * sq_tile_stride<DK>();
+        // streamed: a wave's pieces of one tile are 512 contiguous bytes, i.e. whole lines
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         if constexpr (RPL == 8)
-            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low4(z[0], z[1], z[2], z[3]),
-                                                        pack_low4(z[4], z[5], z[6], z[7]));
+            __builtin_nontemporal_store(u32x2{pack_low4(z[0], z[1], z[2], z[3]), pack_low4(z[4], z[5], z[6], z[7])},
+                                        reinterpret_cast<u32x2*>(dst));
         else
-            *reinterpret_cast<uint32_t*>(dst) = pack_low4(z[0], z[1], z[2], z[3]);
+            __builtin_nontemporal_store(pack_low4(z[0], z[1], z[2], z[3]), reinterpret_cast<uint32_t*>(dst));
     }
 }
 
