@@ -47,10 +47,15 @@ __global__ __launch_bounds__(NT) void fp32_rec_kernel(RecArgs a) {
     const int c0 = (t % CPR4) * 4;
 
     float* h = a.h + head * (size_t)DK * DV;
+    // the state is read once and written once per launch: streamed (a row's 32
+    // lanes cover 512 contiguous bytes, so the stores are whole lines)
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
     float4 H[PASSES];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-        H[p] = *reinterpret_cast<const float4*>(h + (size_t)(p * RPP + rg) * DV + c0);
+    for (int p = 0; p < PASSES; ++p) {
+        const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(h + (size_t)(p * RPP + rg) * DV + c0));
+        H[p] = make_float4(x[0], x[1], x[2], x[3]);
+    }
 
     for (int tok = 0; tok < a.T; ++tok) {
         const size_t th = (size_t)tok * a.heads + head;
@@ -127,7 +132,8 @@ __global__ __launch_bounds__(NT) void fp32_rec_kernel(RecArgs a) {
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
-        *reinterpret_cast<float4*>(h + (size_t)(p * RPP + rg) * DV + c0) = H[p];
+        __builtin_nontemporal_store(f32x4v{H[p].x, H[p].y, H[p].z, H[p].w},
+                                    reinterpret_cast<f32x4v*>(h + (size_t)(p * RPP + rg) * DV + c0));
     (void)GPW;
 }
 
