@@ -230,6 +230,16 @@ class LayerState:
     def c_state(self) -> lq_state:
         return lq_state(*[_ptr(getattr(self, n)) for n in _STATE_FIELDS])
 
+    def rows(self, b0: int, b1: int) -> "LayerState":
+        """Batch rows b0 .. b1-1 as a state of their own: views of the same device
+        memory (no copy) with B = b1 - b0, so that parts of a batch can run as
+        separate calls, e.g. as independent chains on separate streams."""
+        d = lq_dims.from_buffer_copy(self.dims)
+        if not (0 <= b0 < b1 <= d.B):
+            raise ValueError(f"rows {b0}..{b1} outside the batch of {d.B}")
+        d.B = b1 - b0
+        return LayerState(d, *[getattr(self, n)[b0:b1] for n in _STATE_FIELDS])
+
     def ready(self, with_buffer=True) -> lq_state:
         """The C struct of this state, validated (shapes, dtypes, device) once
         for the tensors the fields hold; a field replaced by another tensor is

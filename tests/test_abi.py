@@ -274,3 +274,22 @@ def test_measure_stream_read_argument_errors():
     assert f(src, 1024, 4, 1, 0, sink, 16, None) == lq.LQ_ERR_DIMS
     assert f(src, 1024, 4, 0, 0, sink, 4112, None) == lq.LQ_ERR_DIMS
     assert f(src, 1024, 4, 0, 0, sink, 24, None) == lq.LQ_ERR_DIMS
+
+
+def test_layer_state_rows_are_views():
+    """LayerState.rows: rows b0..b1-1 as a state of their own, sharing memory."""
+    d = lq.make_dims(6, 2, 16, 16, 4, 1, lq.LQ_DECAY_PER_KEY, 1)
+    st = lq.LayerState.allocate(d, "cpu")
+    part = st.rows(2, 5)
+    assert part.dims.B == 3 and st.dims.B == 6
+    assert (part.dims.H, part.dims.dk, part.dims.W, part.dims.C) == (2, 16, 4, 1)
+    for f in ("sq", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_k", "buf_m", "buf_g"):
+        whole, view = getattr(st, f), getattr(part, f)
+        assert view.shape[0] == 3 and view.shape[1:] == whole.shape[1:]
+        assert view.is_contiguous()
+        assert view.data_ptr() == whole[2].data_ptr()
+    part.row_scale.fill_(7.0)
+    assert float(st.row_scale[2:5].min()) == 7.0 and float(st.row_scale[:2].abs().max()) == 0.0
+    for b0, b1 in ((0, 0), (3, 2), (-1, 2), (0, 7)):
+        with pytest.raises(ValueError):
+            st.rows(b0, b1)
