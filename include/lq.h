@@ -51,6 +51,11 @@
  *     the *_ragged calls take one per batch row from a device array.
  *   - Token vectors q, k, v and outputs o are fp32 or bf16 (lq_dims.io_dtype);
  *     everything else is fp32 (int8 / int32 where stated).
+ *   - Batch rows are independent: rows b0 .. b1-1 of a batch are a batch of
+ *     their own (every pointer advanced by b0 rows, lq_dims.B = b1 - b0), and
+ *     calls on disjoint row ranges may run at the same time on different
+ *     streams.  Each (row, head) is computed the same way whatever the batch
+ *     of its call, so the results do not depend on the split.
  */
 #ifndef LQ_H
 #define LQ_H
