@@ -886,16 +886,22 @@ def main():
     o = torch.empty((wl.B, wl.H, wl.dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def step(fused=fuse, lays=None, rows=None, stream=None):
-        # one chain of the step: every layer's window, for batch rows `rows` (all by default)
+    def step(fused=fuse, lays=None, rows=None, stream=None, part="all"):
+        # one chain of the step: every layer's window, for batch rows `rows` (all by
+        # default); part "decode" or "end": only the decode launches or only the
+        # window-end launches
         lays = layers if lays is None else lays
         cut = (lambda x: x) if rows is None else (lambda x: x[rows[0]:rows[1]])
         for n in range(W - 1 if fused else W):
+            if part == "end":
+                break
             for l in range(L):
                 tk = ring[l]
                 lq.lq_gdn_decode_step(lays[l], n, cut(tk["q"][n]), cut(tk["k"][n]), cut(tk["v"][n]),
                                       cut(tk["alpha"][n]), cut(tk["beta"][n]), cut(o), stream=stream)
         for l in range(L):
+            if part == "decode":
+                break
             if fused:
                 tk, n = ring[l], W - 1
                 lq.lq_gdn_decode_step_flush(lays[l], n, cut(tk["q"][n]), cut(tk["k"][n]), cut(tk["v"][n]),
@@ -913,22 +919,13 @@ def main():
     chains = [[st.rows(i * Bs, (i + 1) * Bs) for st in layers] for i in range(S)]
     side = [torch.cuda.Stream(device=dev) for _ in range(S)]
 
-    def step_streams(fused=fuse, decode_only=False):
+    def step_streams(fused=fuse, part="all"):
         main = torch.cuda.current_stream()
         for s_ in side:
             s_.wait_stream(main)
         for i, s_ in enumerate(side):
             with torch.cuda.stream(s_):
-                if decode_only:
-                    for n in range(W - 1):
-                        for l in range(L):
-                            tk = ring[l]
-                            r0, r1 = i * Bs, (i + 1) * Bs
-                            lq.lq_gdn_decode_step(chains[i][l], n, tk["q"][n][r0:r1], tk["k"][n][r0:r1],
-                                                  tk["v"][n][r0:r1], tk["alpha"][n][r0:r1], tk["beta"][n][r0:r1],
-                                                  o[r0:r1], stream=s_)
-                else:
-                    step(fused, lays=chains[i], rows=(i * Bs, (i + 1) * Bs), stream=s_)
+                step(fused, lays=chains[i], rows=(i * Bs, (i + 1) * Bs), stream=s_, part=part)
         for s_ in side:
             main.wait_stream(s_)
 
@@ -981,18 +978,22 @@ def main():
             g1 = capture(step)
             single_ms = time_steps(g1.replay, args.steps)
             del g1
-        gd = capture((lambda: step_streams(decode_only=True)) if S > 1 else
-                     (lambda: [lq.lq_gdn_decode_step(layers[l], n, ring[l]["q"][n], ring[l]["k"][n], ring[l]["v"][n],
-                                                     ring[l]["alpha"][n], ring[l]["beta"][n], o)
-                               for n in range(W - 1) for l in range(L)]))
+        timed_part = (lambda part: (lambda: step_streams(part=part))) if S > 1 else \
+            (lambda part: (lambda: step(part=part)))
+        gd = capture(timed_part("decode"))
         dms = time_steps(gd.replay, args.steps)
         del gd
-        dbytes = L * sum(decode_bytes(wl, n) for n in range(W - 1))
-        sustained = {"schedule": f"the decode launches of the timed step (slots 0..{W - 2}, {L} layers) "
+        ge = capture(timed_part("end"))
+        ems = time_steps(ge.replay, args.steps)
+        del ge
+        dbytes = L * sum(decode_bytes(wl, n) for n in range(W - 1 if fuse else W))
+        sustained = {"schedule": f"the decode launches of the timed step (slots 0..{W - 2 if fuse else W - 1}, {L} layers) "
                                  + (f"as {S} chains of {Bs} batch rows on {S} streams" if S > 1 else "on one stream")
                                  + ", graph-replayed",
                      "ms": round(dms, 4), "bytes": dbytes, "GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
-                     "frac": round(dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                     "frac": round(dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     # the window-end launches alone in the same schedule: per layer, for all B rows
+                     "window_end_us_per_layer": round(1e3 * ems / L, 3)}
         # the timed step's state is reset by running the full step again (windows stay aligned)
         run()
         torch.cuda.synchronize()
