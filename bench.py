@@ -702,6 +702,55 @@ def stream_read_ceiling(wl, slots: int, L: int, reps: int = 6):
     return out
 
 
+def stream_read_sustained(wl, slots: int, L: int, S: int, steps: int):
+    """The sustained counterpart of stream_read_ceiling: the decode launches'
+    bytes of one step (slots 0..slots-1 of L layers) read by the one-shot
+    reference kernel in the timed schedule, S chains of B/S rows (slices of the
+    same buffers), one per stream, captured in one graph and replayed."""
+    import torch
+    from recurrent_state_quant_lq_amd import lq
+    heads = wl.B * wl.H
+    hs = heads // S
+    rw = [decode_read_write_bytes(wl, n) for n in range(slots)]
+    rd = 16 * round(sum(r for r, _ in rw) / slots / 16)
+    wr = 16 * round(sum(w for _, w in rw) / slots / 16)
+    dev = torch.device("cuda:0")
+    srcs = [torch.randint(0, 255, (heads * rd,), dtype=torch.uint8, device=dev) for _ in range(L)]
+    sinks = [torch.empty((heads * wr,), dtype=torch.uint8, device=dev) for _ in range(L)]
+    side = [torch.cuda.Stream(device=dev) for _ in range(S)]
+
+    def run():
+        main = torch.cuda.current_stream()
+        for s_ in side:
+            s_.wait_stream(main)
+        for i, s_ in enumerate(side):
+            for _ in range(slots):
+                for l in range(L):
+                    lq.lq_measure_stream_read(srcs[l][i * hs * rd:(i + 1) * hs * rd], rd, hs, 0, 0,
+                                              sinks[l][i * hs * wr:(i + 1) * hs * wr], wr, stream=s_)
+        for s_ in side:
+            main.wait_stream(s_)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = slots * L * heads * (rd + wr)
+    del g, srcs, sinks
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"schedule": f"one-shot reads of the same bytes, {S} chain(s) of {hs} heads", "ms": round(ms, 4),
+            "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def host_cpu():
     """The host's CPU model, logical CPU count, the CPUs this process may run
     on, and the cgroup CPU quota if one is set."""
@@ -994,6 +1043,9 @@ def main():
                      "frac": round(dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      # the window-end launches alone in the same schedule: per layer, for all B rows
                      "window_end_us_per_layer": round(1e3 * ems / L, 3)}
+        rc_s = stream_read_sustained(wl, W - 1 if fuse else W, L, S, args.steps)
+        sustained["read_ceiling"] = rc_s
+        sustained["frac_of_read"] = round(sustained["frac"] / rc_s["frac"], 4)
         # the timed step's state is reset by running the full step again (windows stay aligned)
         run()
         torch.cuda.synchronize()
