@@ -67,12 +67,11 @@ def decode_bytes(wl, n: int) -> int:
 
 
 def scope_table_decode_bytes(wl, n: int) -> int:
-    """The decode step's algorithmic bytes at slot n as the hot-path scope
-    table counts them, for the WY buffer with both factors stored: per slot
-    4 (2 dk + dv + a) bytes (k, y, u, g), n slots read and slot n written.
-    23,068 + 1,540 n per head at d = 128 (GDN).  This build's buffer stores
-    one projected vector m per slot instead of y and u (4 (dk + dv + a) bytes),
-    which decode_bytes counts."""
+    """The decode step's algorithmic bytes at slot n counted for the WY buffer
+    with both factors stored: per slot 4 (2 dk + dv + a) bytes (k, y, u, g),
+    n slots read and slot n written; 23,068 + 1,540 n per head at d = 128
+    (GDN).  The library's buffer stores one projected vector m per slot
+    instead of y and u (4 (dk + dv + a) bytes), which decode_bytes counts."""
     dk, dv, C = wl.dk, wl.dv, wl.C
     a = dk if wl.per_key else 1
     codec = dk * dv + 4 * dk + 4 * dv + C * (4 * dv + 4)
@@ -1126,8 +1125,8 @@ def main():
                                "timed graph replays",
             "bytes_per_launch_avg": int(sum(dec_bytes) / ND),
             "bytes_note": "the kernel's own algorithmic bytes: its buffer slot holds k, m, g "
-                          "(4 (dk + dv + a) bytes); the WY buffer of the scope table stores y and u "
-                          "(4 (2 dk + dv + a) bytes), counted under scope_table",
+                          "(4 (dk + dv + a) bytes); a WY buffer storing y and u takes "
+                          "4 (2 dk + dv + a) bytes per slot, counted under scope_table",
             "scope_table": {"bytes_per_launch_avg": int(st_bytes / ND),
                             "achieved": round(st_bytes / dec_total_s / 1e9, 1), "frac": round(st_frac, 4)},
             "sustained": sustained,

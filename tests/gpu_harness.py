@@ -285,7 +285,7 @@ def free_run(wl: Workload, sample, *, host_tokens: bool, T: int) -> dict:
 
 def oracle_threads() -> int:
     """Worker threads for per-head oracle work (ctypes releases the GIL in
-    each call); at most 16, the host share of a one-GPU machine."""
+    each call); at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
