@@ -298,9 +298,12 @@ void prefill_kernel(PrefillArgs a) {
                 load_floats<4>((KDA ? sXk : sK) + li * DKP + rt * 16 + 4 * lg, ak);
                 load_floats<4>((KDA ? sXq : sQ) + li * DKP + rt * 16 + 4 * lg, aq);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
+                for (int v = 0; v < 4; ++v)
                     hk = __builtin_amdgcn_mfma_f32_16x16x4f32(KDA ? ak[v] : ak[v] * eg, H[rt][ct][v], hk, 0, 0, 0);
-                    hq = __builtin_amdgcn_mfma_f32_16x16x4f32(KDA ? aq[v] : aq[v] * eg, H[rt][ct][v], hq, 0, 0, 0);
+                if (a.o) {                                // HQ only feeds the outputs
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        hq = __builtin_amdgcn_mfma_f32_16x16x4f32(KDA ? aq[v] : aq[v] * eg, H[rt][ct][v], hq, 0, 0, 0);
                 }
                 if (rt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }

@@ -386,6 +386,28 @@ def test_prefill_kernel(dk, kda, T, zero):
             assert codec_equal(head_codec(st, b, hh), O.quantize(hg, C, 1)), ("codec", b, hh)
 
 
+@pytest.mark.parametrize("dk,kda,bf16", [(128, False, False), (128, True, False), (64, False, True)])
+def test_prefill_state_without_outputs(dk, kda, bf16):
+    """Without an output array the prefill skips the query products; the state
+    and its codec must be the same, bit for bit, as with outputs."""
+    B, H, C, T = 4, 3, 4, 41
+    say(f"prefill without outputs dk={dk} kda={kda} bf16={bf16}")
+    d = lq.make_dims(B, H, dk, dk, 16, C, int(kda), 1, lq.LQ_IO_BF16 if bf16 else lq.LQ_IO_F32)
+    tk = io_tokens(inputs.device_tokens(91 + dk, T, B, H, dk, dk, per_key=kda, beta_lo=0.1, beta_hi=0.9,
+                                        device="cuda"), bf16)
+    g = torch.Generator(device="cuda").manual_seed(dk)
+    h0 = torch.randn((B, H, dk, dk), device="cuda", generator=g) * 0.3
+    h1, h2 = h0.clone(), h0.clone()
+    s1, s2 = lq.LayerState.allocate(d), lq.LayerState.allocate(d)
+    o = torch.empty((T, B, H, dk), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    lq.lq_gdn_prefill(d, s1, h1, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], o)
+    lq.lq_gdn_prefill(d, s2, h2, T, tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    for f in ("sq", "row_scale", "col_scale", "comp_idx", "comp_val"):
+        assert torch.equal(getattr(s1, f), getattr(s2, f)), f
+
+
 @pytest.mark.parametrize("kda", [False, True])
 def test_prefill_matches_fp32_recurrence_full_size(kda):
     """At the benchmark's shape (B=64 H=32 d=128, or B=32 per-key) and a
