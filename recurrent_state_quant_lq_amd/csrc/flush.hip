@@ -12,9 +12,11 @@
 // (k_i, g_i, m_i; m_i = u_i - Hb^T y_i, see decode.hip):
 //     H = Gamma Hb + Kt^T M            (dk x dv,  contraction over N)
 // with Kt[i][c] = exp(g_{N-1}[c] - g_i[c]) k_i[c], M = [m_0; ...; m_{N-1}] and
-// Gamma = diag exp(g_{N-1}).  Gamma Hb is dequantized into the accumulators
-// of v_mfma_f32_16x16x4_f32; each compensator row gamma(idx_c) cv_c is added
-// to row idx_c by the 16 lanes that hold it.
+// Gamma = diag exp(g_{N-1}).  Gamma Hb is dequantized into the MFMA
+// accumulators; each compensator row gamma(idx_c) cv_c is added to row idx_c
+// by the 16 lanes that hold it.  At d = 128 with up to 16 slots Kt^T M runs on
+// v_mfma_f32_16x16x32_bf16 over three-way bf16 splits of Kt and M (exact to
+// fp32 rounding; split3_bf16), otherwise on v_mfma_f32_16x16x4_f32.
 //
 // Register layout ("D layout") of H in one workgroup: NW waves; lane l
 // (li = l % 16, lg = l / 16) of wave w holds, for v4 register (rb, ct),
