@@ -202,6 +202,26 @@ def trace_summary(out_md: str, stats_csv: str, command: str):
               "Averages per kernel family over all its launches (decode: every window slot "
               "but the last equally often; decode_flush: the last token with the flush):", "",
               json.dumps(summ), ""]
+    # per launch size, from the per-dispatch trace beside the stats: launches of
+    # all batch rows and launches of one chain's rows are told apart by their grid
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if trace_csv != stats_csv and os.path.exists(trace_csv):
+        groups = {}
+        for r in _csv_rows(trace_csv):
+            f = family(_short(r["Kernel_Name"])) if "lq::" in r["Kernel_Name"] else None
+            if not f:
+                continue
+            wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            g = groups.setdefault((f, wgs), [0, 0.0])
+            g[0] += 1
+            g[1] += us
+        lines += ["Per launch size (workgroups per launch, from the per-dispatch trace):", "",
+                  "| family | workgroups | launches | average us |", "|---|---:|---:|---:|"]
+        for (f, wgs), (n, tot) in sorted(groups.items()):
+            lines.append(f"| {f} | {wgs} | {n} | {tot / n:.3f} |")
+            summ[f"{f}_{wgs}wg_avg_launch_us"] = round(tot / n, 3)
+        lines += ["", json.dumps({k: v for k, v in summ.items() if "wg_" in k}), ""]
     open(out_md, "w").write("\n".join(lines))
     print(json.dumps(summ))
 
