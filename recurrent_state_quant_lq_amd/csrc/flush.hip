@@ -133,14 +133,32 @@ __device__ __forceinline__ void split3_bf16(const float (&x)[8], uint4& p1, uint
     p3 = make_uint4(c[0], c[1], c[2], c[3]);
 }
 
-// Bits [0, n) set; n may be <= 0 or >= 64.
-__device__ __forceinline__ u64 low_bits(int n) {
-    return n <= 0 ? 0ull : n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+// Rounding of y through the offset (y + 1.5 * 2^23, round to nearest even)
+// with the sum's low byte written into byte B of w and the other bytes of w
+// kept: an SDWA destination select with the unused bits preserved, so the
+// bytes of four values are packed as they are rounded.
+template <int B>
+__device__ __forceinline__ void round_into_byte(uint32_t& w, float y, float off) {
+    static_assert(B >= 1 && B <= 3, "bytes 1..3");
+    if constexpr (B == 1)
+        asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+            : "+v"(w) : "v"(y), "v"(off));
+    else if constexpr (B == 2)
+        asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+            : "+v"(w) : "v"(y), "v"(off));
+    else
+        asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+            : "+v"(w) : "v"(y), "v"(off));
 }
 
-// Number of set bits of the 128-bit mask (lo, hi) below row `row`.
-__device__ __forceinline__ int bits_below(u64 lo, u64 hi, int row) {
-    return __popcll(lo & low_bits(row)) + __popcll(hi & low_bits(row - 64));
+// rint of four values (|y| <= 127) as two's-complement bytes, a first.
+__device__ __forceinline__ uint32_t round_pack4(float a, float b, float c, float d) {
+    const float off = kRoundOff;
+    uint32_t w = __float_as_uint(a + off);       // byte 0; bytes 1..3 are overwritten
+    round_into_byte<1>(w, b, off);
+    round_into_byte<2>(w, c, off);
+    round_into_byte<3>(w, d, off);
+    return w;
 }
 
 // Maxima over the four 16-lane rows of a wave for four values at once, with
@@ -242,33 +260,26 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
     lds_barrier();
 
     // The C largest rows, ties to the lower row: C rounds of a wave argmax
-    // over the magnitudes' bit patterns (every wave computes the same set).
+    // (every wave computes the same set).  A free row's key is its magnitude's
+    // bit pattern plus one (same order; at most 0x7f800001), a taken or absent
+    // row's key is 0, so the maximum is always a free row (C < DK).
     u64 lo = 0, hi = 0;
     {
-        bool ta = lane >= DK, tb = lane + 64 >= DK;     // taken or absent
-        uint32_t ma = ta ? 0u : __float_as_uint(L.m[lane]);
-        uint32_t mb = tb ? 0u : __float_as_uint(L.m[lane + 64]);
+        uint32_t ka = lane < DK ? __float_as_uint(L.m[lane]) + 1u : 0u;
+        uint32_t kb = lane + 64 < DK ? __float_as_uint(L.m[lane + 64]) + 1u : 0u;
 #pragma unroll
         for (int c = 0; c < CMAX; ++c)
             if (c < C) {
-                const uint32_t mx = wave_umax(umax(ma, mb));
-                u64 ca = ballot(!ta && ma == mx), cb = ballot(!tb && mb == mx);
-                if ((ca | cb) == 0) {            // unreachable for valid rows: lowest free row
-                    ca = ballot(!ta);
-                    cb = ballot(!tb);
-                }
-                const int r = ca ? __builtin_ctzll(ca) : 64 + __builtin_ctzll(cb);
-                if (r < 64)
+                const uint32_t mx = wave_umax(umax(ka, kb));
+                const u64 ca = ballot(ka == mx), cb = ballot(kb == mx);
+                if (ca) {
+                    const int r = __builtin_ctzll(ca);
                     lo |= 1ull << r;
-                else
-                    hi |= 1ull << (r - 64);
-                if (lane == r) {
-                    ta = true;
-                    ma = 0u;
-                }
-                if (lane + 64 == r) {
-                    tb = true;
-                    mb = 0u;
+                    ka = lane == r ? 0u : ka;
+                } else {
+                    const int r = __builtin_ctzll(cb);
+                    hi |= 1ull << r;
+                    kb = lane == r ? 0u : kb;
                 }
             }
     }
@@ -291,10 +302,16 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
     // compensator rows stored by the lanes that hold them (one row: 16
     // lanes, one column of each tile), residual rows zeroed
     {
-        const u64 half = (w * 16 * RBW >= 64) ? hi : lo;
-        const uint32_t bits = (uint32_t)(half >> (row0 & 63)) & ((1u << RPL) - 1u);
+        // a wave's rows lie in one 32-row quarter: its bits, and the set bits below it
+        static_assert(16 * RBW <= 32, "row quarters");
+        const int wb = w * 16 * RBW;
+        const u64 hm = wb >= 64 ? hi : lo;
+        const uint32_t qm = (wb & 32) ? (uint32_t)(hm >> 32) : (uint32_t)hm;
+        const int o = row0 & 31;
+        const uint32_t bits = (qm >> o) & ((1u << RPL) - 1u);
         if (ballot(bits != 0)) {
-            const int base = bits_below(lo, hi, row0);
+            const int base = (wb >= 64 ? __popcll(lo) : 0) + ((wb & 32) ? __popc((uint32_t)hm) : 0) +
+                             __popc(qm & ((1u << o) - 1u));
 #pragma unroll
             for (int k = 0; k < RPL; ++k)
                 if ((bits >> k) & 1u) {
@@ -383,17 +400,17 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
     // |Y * lam| <= 127 (1 + 2^-24)^2, which rounds to at most 127.
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-        uint32_t z[RPL];
+        float y[RPL];
 #pragma unroll
-        for (int k = 0; k < RPL; ++k) z[k] = __float_as_uint(H[k / 4][ct][k % 4] * lam[k] + kRoundOff);
+        for (int k = 0; k < RPL; ++k) y[k] = H[k / 4][ct][k % 4] * lam[k];
         int8_t* dst = out.sq + sq_off<DK>(row0, li) + ct * sq_tile_stride<DK>();
         // streamed: a wave's pieces of one tile are 512 contiguous bytes, i.e. whole lines
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         if constexpr (RPL == 8)
-            __builtin_nontemporal_store(u32x2{pack_low4(z[0], z[1], z[2], z[3]), pack_low4(z[4], z[5], z[6], z[7])},
+            __builtin_nontemporal_store(u32x2{round_pack4(y[0], y[1], y[2], y[3]), round_pack4(y[4], y[5], y[6], y[7])},
                                         reinterpret_cast<u32x2*>(dst));
         else
-            __builtin_nontemporal_store(pack_low4(z[0], z[1], z[2], z[3]), reinterpret_cast<uint32_t*>(dst));
+            __builtin_nontemporal_store(round_pack4(y[0], y[1], y[2], y[3]), reinterpret_cast<uint32_t*>(dst));
     }
 }
 
@@ -527,9 +544,14 @@ void flush_kernel(FlushArgs a) {
     const int n = N - 1;                          // DEC: the decoded token's slot
 
     const int8_t* sq = a.sq + head * (DK * DV);
+    // buffered rows up to the last one read (DEC: slot n's row is the token's); the rows
+    // past it repeat it, so they cost no further memory traffic
+    const int rlast = max((DEC ? n : N) - 1, 0);
+    // slots in the window terms; DEC: slot n (Kt row = k, its m from the decode) is a
+    // rank-1 update afterwards
+    const int NM = DEC ? n : N;
 
-    // ---- loads (unconditional; buffer rows clamped to the last one read, slots past
-    //      it masked after the barrier) ----------------------------------------------------------------
+    // ---- loads (unconditional) --------------------------------------------------------------------
     {
         // r, s, compensator rows (DK/4 lanes per vector of 16-byte pieces)
         constexpr int SEGL = DK / 4, SPI = 64 / SEGL;
@@ -573,13 +595,44 @@ void flush_kernel(FlushArgs a) {
             else if (DEC && !KDA && lane == 9) src4 = a.alpha + head;
             if (src4) lds_dma4(src4, s_idx);
         }
-        if (!KDA && w == NW - 1 && lane < NPAD) lds_dma4(a.bg + head * W + min(lane, W - 1), s_gs);
-        // buffered rows up to the last one read (DEC: slot n's row is the token's); the
-        // rows past it repeat it, so they cost no further memory traffic
-        const int rlast = max((DEC ? n : N) - 1, 0);
-        dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, rlast, s_M, w, lane);
-        dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, rlast, s_K, w, lane);
-        if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, rlast, s_G, w, lane);
+        if constexpr (!BX3) {
+            if (!KDA && w == NW - 1 && lane < NPAD) lds_dma4(a.bg + head * W + min(lane, W - 1), s_gs);
+            dma_rows<NPAD, DV, NW>(a.bm + head * (size_t)W * DV, rlast, s_M, w, lane);
+            dma_rows<NPAD, DK, NW>(a.bk + head * (size_t)W * DK, rlast, s_K, w, lane);
+            if constexpr (KDA) dma_rows<NPAD, DK, NW>(a.bg + head * (size_t)W * DK, rlast, s_G, w, lane);
+        }
+    }
+    // bf16 contraction: lane t holds column j of the buffered m and key rows (and per-key
+    // log-decays) for the 8 slots s = 8 hs .. 8 hs + 7 of its half, in registers, loaded
+    // before the state bytes so that the split below runs while those are in flight.
+    // g_last: the log-decay of the last slot, g_{N-1}, or (DEC) the decoded token's
+    // g_n = g_{n-1} + log alpha; per head (scalar decay) or for column j (per-key).
+    const int j = t & (DK - 1), hs = t / DK;
+    [[maybe_unused]] float mv[8], kv[8], gv[8];
+    [[maybe_unused]] float gs_l = 0.0f, g_prev = 0.0f, al = 1.0f;
+    if constexpr (BX3) {
+        // g_prev: g_{n-1} (DEC; 0 at n = 0) or g_{N-1}; al: the token's decay (DEC);
+        // per head (scalar decay) or for column j (per-key)
+        if constexpr (KDA) {
+            const float* bg = a.bg + head * (size_t)W * DK + j;
+            g_prev = DEC ? (n > 0 ? bg[(n - 1) * DK] : 0.0f) : bg[(N - 1) * DK];
+            if constexpr (DEC) al = a.alpha[head * DK + j];
+        } else {
+            const float* bg = a.bg + head * (size_t)W;
+            g_prev = DEC ? (n > 0 ? bg[n - 1] : 0.0f) : bg[N - 1];
+            if constexpr (DEC) al = a.alpha[head];
+            // lane (8 hs + e) % 64 holds slot 8 hs + e's log-decay, e < 8
+            gs_l = bg[min(8 * hs + (lane & 7), rlast)];
+        }
+        const float* bm = a.bm + head * (size_t)W * DV + j;
+        const float* bk = a.bk + head * (size_t)W * DK + j;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sl = min(8 * hs + e, rlast);
+            mv[e] = bm[sl * DV];
+            kv[e] = bk[sl * DK];
+            if constexpr (KDA) gv[e] = a.bg[(head * (size_t)W + sl) * DK + j];
+        }
     }
     // D-layout bytes of the base state: column 16 ct + li, this lane's RPL rows
     const int row0 = row_of<DK, DV>(w, lg, 0, 0);
@@ -587,63 +640,44 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
         hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + sq_off<DK>(row0, li) + ct * sq_tile_stride<DK>());
-    all_loads_barrier();
-
-    // log-decay of the last slot, g_{N-1}[row]: from the buffer, or (DEC) the
-    // decoded token's g_n = g_{n-1} + log alpha
-    float gn_s = 0.0f;
-    if constexpr (DEC && !KDA) gn_s = (n > 0 ? s_gs[n - 1] : 0.0f) + logf(__int_as_float(s_idx[9]));
-    auto glast = [&](int row) -> float {
-        if constexpr (DEC)
-            return KDA ? (n > 0 ? s_G[(n - 1) * DK + row] : 0.0f) + logf(s_tal[row]) : gn_s;
-        else
-            return KDA ? s_G[(N - 1) * DK + row] : s_gs[N - 1];
-    };
-    if constexpr (DEC) {
-        // slot n's key and log-decay
-        if (t < DK) {
-            st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, seg_ld<TI>(s_tk, t));
-            if constexpr (KDA) st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, glast(t));
-            else if (t == 0) st_nt(a.bg + head * (size_t)W + n, gn_s);
-        }
-    }
-
-    // ---- H = Gamma Hb + Kt^T M (MFMA, accumulating in place) ------------------------------------
-    // DEC: the MFMA terms cover slots < n; slot n (Kt row = k, its m from the decode) is a
-    // rank-1 update afterwards.
-    const int NM = DEC ? n : N;
-    // fp32 MFMA: A operands Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg
-    // (0 from NM on).
-    [[maybe_unused]] float ka[RBW][NPAD / 4];
+    // The state-byte loads stay issued ahead of the split, and the split's inputs pass
+    // through empty asm statements after them: the split cannot be scheduled above the
+    // state-byte loads, and since loads return in order its wait leaves those in flight.
+    asm volatile("" ::: "memory");
     if constexpr (BX3) {
-        // bf16 MFMA: lane t splits M[s][j] and Kt[s][j] for the 8 slots s = 8 hs .. 8 hs + 7
-        // of its half (zero from NM on; the buffer may hold anything there) into three bf16
-        // parts each, stored as [part][half][column or row] runs of 8 slots.
-        char* parts = smem + LY::PARTS;
-        const int j = t & (DK - 1), hs = t / DK;
-        float mv[8], kv[8];
-        float gl = 0.0f;
-        if constexpr (KDA) {
-            gl = glast(j);
-            if (hs == 0) s_gam[j] = __expf(gl);
-        } else {
-            gl = glast(0);
-        }
-        // scalar decay: the half's 8 factors e^{g_last - g_s} (hs is uniform in a wave),
-        // one per lane, then read from lanes 0..7
-        [[maybe_unused]] float es = 0.0f;
-        if constexpr (!KDA) es = __expf(gl - s_gs[8 * hs + (lane & 7)]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int sl = 8 * hs + e;
-            const bool live = sl < NM;
-            float ef;
-            if constexpr (KDA) ef = __expf(gl - s_G[sl * DK + j]);
-            else ef = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(es), e));
-            mv[e] = live ? s_M[sl * DV + j] : 0.0f;
-            kv[e] = live ? ef * s_K[sl * DK + j] : 0.0f;
+            asm volatile("" : "+v"(mv[e]));
+            asm volatile("" : "+v"(kv[e]));
+            if constexpr (KDA) asm volatile("" : "+v"(gv[e]));
         }
-        lds_barrier();                          // buffered rows read: the parts overwrite them
+        asm volatile("" : "+v"(g_prev));
+        asm volatile("" : "+v"(al));
+        if constexpr (!KDA) asm volatile("" : "+v"(gs_l));
+    }
+    // g_last: the decoded token's g_n = g_{n-1} + log alpha (DEC), else g_{N-1}
+    [[maybe_unused]] const float gl_b = DEC ? g_prev + logf(al) : g_prev;
+    [[maybe_unused]] const float gl_j = gl_b, gl_h = gl_b;
+
+    if constexpr (BX3) {
+        // Kt[s][j] = e^{g_last - g_s} k_s[j], zero from slot NM on (those slots' m rows repeat
+        // a written row, so their products are zero); M and Kt split into three bf16 parts
+        // each, stored as [part][half][column or row] runs of 8 slots.  The parts region
+        // is no copy's target, so it is written before the loads have all landed.
+        char* parts = smem + LY::PARTS;
+        float ev[8];
+        if constexpr (KDA) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ev[e] = 8 * hs + e < NM ? __expf(gl_j - gv[e]) : 0.0f;
+            if (hs == 0) s_gam[j] = __expf(gl_j);
+        } else {
+            // the half's 8 factors, one per lane, then read from lanes 0..7 (hs is uniform in a wave)
+            const float es = 8 * hs + (lane & 7) < NM ? __expf(gl_h - gs_l) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ev[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(es), e));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[e] = ev[e] * kv[e];
         uint4 p[3];
         split3_bf16(mv, p[0], p[1], p[2]);
 #pragma unroll
@@ -652,6 +686,34 @@ void flush_kernel(FlushArgs a) {
 #pragma unroll
         for (int q = 0; q < 3; ++q)
             *reinterpret_cast<uint4*>(parts + Bx3<DK, NPAD>::SIDE + ((q * 2 + hs) * DK + j) * 16) = p[q];
+    }
+    all_loads_barrier();                        // copies landed; parts (and s_gam) written
+
+    // g_last for the fp32-MFMA paths, from the copied rows
+    float gn_s = gl_h;
+    if constexpr (DEC && !KDA && !BX3) gn_s = (n > 0 ? s_gs[n - 1] : 0.0f) + logf(__int_as_float(s_idx[9]));
+    if constexpr (!DEC && !KDA && !BX3) gn_s = s_gs[N - 1];
+    auto glast = [&](int row) -> float {
+        if constexpr (DEC)
+            return KDA ? (n > 0 ? s_G[(n - 1) * DK + row] : 0.0f) + logf(s_tal[row]) : gn_s;
+        else
+            return KDA ? s_G[(N - 1) * DK + row] : gn_s;
+    };
+    if constexpr (DEC) {
+        // slot n's key and log-decay
+        if (t < DK) {
+            st_nt(a.bk + head * (size_t)W * DK + (size_t)n * DK + t, seg_ld<TI>(s_tk, t));
+            if constexpr (KDA) st_nt(a.bg + head * (size_t)W * DK + (size_t)n * DK + t, BX3 ? gl_j : glast(t));
+            else if (t == 0) st_nt(a.bg + head * (size_t)W + n, gn_s);
+        }
+    }
+
+    // ---- H = Gamma Hb + Kt^T M (MFMA, accumulating in place) ------------------------------------
+    // fp32 MFMA: A operands Kt[slot][rowa], rowa = row(w, li/4, rb, li%4), slot = 4*ks + lg
+    // (0 from NM on).
+    [[maybe_unused]] float ka[RBW][NPAD / 4];
+    if constexpr (BX3) {
+        // the bf16 parts are in LDS
     } else if constexpr (KDA) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
@@ -728,7 +790,6 @@ void flush_kernel(FlushArgs a) {
         // three K = 32 steps, each lane group pairing one part of Kt with one part of M for
         // its half of the slots: x1 y1, x2 y1, x1 y3 (lane groups 0, 1) and x1 y2, x2 y2,
         // x3 y1 (lane groups 2, 3), x = Kt, y = M
-        lds_barrier();                          // parts written
         const char* parts = smem + LY::PARTS;
         const int hs = lg & 1, hi = lg >> 1;
         if (NM > 0) {

@@ -192,12 +192,6 @@ __device__ __forceinline__ float group_absmax(float x) {
 // 1.5*2^23 +- 127.
 constexpr float kRoundOff = 12582912.0f;   // 1.5 * 2^23
 
-// Four low bytes (a first) into one word.
-__device__ __forceinline__ uint32_t pack_low4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);    // a.b0 | b.b0 << 8
-    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
-    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);               // ab.lo16 | cd.lo16 << 16
-}
 
 // ---------------------------------------------------------------------------
 // memory
