@@ -133,6 +133,15 @@ __device__ __forceinline__ void split3_bf16(const float (&x)[8], uint4& p1, uint
     p3 = make_uint4(c[0], c[1], c[2], c[3]);
 }
 
+// Raw buffer over `bytes` bytes from base (gfx9 descriptor: 32-bit data format);
+// loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const float* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 // Rounding of y through the offset (y + 1.5 * 2^23, round to nearest even)
 // with the sum's low byte written into byte B of w and the other bytes of w
 // kept: an SDWA destination select with the unused bits preserved, so the
@@ -539,14 +548,15 @@ void flush_kernel(FlushArgs a) {
     const size_t head = blockIdx.x;
     const int W = a.W, C = a.C;
     // n_dev: the slot count per batch row, or (DEC) the decoded token's position
-    const int N = a.n_dev ? a.n_dev[head / (unsigned)a.H] + (DEC ? 1 : 0) : a.N;
+    // (uniform: every value derived from it stays scalar)
+    const int N = __builtin_amdgcn_readfirstlane(a.n_dev ? a.n_dev[head / (unsigned)a.H] + (DEC ? 1 : 0) : a.N);
     if (N <= 0 || N > W) return;                  // nothing buffered (or out of range): untouched
     const int n = N - 1;                          // DEC: the decoded token's slot
 
     const int8_t* sq = a.sq + head * (DK * DV);
     // buffered rows up to the last one read (DEC: slot n's row is the token's); the rows
     // past it repeat it, so they cost no further memory traffic
-    const int rlast = max((DEC ? n : N) - 1, 0);
+    const int rlast = __builtin_amdgcn_readfirstlane(max((DEC ? n : N) - 1, 0));
     // slots in the window terms; DEC: slot n (Kt row = k, its m from the decode) is a
     // rank-1 update afterwards
     const int NM = DEC ? n : N;
@@ -607,7 +617,7 @@ void flush_kernel(FlushArgs a) {
     // before the state bytes so that the split below runs while those are in flight.
     // g_last: the log-decay of the last slot, g_{N-1}, or (DEC) the decoded token's
     // g_n = g_{n-1} + log alpha; per head (scalar decay) or for column j (per-key).
-    const int j = t & (DK - 1), hs = t / DK;
+    const int j = t & (DK - 1), hs = __builtin_amdgcn_readfirstlane(t / DK);   // hs: uniform in a wave
     [[maybe_unused]] float mv[8], kv[8], gv[8];
     [[maybe_unused]] float gs_l = 0.0f, g_prev = 0.0f, al = 1.0f;
     if constexpr (BX3) {
@@ -624,22 +634,34 @@ void flush_kernel(FlushArgs a) {
             // lane (8 hs + e) % 64 holds slot 8 hs + e's log-decay, e < 8
             gs_l = bg[min(8 * hs + (lane & 7), rlast)];
         }
-        const float* bm = a.bm + head * (size_t)W * DV + j;
-        const float* bk = a.bk + head * (size_t)W * DK + j;
+        // buffer loads: the head's rows as one buffer, the row in the scalar offset and
+        // the lane's column in the vector offset (no per-load address arithmetic)
+        const uint32_t jb = 4u * (uint32_t)j;
+        const auto rm = buf_rsrc(a.bm + head * (size_t)W * DV, W * DV * 4);
+        const auto rk = buf_rsrc(a.bk + head * (size_t)W * DK, W * DK * 4);
+        [[maybe_unused]] const auto rg = buf_rsrc(a.bg + head * (size_t)W * DK, W * DK * 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int sl = min(8 * hs + e, rlast);
-            mv[e] = bm[sl * DV];
-            kv[e] = bk[sl * DK];
-            if constexpr (KDA) gv[e] = a.bg[(head * (size_t)W + sl) * DK + j];
+            const int sl = min(8 * hs + e, rlast);               // uniform
+            mv[e] = buf_ld(rm, jb, sl * DV * 4);
+            kv[e] = buf_ld(rk, jb, sl * DK * 4);
+            if constexpr (KDA) gv[e] = buf_ld(rg, jb, sl * DK * 4);
         }
     }
     // D-layout bytes of the base state: column 16 ct + li, this lane's RPL rows
     const int row0 = row_of<DK, DV>(w, lg, 0, 0);
     typename RBy::T hb[CT];
+    {
+        const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(sq), 0, DK * DV, 0x00020000);
+        const uint32_t vo = (uint32_t)sq_off<DK>(row0, li);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-        hb[ct] = *reinterpret_cast<const typename RBy::T*>(sq + sq_off<DK>(row0, li) + ct * sq_tile_stride<DK>());
+        for (int ct = 0; ct < CT; ++ct) {
+            if constexpr (RPL == 8)
+                hb[ct] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, vo, ct * sq_tile_stride<DK>(), 0));
+            else
+                hb[ct] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo, ct * sq_tile_stride<DK>(), 0);
+        }
+    }
     // The state-byte loads stay issued ahead of the split, and the split's inputs pass
     // through empty asm statements after them: the split cannot be scheduled above the
     // state-byte loads, and since loads return in order its wait leaves those in flight.
