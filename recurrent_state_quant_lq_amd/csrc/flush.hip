@@ -185,6 +185,16 @@ __device__ __forceinline__ uint32_t rows_umax4(uint32_t a, uint32_t b, uint32_t 
     return umax(s2[0], s2[1]);
 }
 
+// Maximum over the 64 lanes, in every lane: 16-lane rows by DPP, then the
+// rows exchanged by the gfx950 row swaps (no scalar round trip).
+__device__ __forceinline__ uint32_t wave_umax_v(uint32_t x) {
+    x = group_umax<16>(x);
+    const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);   // rows 2, 3 | rows 0, 1
+    x = umax(s[0], s[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);   // odd | even rows
+    return umax(r[0], r[1]);
+}
+
 // Maxima over the 16 lanes of a lane group of N values per lane (non-negative
 // floats as bit patterns), by halving exchanges: at step S the lanes whose lane
 // bit 8 >> S is set keep the second half of their values and pass the first half
@@ -279,7 +289,7 @@ __device__ void codec_store(v4f (&H)[RBW][CT], CodecLds<DK, DV, NW>& L, const Co
 #pragma unroll
         for (int c = 0; c < CMAX; ++c)
             if (c < C) {
-                const uint32_t mx = wave_umax(umax(ka, kb));
+                const uint32_t mx = wave_umax_v(umax(ka, kb));
                 const u64 ca = ballot(ka == mx), cb = ballot(kb == mx);
                 if (ca) {
                     const int r = __builtin_ctzll(ca);
