@@ -30,6 +30,8 @@
 // int8 bytes, scales and compensator rows are a function of the fp32 H.
 #include "lq_internal.h"
 
+#include <atomic>
+
 #pragma clang fp contract(off)
 
 namespace lq {
@@ -456,6 +458,11 @@ struct FlushArgs {
     const float* alpha;
     const float* beta;
     void* o;
+    // staggered start of the first round (0 ticks: none): workgroup b < stag_wgs
+    // waits (b / stag_cus) * stag_ticks ticks of the 100 MHz real-time counter
+    unsigned stag_ticks;
+    unsigned stag_cus;
+    unsigned stag_wgs;
 };
 
 // Rows 0..NPAD-1 of a [rows][D] fp32 block (row index clamped to rmax) into
@@ -535,6 +542,19 @@ void flush_kernel(FlushArgs a) {
     using LY = FlushLds<DK, DV, NPAD, KDA, DEC>;
 
     __shared__ __align__(16) char smem[LY::BYTES];
+    // Staggered start.  The dispatcher fills the CUs slot by slot (workgroup b
+    // goes to slot b / CUs of its CU), and loads issued together land in about
+    // that order, so a first round started all at once computes nothing until
+    // most of its loads have landed.  Slot s waits s times the time one slot's
+    // loads take to stream in, so the earlier slots compute meanwhile.  The
+    // wait is bounded (the counter only advances; at most 4096 sleeps).
+    if (a.stag_ticks && blockIdx.x < a.stag_wgs) {
+        const unsigned slot = blockIdx.x / a.stag_cus;
+        if (slot) {
+            const unsigned long long t_end = __builtin_amdgcn_s_memrealtime() + (unsigned long long)a.stag_ticks * slot;
+            for (int i = 0; i < 4096 && __builtin_amdgcn_s_memrealtime() < t_end; ++i) __builtin_amdgcn_s_sleep(2);
+        }
+    }
     float* s_r = reinterpret_cast<float*>(smem + LY::RS);
     float* s_s = s_r + DK;
     float* s_cv = s_r + 2 * DK;                                    // [CMAX][DV]
@@ -1014,14 +1034,58 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
     }
 }
 
+// Compute units of the current device, cached per device (0 if unknown).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 0;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// The rate the first round's loads are taken to stream in at when the start
+// is staggered: 55,000 bytes per 10 ns tick, i.e. 5.5 TB/s (tuned by
+// measurement at B = 64, H = 32, d = 128: slot delays of 1.3-1.7 us, i.e. 256
+// heads' loads at 5.5-7 TB/s, were best, 2.1 us worse).
+constexpr size_t kStaggerBytesPerTick = 55000;
+
+template <int DK, int WM, bool KDA, bool DEC, typename TI>
+hipError_t flush_launch(const lq_dims& d, const FlushArgs& args_in, hipStream_t s) {
+    auto kernel = flush_kernel<DK, DK, WM, KDA, DEC, TI>;
+    const dim3 grid((unsigned)d.B * (unsigned)d.H), block(FS<DK, DK>::NT);
+    // resident workgroups per CU of this kernel (cached; 0 if the query fails)
+    static std::atomic<int> occ{-1};
+    int slots = occ.load(std::memory_order_relaxed);
+    if (slots < 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&slots, kernel, (int)block.x, 0) != hipSuccess) slots = 0;
+        occ.store(slots, std::memory_order_relaxed);
+    }
+    FlushArgs args = args_in;
+    const int cus = device_cus();
+    // only launches of more than one round: a launch that fits at once may run
+    // beside other work (e.g. another stream's), which sleeping workgroups
+    // would keep out of their CU slots
+    if (cus > 0 && slots > 1 && grid.x > (unsigned)cus * (unsigned)slots) {
+        // bytes a head reads before it computes: codec, buffered rows (at most W - 1
+        // with a decoded token, W without), the token's vectors
+        const size_t gd = KDA ? DK : 1;
+        const size_t rows = DEC ? d.W - 1 : d.W;
+        size_t head = (size_t)DK * DK + 4 * (2 * DK + (size_t)d.C * DK + d.C) + rows * 4 * (2 * DK + gd);
+        if (DEC) head += sizeof(TI) * 3 * DK + (KDA ? 4 * DK : 8);
+        args.stag_ticks = (unsigned)((size_t)cus * head / kStaggerBytesPerTick);
+        args.stag_cus = (unsigned)cus;
+        args.stag_wgs = (unsigned)cus * (unsigned)slots;
+    }
+    return launch_kernel(DEC ? LQ_KERNEL_DECODE_FLUSH : LQ_KERNEL_FLUSH, kernel, grid, block, s, args);
+}
+
 template <int DK, int WM, bool KDA, bool DEC>
 hipError_t flush_t(const lq_dims& d, const FlushArgs& args, hipStream_t s) {
-    const dim3 grid((unsigned)d.B * (unsigned)d.H), block(FS<DK, DK>::NT);
-    if (DEC && d.io_dtype == LQ_IO_BF16)
-        return launch_kernel(LQ_KERNEL_DECODE_FLUSH, flush_kernel<DK, DK, WM, KDA, DEC, uint16_t>, grid, block, s,
-                             args);
-    return launch_kernel(DEC ? LQ_KERNEL_DECODE_FLUSH : LQ_KERNEL_FLUSH, flush_kernel<DK, DK, WM, KDA, DEC, float>,
-                         grid, block, s, args);
+    if (DEC && d.io_dtype == LQ_IO_BF16) return flush_launch<DK, WM, KDA, DEC, uint16_t>(d, args, s);
+    return flush_launch<DK, WM, KDA, DEC, float>(d, args, s);
 }
 
 template <int DK, bool DEC>
@@ -1046,7 +1110,7 @@ hipError_t launch_flush(const lq_dims& d, const lq_state& st, int n_buffered, co
                         float* h_out, hipStream_t s) {
     FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
                    st.buf_k, st.buf_m, st.buf_g, h_out, n_dev, d.W, d.C, n_buffered, d.smooth, d.H,
-                   nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+                   nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
     return flush_any<false>(d, args, s);
 }
 
@@ -1055,7 +1119,7 @@ hipError_t launch_decode_flush(const lq_dims& d, const lq_state& st, int pos, co
                                const float* beta, void* o, float* h_out, hipStream_t s) {
     FlushArgs args{st.sq, st.row_scale, st.col_scale, st.comp_idx, st.comp_val,
                    st.buf_k, st.buf_m, st.buf_g, h_out, pos_dev, d.W, d.C, pos + 1, d.smooth, d.H,
-                   q, k, v, alpha, beta, o};
+                   q, k, v, alpha, beta, o, 0, 0, 0};
     return flush_any<true>(d, args, s);
 }
 
