@@ -643,8 +643,8 @@ void flush_kernel(FlushArgs a) {
         }
     }
     // bf16 contraction: lane t holds column j of the buffered m and key rows (and per-key
-    // log-decays) for the 8 slots s = 8 hs .. 8 hs + 7 of its half, in registers, loaded
-    // before the state bytes so that the split below runs while those are in flight.
+    // log-decays) for the 8 slots s = 8 hs .. 8 hs + 7 of its half, in registers (no LDS
+    // round trip, and no barrier between reading the rows and writing the parts).
     // g_last: the log-decay of the last slot, g_{N-1}, or (DEC) the decoded token's
     // g_n = g_{n-1} + log alpha; per head (scalar decay) or for column j (per-key).
     const int j = t & (DK - 1), hs = __builtin_amdgcn_readfirstlane(t / DK);   // hs: uniform in a wave
@@ -692,9 +692,11 @@ void flush_kernel(FlushArgs a) {
                 hb[ct] = __builtin_amdgcn_raw_buffer_load_b32(rq, vo, ct * sq_tile_stride<DK>(), 0);
         }
     }
-    // The state-byte loads stay issued ahead of the split, and the split's inputs pass
-    // through empty asm statements after them: the split cannot be scheduled above the
-    // state-byte loads, and since loads return in order its wait leaves those in flight.
+    // The state-byte loads stay issued ahead of the split: the split's inputs pass through
+    // empty asm statements after them, so the compiler cannot start the split (and wait for
+    // its loads) before it has issued the state-byte loads.  (With copies to LDS in flight
+    // that wait covers every load: the compiler does not order copies to LDS with register
+    // loads.)
     asm volatile("" ::: "memory");
     if constexpr (BX3) {
 #pragma unroll
