@@ -542,19 +542,6 @@ void flush_kernel(FlushArgs a) {
     using LY = FlushLds<DK, DV, NPAD, KDA, DEC>;
 
     __shared__ __align__(16) char smem[LY::BYTES];
-    // Staggered start.  The dispatcher fills the CUs slot by slot (workgroup b
-    // goes to slot b / CUs of its CU), and loads issued together land in about
-    // that order, so a first round started all at once computes nothing until
-    // most of its loads have landed.  Slot s waits s times the time one slot's
-    // loads take to stream in, so the earlier slots compute meanwhile.  The
-    // wait is bounded (the counter only advances; at most 4096 sleeps).
-    if (a.stag_ticks && blockIdx.x < a.stag_wgs) {
-        const unsigned slot = blockIdx.x / a.stag_cus;
-        if (slot) {
-            const unsigned long long t_end = __builtin_amdgcn_s_memrealtime() + (unsigned long long)a.stag_ticks * slot;
-            for (int i = 0; i < 4096 && __builtin_amdgcn_s_memrealtime() < t_end; ++i) __builtin_amdgcn_s_sleep(2);
-        }
-    }
     float* s_r = reinterpret_cast<float*>(smem + LY::RS);
     float* s_s = s_r + DK;
     float* s_cv = s_r + 2 * DK;                                    // [CMAX][DV]
@@ -582,6 +569,19 @@ void flush_kernel(FlushArgs a) {
     const int N = __builtin_amdgcn_readfirstlane(a.n_dev ? a.n_dev[head / (unsigned)a.H] + (DEC ? 1 : 0) : a.N);
     if (N <= 0 || N > W) return;                  // nothing buffered (or out of range): untouched
     const int n = N - 1;                          // DEC: the decoded token's slot
+    // Staggered start.  The dispatcher fills the CUs slot by slot (workgroup b
+    // goes to slot b / CUs of its CU), and loads issued together land in about
+    // that order, so a first round started all at once computes nothing until
+    // most of its loads have landed.  Slot s waits s times the time one slot's
+    // loads take to stream in, so the earlier slots compute meanwhile.  The
+    // wait is bounded (the counter only advances; at most 4096 sleeps).
+    if (a.stag_ticks && blockIdx.x < a.stag_wgs) {
+        const unsigned slot = blockIdx.x / a.stag_cus;
+        if (slot) {
+            const unsigned long long t_end = __builtin_amdgcn_s_memrealtime() + (unsigned long long)a.stag_ticks * slot;
+            for (int i = 0; i < 4096 && __builtin_amdgcn_s_memrealtime() < t_end; ++i) __builtin_amdgcn_s_sleep(2);
+        }
+    }
 
     const int8_t* sq = a.sq + head * (DK * DV);
     // buffered rows up to the last one read (DEC: slot n's row is the token's); the rows
@@ -1067,10 +1067,11 @@ hipError_t flush_launch(const lq_dims& d, const FlushArgs& args_in, hipStream_t 
     }
     FlushArgs args = args_in;
     const int cus = device_cus();
-    // only launches of more than one round: a launch that fits at once may run
-    // beside other work (e.g. another stream's), which sleeping workgroups
-    // would keep out of their CU slots
-    if (cus > 0 && slots > 1 && grid.x > (unsigned)cus * (unsigned)slots) {
+    // only launches of more than one round in which every head has work: a
+    // launch that fits at once may run beside other work (e.g. another stream's),
+    // which sleeping workgroups would keep out of their CU slots, and with
+    // per-row slot counts most rows may have nothing to do
+    if (!args_in.n_dev && cus > 0 && slots > 1 && grid.x > (unsigned)cus * (unsigned)slots) {
         // bytes a head reads before it computes: codec, buffered rows (at most W - 1
         // with a decoded token, W without), the token's vectors
         const size_t gd = KDA ? DK : 1;
