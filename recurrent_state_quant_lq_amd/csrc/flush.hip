@@ -496,8 +496,8 @@ struct Bx3 {
 };
 
 // Workgroup LDS of the flush kernel (byte offsets).  With the bf16 contraction
-// the split operands (M parts, then Kt parts) overwrite the buffered rows
-// from MB on once they have been read into registers.
+// the buffered rows are loaded into registers, not copied here, and the split
+// operands (M parts, then Kt parts) take the rows' region from MB on.
 template <int DK, int DV, int NPAD, bool KDA, bool DEC>
 struct FlushLds {
     static constexpr int RS = 0;                                   // r | s | cv rows
