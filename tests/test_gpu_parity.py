@@ -67,6 +67,16 @@ def test_kda_full_size_sampled():
     _check(resync_run(wl, sample, host_tokens=False, log_every=8), "kda")
 
 
+def test_kda_b64_fused_sampled():
+    """Per-key decay at B = 64 (2,048 heads: the fused and plain flush launches
+    run more than one round of workgroups, the first one started staggered):
+    three windows, each ending with the fused call, on heads spread over the
+    grid, against the oracle."""
+    wl = PRESETS["kda"].with_(B=64, T=48)
+    sample = [(0, 0), (17, 3), (40, 7), (63, 31)]
+    _check(resync_run(wl, sample, host_tokens=False, fused=True), "kda B=64 fused")
+
+
 def test_outlier_sweep_w16_full_T_sampled():
     """B=256 H=32 d=128 with outlier channels, W = 16: all 64 windows of
     T = 1024 tokens after the 2048-token prefill."""
@@ -828,18 +838,21 @@ def test_fused_decode_flush_shapes(dk, W, C, kda, smooth, T):
            f"fused shape dk={dk} W={W} C={C} kda={kda}")
 
 
-def test_fused_matches_two_calls():
+@pytest.mark.parametrize("name", ["gdn_batched", "kda_b64"])
+def test_fused_matches_two_calls(name):
     """The fused call against lq_gdn_decode_step + lq_gdn_window_flush on the
-    same state and token (full gdn_batched size): o, the new buffer slot and
-    h_out agree to fp32 rounding; the earlier slots are left untouched."""
-    wl = PRESETS["gdn_batched"]
+    same state and token (full gdn_batched size, and the per-key preset at
+    B = 64: launches of more than one round of workgroups, whose first round
+    starts staggered): o, the new buffer slot and h_out agree to fp32
+    rounding; the earlier slots are left untouched."""
+    wl = PRESETS["gdn_batched"] if name == "gdn_batched" else PRESETS["kda"].with_(B=64)
     d = dims_of(wl)
-    say(f"fused vs two calls B={wl.B} H={wl.H}")
+    say(f"fused vs two calls {name} B={wl.B} H={wl.H}")
     g = torch.Generator(device="cuda").manual_seed(5)
     st = lq.LayerState.allocate(d)
     h0 = torch.randn((wl.B, wl.H, wl.dk, wl.dv), device="cuda", generator=g) * 0.3
     lq.lq_gdn_state_quantize(st, h0)
-    tk = inputs.device_tokens(17, wl.W, wl.B, wl.H, wl.dk, wl.dv, per_key=False, beta_lo=0.1,
+    tk = inputs.device_tokens(17, wl.W, wl.B, wl.H, wl.dk, wl.dv, per_key=wl.per_key, beta_lo=0.1,
                               beta_hi=0.9, device="cuda")
     o = torch.empty((wl.B, wl.H, wl.dv), device="cuda")
     for n in range(wl.W - 1):
