@@ -32,6 +32,7 @@ def _gpu():
 def _check(rep, name, o_tol=O_TOL):
     say(f"{name}: windows {rep.windows} heads {rep.heads} o_err {rep.o_err:.3e} "
         f"h_err {rep.h_err:.3e} buf_err {rep.buf_err:.3e} bytes_exact {rep.bytes_exact}")
+    assert rep.windows > 0
     assert rep.bytes_exact, rep.mismatches[:5]
     assert rep.o_err <= o_tol
     assert rep.h_err <= H_TOL
@@ -57,14 +58,18 @@ def test_gdn_batched_full_size_sampled():
     (the bench's schedule: the last token of each window fused with the flush)."""
     wl = PRESETS["gdn_batched"]
     sample = [(0, 0), (17, 5), (40, 31), (63, 31)]
-    _check(resync_run(wl, sample, host_tokens=False, log_every=16, fused=True), "gdn_batched")
+    rep = resync_run(wl, sample, host_tokens=False, log_every=16, fused=True)
+    assert rep.windows == wl.T // wl.W
+    _check(rep, "gdn_batched")
 
 
 def test_kda_full_size_sampled():
     """B=32 H=32 d=128 per-key decay: all 32 windows of T = 512 tokens."""
     wl = PRESETS["kda"]
     sample = [(0, 0), (9, 20), (31, 31)]
-    _check(resync_run(wl, sample, host_tokens=False, log_every=8), "kda")
+    rep = resync_run(wl, sample, host_tokens=False, log_every=8)
+    assert rep.windows == wl.T // wl.W
+    _check(rep, "kda")
 
 
 def test_kda_b64_fused_sampled():
@@ -77,13 +82,15 @@ def test_kda_b64_fused_sampled():
     _check(resync_run(wl, sample, host_tokens=False, fused=True), "kda B=64 fused")
 
 
-def test_outlier_sweep_w16_full_T_sampled():
-    """B=256 H=32 d=128 with outlier channels, W = 16: all 64 windows of
-    T = 1024 tokens after the 2048-token prefill."""
+@pytest.mark.parametrize("W", [8, 16, 32])
+def test_outlier_sweep_full_T_sampled(W):
+    """B=256 H=32 d=128 with outlier channels: all 1024 / W windows of
+    T = 1024 tokens after the 2048-token prefill, each ending with the fused call."""
     wl = PRESETS["outlier_sweep"]
     sample = [(0, 3), (131, 17), (255, 31)]
-    _check(resync_run(wl, sample, host_tokens=False, W=16, log_every=16, fused=True),
-           "outlier_sweep W=16 T=1024")
+    rep = resync_run(wl, sample, host_tokens=False, W=W, log_every=16, fused=True)
+    assert rep.windows == wl.T // W
+    _check(rep, f"outlier_sweep W={W} T={wl.T}")
 
 
 @pytest.mark.parametrize("W", [8, 16, 32])
