@@ -31,7 +31,7 @@ recurrence on a sample of heads.
 
 Profile summaries (text under profiles/) from rocprofv3 output:
     python bench.py --trace-summary OUT.md  STATS.csv  -- "<command that made it>"
-    python bench.py --pmc-summary   OUT.md  FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR -- "<commands>"
+    python bench.py --pmc-summary   OUT.md  FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR [--workload NAME] -- "<commands>"
     python bench.py --counter-summary OUT.md DIR [DIR ...] -- "<commands>"
 """
 from __future__ import annotations
@@ -51,7 +51,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F32_PEAK_TFS = 157.3      # MI355X dense fp32 matrix, published
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix, published
 METRIC = "decode tokens/s and state HBM GB/s (% of peak), int8 GDN, B=64 H=32 d=128"
-PMC_FILE = os.path.join(ROOT, "profiles", "decode_step_gdn_b64_h32_d128_w16_pmc.md")
+PMC_GLOB = os.path.join(ROOT, "profiles", "decode_step_*_pmc.md")
 
 
 def decode_bytes(wl, n: int) -> int:
@@ -149,17 +149,17 @@ def kernel_hash() -> str:
 
 
 def read_traffic(hsh: str, alg_bytes: int):
-    """Measured HBM bytes per decode launch from the committed rocprofv3 PMC
-    summary, if it was taken on the current decode kernel and on a workload
+    """Measured HBM bytes per decode launch from a committed rocprofv3 PMC
+    summary, if one was taken on the current decode kernel and on a workload
     with the same algorithmic bytes per launch (i.e. the same workload)."""
-    if not os.path.exists(PMC_FILE):
-        return None
-    for line in open(PMC_FILE):
-        line = line.strip()
-        if line.startswith("{") and '"kernel_hash"' in line:
-            rec = json.loads(line)
-            if rec.get("kernel_hash") == hsh and rec.get("algorithmic_bytes_per_launch") == alg_bytes:
-                return rec.get("hbm_bytes_per_launch")
+    import glob
+    for path in sorted(glob.glob(PMC_GLOB)):
+        for line in open(path):
+            line = line.strip()
+            if line.startswith("{") and '"kernel_hash"' in line:
+                rec = json.loads(line)
+                if rec.get("kernel_hash") == hsh and rec.get("algorithmic_bytes_per_launch") == alg_bytes:
+                    return rec.get("hbm_bytes_per_launch")
     return None
 
 
@@ -239,10 +239,10 @@ def _pmc_per_dispatch(d: str, counter: str, fam: str):
 
 
 def pmc_summary(out_md: str, fetch_dir: str, write_dir: str, cal_fetch: str, cal_write: str,
-                command: str):
+                command: str, workload: str = "gdn_batched"):
     """HBM traffic per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the counter reads for a plain device copy
-    of known size."""
+    of known size; `workload` names the preset the counters were taken on."""
     wl_bytes = 1 << 30                      # --copy-calib: 1 GiB read + 1 GiB written per copy
     # the copy dispatches are the largest ones in the calibration run
     def largest(d, c):
@@ -263,10 +263,10 @@ def pmc_summary(out_md: str, fetch_dir: str, write_dir: str, cal_fetch: str, cal
     dec_bytes = df * 1024.0 * f_fetch + dw * 1024.0 * f_write
     fl_bytes = (ff * 1024.0 * f_fetch + fw * 1024.0 * f_write) if ff is not None else None
     from recurrent_state_quant_lq_amd.configs import PRESETS
-    wl = PRESETS["gdn_batched"]
+    wl = PRESETS[workload]
     alg = sum(decode_bytes(wl, n) for n in range(wl.W - 1)) / (wl.W - 1)
     fl_alg = decode_flush_bytes(wl, wl.W)
-    rec = {"kernel_hash": kernel_hash(), "hbm_bytes_per_launch": int(dec_bytes),
+    rec = {"workload": workload, "kernel_hash": kernel_hash(), "hbm_bytes_per_launch": int(dec_bytes),
            "algorithmic_bytes_per_launch": int(alg), "traffic_over_algorithmic": round(dec_bytes / alg, 4),
            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
            "decode_flush_hbm_bytes_per_launch": int(fl_bytes) if fl_bytes else None,
@@ -870,7 +870,12 @@ def main():
         elif sys.argv[1] == "--counter-summary":
             counter_summary(argv[0], argv[1:], cmd)
         else:
-            pmc_summary(argv[0], argv[1], argv[2], argv[3], argv[4], cmd)
+            wl_name = "gdn_batched"
+            if "--workload" in argv:
+                k = argv.index("--workload")
+                wl_name = argv[k + 1]
+                argv = argv[:k] + argv[k + 2:]
+            pmc_summary(argv[0], argv[1], argv[2], argv[3], argv[4], cmd, wl_name)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)

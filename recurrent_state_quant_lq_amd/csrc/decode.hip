@@ -182,13 +182,15 @@ void decode_kernel(DecodeArgs a) {
     // ---- buffer rows -> VGPRs -------------------------------------------------------------
     const int slot0 = t / TPS;
     const int c0 = (t % TPS) * CH;
-    // decay rows of the slot groups; the slot index is clamped into the buffer so
-    // the loads are unconditional (values of slots >= n are never used)
+    // decay rows of the slot groups.  The loads are unconditional: a slot >= n (its
+    // value is never used) reads row n - 1 again, a row this workgroup reads anyway,
+    // so the rows past it cost no memory traffic
     float gs[ROUNDS][KDA ? CH : 1];
     float gslot[ROUNDS];
+    const int glast = max(n - 1, 0);
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
-        const int slot = min(slot0 + rd * SPR, W - 1);
+        const int slot = min(slot0 + rd * SPR, glast);
         if constexpr (KDA) load_floats<CH>(bgr + (size_t)slot * DK + c0, gs[rd]);
         else gslot[rd] = bgr[slot];
     }
@@ -502,11 +504,13 @@ void decode_split_kernel(DecodeArgs a) {
             }
         }
     };
-    // decay rows of this lane's slot groups (slot index clamped into the buffer)
+    // decay rows of this lane's slot groups; a slot >= n (its value is never used)
+    // reads row n - 1 again, so the rows past it cost no memory traffic
     auto load_decays = [&](float (&gs)[ROUNDS][KDA ? CH : 1], float (&gslot)[ROUNDS]) {
+        const int glast = max(n - 1, 0);
 #pragma unroll
         for (int rd = 0; rd < ROUNDS; ++rd) {
-            const int slot = min(slot0 + rd * SPR, W - 1);
+            const int slot = min(slot0 + rd * SPR, glast);
             if constexpr (KDA) load_floats<CH>(bgr + (size_t)slot * DK + c0, gs[rd]);
             else gslot[rd] = bgr[slot];
         }
