@@ -410,10 +410,12 @@ void decode_kernel(DecodeArgs a) {
 // first barrier waits for the small vectors only, and the state waves pass it
 // with their state loads still in flight.  Phase A (digits, slot dot products,
 // compensator coefficients) and the buffer sums then run while the state
-// streams in; after the state lands only the state waves' MFMAs and the token
-// waves' output step remain.  Each role is its own branch (the wave index is
-// uniform), so the register allocator never holds the state registers and the
-// m columns at once.
+// streams in; the token waves hand the buffer sums over in LDS and end.  After
+// the state lands, only the state waves' MFMAs, two row swaps that bring each
+// column's query and key sums to one lane, and the output step remain, with no
+// barrier or LDS round trip left on that path.  Each role is its own branch
+// (the wave index is uniform), so the register allocator never holds the state
+// registers and the m columns at once.
 template <int WM, bool KDA, int NB, typename TI>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(Dec<128, 128, WM, KDA>::WPE, Dec<128, 128, WM, KDA>::WPE)))
@@ -431,7 +433,7 @@ void decode_split_kernel(DecodeArgs a) {
     __shared__ __align__(16) float s_cqk[2][CMAX];            // e^{g_n}[idx_c] q[idx_c], ... k[idx_c]
     __shared__ __align__(16) int8_t s_dig[6][128];           // digits of q~'' (0..2), k~'' (3..5)
     __shared__ __align__(16) float s_msc[2];                 // digit scales of q~'', k~''
-    __shared__ __align__(16) float s_gem[2][DV];             // sq^T q~'', sq^T k~''
+    __shared__ __align__(16) float s_sum[2][DV];             // sum_i rr_i m_i, sum_i a_i m_i per value column
     // dwords 0..7: compensator rows; 8: beta; 9: alpha (scalar decay); 10: g_{n-1} (scalar decay)
     __shared__ __align__(16) int s_misc[16];
 
@@ -571,7 +573,6 @@ void decode_split_kernel(DecodeArgs a) {
             if (i < n) mcol[i] = ld_nt(bmr + (size_t)i * DV + t);
         all_loads_barrier();                                                        // (1)
 
-        const float beta = __int_as_float(s_misc[8]);
         float gn_s = 0.0f;
         if constexpr (!KDA) gn_s = (n > 0 ? __int_as_float(s_misc[10]) : 0.0f) + __logf(__int_as_float(s_misc[9]));
         // ---- A. digits of r o e^g o q and r o e^g o k; slot n's key and decay ------------------
@@ -616,7 +617,7 @@ void decode_split_kernel(DecodeArgs a) {
         }
         dot_products(gs, gslot, gn_s);
         lds_barrier();                                                              // (2)
-        // ---- buffer sums --------------------------------------------------------------------
+        // ---- buffer sums (value column t), handed to the state waves ---------------------------
         float sr = 0.0f, sa = 0.0f;
 #pragma unroll
         for (int i = 0; i < WM - 1; ++i)
@@ -624,21 +625,9 @@ void decode_split_kernel(DecodeArgs a) {
                 sr += s_rr[i] * mcol[i];
                 sa += s_a[i] * mcol[i];
             }
+        s_sum[0][t] = sr;
+        s_sum[1][t] = sa;
         lds_barrier();                                                              // (3)
-        // ---- C. m_n and the output (value column t) -----------------------------------------
-        const int j = t;
-        const float sj = s_vec[D::SS * DK + j];
-        float hq = sj * s_gem[0][j], hk = sj * s_gem[1][j];
-#pragma unroll
-        for (int c = 0; c < CMAX; ++c)
-            if (c < C) {
-                const float cvj = s_vec[(D::SCV + c) * DK + j];
-                hq += s_cqk[0][c] * cvj;
-                hk += s_cqk[1][c] * cvj;
-            }
-        const float mn = beta * (seg_ld<TI>(s_vec + D::SV * DK, j) - hk - sr);
-        st_nt(a.bm + head * (size_t)W * DV + (size_t)n * DV + j, mn);
-        tok_st<TI>(a.o, head * DV + j, hq + sa + s_a[n] * mn);
     } else {
         // ================= state waves ============================================================
         float gs[ROUNDS][KDA ? CH : 1], gslot[ROUNDS];
@@ -681,28 +670,61 @@ void decode_split_kernel(DecodeArgs a) {
         // A = the digits (rows 0..2: q~'', rows 4..6: k~'', other rows zero), B = the state
         // bytes as loaded; lane group 0 ends with the digit sums of q~'' for value column
         // l % 16, lane group 1 those of k~''.
+        const int li = lane % 16, lg = lane / 16;
+        v4i aop[2];
         {
-            const int li = lane % 16, lg = lane / 16;
             const int drow = li < 3 ? li : (li >= 4 && li < 7) ? li - 1 : -1;
-            v4i aop[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 aop[ks] = drow >= 0 ? *reinterpret_cast<const v4i*>(&s_dig[drow][ks * 64 + 16 * lg])
                                     : v4i{0, 0, 0, 0};
-            const float sc = lg < 2 ? s_msc[lg] : 0.0f;
-#pragma unroll
-            for (int tw = 0; tw < TPSW; ++tw) {
-                // |digit| <= 127 and |byte| <= 127 over 128 channels: int32 sums below 2^21
-                v4i dv4 = v4i{0, 0, 0, 0};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    dv4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[ks], sqa[tw][ks], dv4, 0, 0, 0);
-                const float x = __builtin_fmaf((float)dv4[2], kDigitW2,
-                                               __builtin_fmaf((float)dv4[1], kDigitW1, (float)dv4[0]));
-                if (lg < 2) s_gem[lg][((w - 2) * TPSW + tw) * 16 + li] = x * sc;
-            }
         }
+        const float sc = lg < 2 ? s_msc[lg] : 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();                                                              // (3)
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- C. m_n and the output, value column j of lane group lg = this wave's tile lg ----
+        // (everything but the GEMV is read while the state is still streaming in)
+        const int j = ((w - 2) * TPSW + lg) * 16 + li;
+        const float sj = s_vec[D::SS * DK + j];
+        const float vj = seg_ld<TI>(s_vec + D::SV * DK, j);
+        const float sr = s_sum[0][j], sa = s_sum[1][j];
+        const float an = s_a[n];
+        const float beta = __int_as_float(s_misc[8]);
+        // the compensator rows' share of Hb^T q~ and Hb^T k~ for column j
+        float cq = 0.0f, ck = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c)
+            if (c < C) {
+                const float cvj = s_vec[(D::SCV + c) * DK + j];
+                cq += s_cqk[0][c] * cvj;
+                ck += s_cqk[1][c] * cvj;
+            }
+        // the MFMAs stay below the barrier and the LDS reads above them: only the
+        // MFMAs and what follows wait for the state
+        __builtin_amdgcn_sched_barrier(0);
+        float x[TPSW];
+#pragma unroll
+        for (int tw = 0; tw < TPSW; ++tw) {
+            // |digit| <= 127 and |byte| <= 127 over 128 channels: int32 sums below 2^21
+            v4i dv4 = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                dv4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[ks], sqa[tw][ks], dv4, 0, 0, 0);
+            x[tw] = __builtin_fmaf((float)dv4[2], kDigitW2, __builtin_fmaf((float)dv4[1], kDigitW1, (float)dv4[0])) * sc;
+        }
+        // Row r of x[tw] holds (q, k, 0, 0)[r] of tile tw.  The row swaps bring tile lg's
+        // q and k sums to lane group lg: v_permlane16_swap gives rows (q0, q1, -, -) and
+        // (k0, k1, -, -) from tiles 0 and 1 (and the same from tiles 2 and 3), and
+        // v_permlane32_swap the upper tiles' rows 0-1 to rows 2-3.
+        const auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[0]), __float_as_uint(x[1]), false, false);
+        const auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[2]), __float_as_uint(x[3]), false, false);
+        const auto pq = __builtin_amdgcn_permlane32_swap(p01[0], p23[0], false, false);
+        const auto pk = __builtin_amdgcn_permlane32_swap(p01[1], p23[1], false, false);
+        const float hq = sj * __uint_as_float(pq[0]) + cq, hk = sj * __uint_as_float(pk[0]) + ck;
+        const float mn = beta * (vj - hk - sr);
+        st_nt(a.bm + head * (size_t)W * DV + (size_t)n * DV + j, mn);
+        tok_st<TI>(a.o, head * DV + j, hq + sa + an * mn);
     }
 }
 
