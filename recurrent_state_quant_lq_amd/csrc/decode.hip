@@ -403,12 +403,12 @@ void decode_kernel(DecodeArgs a) {
 
 // dk = dv = 128: the same step with the waves split by role, so that the token
 // work does not wait for the state bytes.  Waves 0-1 (token waves, lane t =
-// channel t = value column t) copy the per-head vectors, compensator rows and
-// buffered keys to LDS and load the buffered m columns; waves 2-3 (state waves)
-// load the int8 state, wave w the column tiles 4 (w - 2) .. + 3.  A wave's
-// counter of outstanding loads covers only its own loads, so the token waves'
-// first barrier waits for the small vectors only, and the state waves pass it
-// with their state loads still in flight.  Phase A (digits, slot dot products,
+// channel t = value column t) copy the per-head vectors and compensator rows to
+// LDS and load the buffered m columns; waves 2-3 (state waves) copy the buffered
+// keys to LDS, then, after the first barrier, load the int8 state, wave w the
+// column tiles 4 (w - 2) .. + 3.  The first barrier thus waits for the head's
+// token data only (each wave's counter of outstanding loads covers only its own
+// loads), and the state waves' later waits leave their state loads in flight.  Phase A (digits, slot dot products,
 // compensator coefficients) and the buffer sums then run while the state
 // streams in; the token waves hand the buffer sums over in LDS and end.  After
 // the state lands, only the state waves' MFMAs, two row swaps that bring each
@@ -550,12 +550,6 @@ void decode_split_kernel(DecodeArgs a) {
                 const int c = base + t;
                 if (c < ccv) lds_dma16(a.cv + head * (size_t)C * DV + 4 * c, s_vec + D::SCV * DK + 4 * (base + 64 * w));
             }
-            // buffered keys k_0 .. k_{n-1}: n*DK contiguous floats
-            const int ckb = n * DK / 4;
-            for (int base = 0; base < ckb; base += 128) {
-                const int c = base + t;
-                if (c < ckb) lds_dma16(bkr + 4 * c, s_vec + D::SKB * DK + 4 * (base + 64 * w));
-            }
             if (w == 0) {
                 const void* src4 = nullptr;
                 if (lane < C) src4 = a.idx + head * C + lane;
@@ -631,8 +625,20 @@ void decode_split_kernel(DecodeArgs a) {
     } else {
         // ================= state waves ============================================================
         float gs[ROUNDS][KDA ? CH : 1], gslot[ROUNDS];
+        {
+            // buffered keys k_0 .. k_{n-1}: n*DK contiguous floats.  Copied by these
+            // waves, the token waves' share of the head's token loads is issued sooner
+            // and the keys stream beside it; this wave waits for its copies at the
+            // first barrier, before any wave reads them.
+            const int ckb = n * DK / 4;
+            const int ts = t - 128;
+            for (int base = 0; base < ckb; base += 128) {
+                const int c = base + ts;
+                if (c < ckb) lds_dma16(bkr + 4 * c, s_vec + D::SKB * DK + 4 * (base + 64 * (w - 2)));
+            }
+        }
         load_decays(gs, gslot);
-        lds_barrier();                                                              // (1)
+        all_loads_barrier();                                                        // (1)
         // The int8 state, requested once this head's token data has landed: every
         // workgroup's token data then reaches the queue ahead of the state streams, so
         // the token work of even the last heads is done before their state arrives.
